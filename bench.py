@@ -1,0 +1,356 @@
+"""Benchmark of the grouped 4-bit MoE layer step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config olmoe]
+
+A step is one pass of the hot path over one batch of synthetic tokens:
+gnf4_route -> gnf4_grouped_gemm (gate_up, rows gathered from the token
+activations) -> gnf4_grouped_gemm (down, input already in routed order) ->
+gnf4_combine. Decode steps (T = 1) and prefill steps (the workload's largest
+T) are captured once per input slot as HIP graphs and replayed; successive
+steps rotate over input slots and over copies of the layer's packed weights
+so that no step finds its weights in the 256 MB Infinity Cache.
+
+Reported (one JSON line on stdout):
+  value      decode packed-weight GB/s of the whole step (codes + scales of
+             the experts the step routes to, both projections, / step time)
+  roofline   the decode gate_up GEMM kernel: algorithmic packed bytes per
+             launch / its mean duration from HIP events on the launch stream
+  prefill    TFLOP/s of the prefill step and the roofline of its gate_up
+             MFMA kernel (algorithmic flops 2*rows*N*K per launch)
+  cpu_baseline  the float64 CPU oracle (dequant + matmul + combine) timed on
+             this host on one decode step of the same workload
+Inputs are resident in device memory before timing starts.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2516.6      # MI355X dense bf16 MFMA, published (2.5 PFLOP/s)
+MALL_BYTES = 256 << 20
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default="olmoe")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--only", choices=["decode", "prefill"], default=None)
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run a plain 1 GiB device copy (counter calibration)")
+    return ap.parse_args()
+
+
+def packed_bytes_per_expert(pw):
+    return pw.nbytes() // pw.E
+
+
+class Layer:
+    """Packed weights of one FFN layer (or the single projection of tiny)."""
+
+    def __init__(self, torch, gnf4, cfg, seed=0):
+        self.cfg = cfg
+        self.projs = []
+        g = torch.Generator(device="cuda")
+        for pi, proj in enumerate(cfg.projs):
+            g.manual_seed(1000 * seed + 17 * cfg.config_id + pi)
+            pw = gnf4.empty_packed(cfg.fmt, cfg.E, proj.N, proj.K)
+            if cfg.fmt == "nf4_dq":
+                W = torch.randn((cfg.E, proj.N, proj.K), generator=g, device="cuda") * 0.02
+                gnf4.quantize(cfg.fmt, W, pw)
+                del W
+            else:
+                step = max(1, (1 << 28) // (proj.N * proj.K))   # experts per quantize call
+                for e0 in range(0, cfg.E, step):
+                    n = min(step, cfg.E - e0)
+                    W = torch.randn((n, proj.N, proj.K), generator=g, device="cuda") * 0.02
+                    gnf4.quantize_into(cfg.fmt, W, pw, e0)
+                    del W
+            self.projs.append(pw)
+        torch.cuda.synchronize()
+
+    def clone(self, torch):
+        other = Layer.__new__(Layer)
+        other.cfg = self.cfg
+        other.projs = []
+        for pw in self.projs:
+            other.projs.append(type(pw)(pw.format, pw.E, pw.N, pw.K, pw.codes.clone(),
+                                        pw.scales.clone(),
+                                        pw.scales2.clone() if pw.scales2 is not None else None))
+        return other
+
+    def nbytes(self):
+        return sum(pw.nbytes() for pw in self.projs)
+
+
+class StepSlot:
+    """Inputs, outputs and the captured graph of one step."""
+
+    def __init__(self, torch, gnf4, cfg, layer, T, seed):
+        import synth
+        k = cfg.k
+        ids, tw = synth.routing_inputs(cfg, T, seed=seed)
+        self.n_active = int(np.unique(ids).size)
+        self.T = T
+        self.ids = torch.from_numpy(ids).cuda()
+        self.tw = torch.from_numpy(tw).cuda()
+        first = cfg.projs[0]
+        self.X = torch.from_numpy(synth.activations(cfg, T, first.K, synth.T_X, seed, T).view(np.int16)).cuda()
+        self.layer = layer
+        self.r = gnf4.route_buffers(T, k, cfg.E)
+        self.Y = [torch.empty((T * k, p.N), dtype=torch.float32, device="cuda") for p in cfg.projs]
+        if len(cfg.projs) > 1:
+            down = cfg.projs[1]
+            self.Xd = torch.from_numpy(synth.activations(cfg, T * k, down.K, synth.T_X_DOWN, seed, T)
+                                       .view(np.int16)).cuda()
+        self.out = torch.empty((T, cfg.projs[-1].N), dtype=torch.float32, device="cuda")
+        self.graph = None
+
+    def run(self, gnf4):
+        cfg, T, k = self.layer.cfg, self.T, self.layer.cfg.k
+        r = gnf4.route(self.ids, cfg.E, out=self.r)
+        gnf4.grouped_gemm(self.layer.projs[0], self.X, 1, r, T, k, self.Y[0])
+        last = self.Y[0]
+        if len(self.layer.projs) > 1:
+            gnf4.grouped_gemm(self.layer.projs[1], self.Xd, 0, r, T, k, self.Y[1])
+            last = self.Y[1]
+        gnf4.combine(last, r["inv"], self.tw, T, k, self.out)
+
+    def capture(self, torch, gnf4):
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            self.run(gnf4)                     # warm the launch path outside capture
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        self.graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.graph):
+            self.run(gnf4)
+        torch.cuda.synchronize()
+
+    def weight_bytes(self):
+        return sum(self.n_active * pw.nbytes() // pw.E for pw in self.layer.projs)
+
+    def flops(self):
+        return sum(2.0 * self.T * self.layer.cfg.k * pw.N * pw.K for pw in self.layer.projs)
+
+
+def time_steps(torch, slots, steps, warmup):
+    for i in range(warmup):
+        slots[i % len(slots)].graph.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        slots[i % len(slots)].graph.replay()
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / steps
+    per = np.mean([slots[i % len(slots)].weight_bytes() for i in range(steps)])
+    fl = np.mean([slots[i % len(slots)].flops() for i in range(steps)])
+    return dt, per, fl
+
+
+def time_kernel(torch, gnf4, slots, steps, warmup):
+    """Mean duration of the gate_up GEMM launch, from HIP events recorded on
+    the stream it is launched on (torch's current stream), over `steps`
+    launches rotating through the slots (route outputs already computed)."""
+    for sl in slots:
+        gnf4.route(sl.ids, sl.layer.cfg.E, out=sl.r)
+    torch.cuda.synchronize()
+    cfg = slots[0].layer.cfg
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    for i in range(warmup):
+        sl = slots[i % len(slots)]
+        gnf4.grouped_gemm(sl.layer.projs[0], sl.X, 1, sl.r, sl.T, cfg.k, sl.Y[0])
+    for i in range(steps):
+        sl = slots[i % len(slots)]
+        evs[i][0].record()
+        gnf4.grouped_gemm(sl.layer.projs[0], sl.X, 1, sl.r, sl.T, cfg.k, sl.Y[0])
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    ms = np.array([a.elapsed_time(b) for a, b in evs])
+    byts = np.array([slots[i % len(slots)].n_active * slots[i % len(slots)].layer.projs[0].nbytes()
+                     // cfg.E for i in range(steps)], dtype=np.float64)
+    fl = np.array([2.0 * slots[i % len(slots)].T * cfg.k * slots[i % len(slots)].layer.projs[0].N
+                   * slots[i % len(slots)].layer.projs[0].K for i in range(steps)])
+    return float(ms.mean()), float(byts.mean()), float(fl.mean())
+
+
+def cpu_baseline(cfg, T):
+    """The float64 oracle on one decode step of this workload (route, both
+    projections' dequant + matmul for the routed experts, combine)."""
+    import synth
+    from oracle import combine, grouped_gemm, mxfp4, nf4, routing
+    try:
+        from threadpoolctl import threadpool_info, threadpool_limits
+    except Exception:  # pragma: no cover
+        threadpool_limits = None
+        threadpool_info = None
+    cores = len(os.sched_getaffinity(0))
+    ids, tw = synth.routing_inputs(cfg, T, seed=12345)
+    active = sorted(set(int(v) for v in ids.reshape(-1)))
+    packs = []
+    for proj in cfg.projs:
+        nb = proj.K // (32 if cfg.fmt == "mxfp4" else 64)
+        codes = np.zeros((cfg.E, proj.N, proj.K // 2), dtype=np.uint8)
+        scales = np.zeros((cfg.E, proj.N, nb), dtype=np.uint8 if cfg.fmt == "mxfp4" else np.float32)
+        scales2 = None
+        for e in active:
+            W = synth.expert_weight(cfg, proj, e)
+            codes[e], scales[e] = (mxfp4.quantize if cfg.fmt == "mxfp4" else nf4.quantize)(W)
+        if cfg.fmt == "nf4_dq":
+            q8, scales2 = nf4.double_quantize_absmax(scales.reshape(-1))
+            scales = q8.reshape(cfg.E, proj.N, nb)
+        packs.append((proj, codes, scales, scales2))
+    X = synth.token_inputs(cfg, T)
+    Xd = synth.down_inputs(cfg, T) if len(cfg.projs) > 1 else None
+    limit = threadpool_limits(limits=cores) if threadpool_limits else None
+    reps, t_total, byts = 0, 0.0, 0
+    t_start = time.perf_counter()
+    while True:
+        t0 = time.perf_counter()
+        r = routing.route(ids, cfg.E)
+        Y = None
+        for pi, (proj, codes, scales, scales2) in enumerate(packs):
+            inp = X if pi == 0 else Xd
+            Y = grouped_gemm.grouped_gemm(cfg.fmt, codes, scales, scales2, inp, 1 if pi == 0 else 0,
+                                          r["offsets"], r["perm"], cfg.k, proj.N, proj.K)
+        combine.combine(Y, r["inv"], tw, T, cfg.k)
+        t_total += time.perf_counter() - t0
+        reps += 1
+        for proj, codes, scales, scales2 in packs:
+            per = codes[0].nbytes + scales[0].nbytes
+            byts += len(active) * per
+        if time.perf_counter() - t_start > 10.0 or reps >= 20:
+            break
+    threads = cores
+    if threadpool_info is not None:
+        info = threadpool_info()
+        if info:
+            threads = max(int(i.get("num_threads", 1)) for i in info)
+    if limit is not None:
+        limit.unregister() if hasattr(limit, "unregister") else None
+    return {"value": round(byts / t_total / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": "%d full decode step(s) (T=%d, %d routed experts, both projections: dequant + "
+                      "float64 matmul + combine), %.1f s" % (reps, T, len(active), t_total)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import synth
+    from bit_mixture_experts_topk_amd import gnf4
+    gnf4.lib()
+    cfg = synth.CONFIGS[args.config]
+    torch.cuda.set_device(0)
+    base = Layer(torch, gnf4, cfg)
+    layer_bytes = base.nbytes()
+
+    result = {"metric": "packed-weight GB/s (% of HBM peak) at bs=1; prefill TFLOP/s (% MFMA peak)",
+              "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+              "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+              "data": "synthetic"}
+    T_dec = min(cfg.Ts)
+    T_pre = max(cfg.Ts)
+    decode_ok = T_dec * cfg.k <= 64 and args.only != "prefill"
+    prefill_ok = T_pre * cfg.k > 64 and args.only != "decode"
+
+    out = {}
+    if decode_ok:
+        # enough weight copies that a copy is reused only after > 2x MALL of other traffic
+        step_bytes = layer_bytes * min(1.0, T_dec * cfg.k / cfg.E)
+        copies = int(min(32, max(4, np.ceil(3 * MALL_BYTES / max(step_bytes, 1)))))
+        layers = [base] + [base.clone(torch) for _ in range(copies - 1)]
+        slots = [StepSlot(torch, gnf4, cfg, layers[i % copies], T_dec, seed=100 + i)
+                 for i in range(max(copies, 16))]
+        for sl in slots:
+            sl.capture(torch, gnf4)
+        dt, byts, _ = time_steps(torch, slots, args.steps, args.warmup)
+        kms, kbytes, _ = time_kernel(torch, gnf4, slots, args.steps, args.warmup)
+        out["decode"] = dict(T=T_dec, ms_per_step=dt * 1e3, gbs=byts / dt / 1e9,
+                             kernel_us=kms * 1e3, kernel_bytes=kbytes, copies=copies)
+        del slots, layers
+        torch.cuda.empty_cache()
+    if prefill_ok:
+        copies = int(min(8, max(2, np.ceil(3 * MALL_BYTES / max(layer_bytes, 1)))))
+        layers = [base] + [base.clone(torch) for _ in range(copies - 1)]
+        slots = [StepSlot(torch, gnf4, cfg, layers[i % copies], T_pre, seed=200 + i)
+                 for i in range(copies)]
+        for sl in slots:
+            sl.capture(torch, gnf4)
+        steps = max(10, args.steps // 10)
+        dt, byts, fl = time_steps(torch, slots, steps, max(2, args.warmup // 5))
+        kms, kbytes, kfl = time_kernel(torch, gnf4, slots, steps, max(2, args.warmup // 5))
+        out["prefill"] = dict(T=T_pre, ms_per_step=dt * 1e3, tflops=fl / dt / 1e12,
+                              kernel_us=kms * 1e3, kernel_flops=kfl, copies=copies)
+        del slots, layers
+        torch.cuda.empty_cache()
+
+    if args.calib_copy:
+        a = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+
+    wl = {"workload": "%s-shaped MoE FFN layer: E=%d top-%d, d=%d, I=%d, %s (block %d); "
+                      "decode T=%s, prefill T=%s" % (cfg.name, cfg.E, cfg.k, cfg.d, cfg.inter,
+                                                     cfg.fmt.upper(), 32 if cfg.fmt == "mxfp4" else 64,
+                                                     T_dec if decode_ok else "-",
+                                                     T_pre if prefill_ok else "-"),
+          "global_batch": T_dec if decode_ok else T_pre, "layer_packed_MB": round(layer_bytes / 1e6, 2),
+          "parallelism": "single GPU"}
+    result["config"] = wl
+    if "decode" in out:
+        d = out["decode"]
+        result["value"] = round(d["gbs"], 2)
+        result["ms_per_step"] = round(d["ms_per_step"], 5)
+        ach = d["kernel_bytes"] / (d["kernel_us"] * 1e-6) / 1e9
+        result["roofline"] = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
+                              "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
+                              "kernel": "gemv_kernel (gate_up, T=%d)" % d["T"],
+                              "kernel_us": round(d["kernel_us"], 3),
+                              "bytes_per_launch": int(d["kernel_bytes"])}
+        result["decode"] = {"step_us": round(d["ms_per_step"] * 1e3, 3),
+                            "pct_hbm_peak_step": round(100 * d["gbs"] / HBM_PEAK_GBS, 2),
+                            "weight_copies": d["copies"]}
+    if "prefill" in out:
+        p = out["prefill"]
+        kt = p["kernel_flops"] / (p["kernel_us"] * 1e-6) / 1e12
+        result["prefill"] = {"T": p["T"], "step_ms": round(p["ms_per_step"], 4),
+                             "tflops": round(p["tflops"], 2),
+                             "pct_mfma_peak_step": round(100 * p["tflops"] / BF16_PEAK_TFLOPS, 2),
+                             "roofline": {"bound": "mfma", "achieved": round(kt, 2),
+                                          "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                          "frac": round(kt / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                                          "kernel": "mfma_kernel (gate_up, T=%d)" % p["T"],
+                                          "kernel_us": round(p["kernel_us"], 2)}}
+        if "decode" not in out:
+            result["value"] = round(p["tflops"], 3)
+            result["unit"] = "TFLOP/s"
+            result["ms_per_step"] = round(p["ms_per_step"], 5)
+            result["roofline"] = result["prefill"]["roofline"]
+    if not args.no_cpu and decode_ok:
+        result["cpu_baseline"] = cpu_baseline(cfg, T_dec)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,220 @@
+// Host side of the gnf4 C ABI: argument validation, path dispatch, error text.
+// Every check runs before any HIP call, so invalid arguments are rejected
+// identically on machines without a GPU.
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+
+#include "common.h"
+
+#ifndef GNF4_REVISION
+#define GNF4_REVISION "unknown"
+#endif
+
+namespace gnf4 {
+
+static thread_local char g_err[512] = "";
+
+static gnf4_status fail(gnf4_status st, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+static gnf4_status ok() {
+  g_err[0] = '\0';
+  return GNF4_OK;
+}
+
+static gnf4_status device_status(hipError_t e, const char *what) {
+  if (e == hipSuccess) return ok();
+  return fail(GNF4_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
+}
+
+static bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+int device_cu_count() {
+  static std::mutex mu;
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  std::lock_guard<std::mutex> lock(mu);
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+static gnf4_status check_weights(const gnf4_weights *w) {
+  if (!w) return fail(GNF4_ERR_INVALID_ARG, "weights descriptor is NULL");
+  if (w->format < GNF4_NF4 || w->format > GNF4_MXFP4)
+    return fail(GNF4_ERR_INVALID_ARG, "unknown format %d", w->format);
+  if (w->E < 1 || w->E > GNF4_MAX_EXPERTS)
+    return fail(GNF4_ERR_INVALID_ARG, "E = %d outside [1, %d]", w->E, GNF4_MAX_EXPERTS);
+  if (w->N < 1 || w->N > GNF4_MAX_N)
+    return fail(GNF4_ERR_INVALID_ARG, "N = %d outside [1, %d]", w->N, GNF4_MAX_N);
+  const int blk = w->format == GNF4_MXFP4 ? 32 : 64;
+  if (w->K < blk || w->K > GNF4_MAX_K || w->K % blk)
+    return fail(GNF4_ERR_INVALID_ARG, "K = %d must be a positive multiple of %d up to %d", w->K,
+                blk, GNF4_MAX_K);
+  if (!w->codes || !w->scales) return fail(GNF4_ERR_INVALID_ARG, "codes or scales is NULL");
+  if (!aligned16(w->codes)) return fail(GNF4_ERR_INVALID_ARG, "codes must be 16-byte aligned");
+  if (w->format == GNF4_NF4 && ((uintptr_t)w->scales & 3u))
+    return fail(GNF4_ERR_INVALID_ARG, "float32 scales must be 4-byte aligned");
+  if (w->format == GNF4_NF4_DQ && !w->scales2)
+    return fail(GNF4_ERR_INVALID_ARG, "NF4_DQ needs scales2");
+  if (w->format == GNF4_NF4_DQ && ((uintptr_t)w->scales2 & 3u))
+    return fail(GNF4_ERR_INVALID_ARG, "scales2 must be 4-byte aligned");
+  if ((int64_t)w->E * w->N * (w->K / 2) > (int64_t)1 << 40)
+    return fail(GNF4_ERR_UNSUPPORTED, "weight tensor too large");
+  return ok();
+}
+
+static Weights to_kernel(const gnf4_weights *w) {
+  Weights k;
+  k.format = w->format;
+  k.E = w->E;
+  k.N = w->N;
+  k.K = w->K;
+  k.codes = w->codes;
+  k.scales = w->scales;
+  k.scales2 = w->scales2;
+  return k;
+}
+
+// Decode path for T*k routed rows at or below this count.
+constexpr int kGemvMaxRows = 64;
+
+}  // namespace gnf4
+
+using namespace gnf4;
+
+extern "C" {
+
+gnf4_status gnf4_route(const int32_t *topk_ids, int32_t T, int32_t k, int32_t E, int32_t *counts,
+                       int32_t *offsets, int32_t *perm, int32_t *inv, int32_t *active,
+                       int32_t *n_active, int32_t *bad_id_flag, gnf4_stream_t stream) {
+  if (E < 1 || E > GNF4_MAX_EXPERTS)
+    return fail(GNF4_ERR_INVALID_ARG, "E = %d outside [1, %d]", E, GNF4_MAX_EXPERTS);
+  if (k < 1 || k > 64) return fail(GNF4_ERR_INVALID_ARG, "k = %d outside [1, 64]", k);
+  if (T < 0) return fail(GNF4_ERR_INVALID_ARG, "T = %d is negative", T);
+  if ((int64_t)T * k >= ((int64_t)1 << 31) - 1024)
+    return fail(GNF4_ERR_INVALID_ARG, "T*k too large");
+  if (!counts || !offsets || !active || !n_active || !bad_id_flag)
+    return fail(GNF4_ERR_INVALID_ARG, "an output pointer is NULL");
+  if (T > 0 && (!topk_ids || !perm || !inv))
+    return fail(GNF4_ERR_INVALID_ARG, "topk_ids, perm or inv is NULL");
+  return device_status(launch_route(topk_ids, T, k, E, counts, offsets, perm, inv, active,
+                                    n_active, bad_id_flag, (hipStream_t)stream),
+                       "route launch");
+}
+
+gnf4_status gnf4_grouped_gemm(const gnf4_weights *w, const uint16_t *X, int32_t gather,
+                              const int32_t *offsets, const int32_t *perm, const int32_t *active,
+                              const int32_t *n_active, int32_t T, int32_t k, float *Y,
+                              gnf4_stream_t stream) {
+  gnf4_status st = check_weights(w);
+  if (st != GNF4_OK) return st;
+  if (gather != 0 && gather != 1) return fail(GNF4_ERR_INVALID_ARG, "gather must be 0 or 1");
+  if (k < 1 || k > 64) return fail(GNF4_ERR_INVALID_ARG, "k = %d outside [1, 64]", k);
+  if (T < 0) return fail(GNF4_ERR_INVALID_ARG, "T = %d is negative", T);
+  if ((int64_t)T * k >= ((int64_t)1 << 31) - 1024)
+    return fail(GNF4_ERR_INVALID_ARG, "T*k too large");
+  if (T == 0) return ok();
+  if (!X || !offsets || !perm || !active || !n_active || !Y)
+    return fail(GNF4_ERR_INVALID_ARG, "a pointer argument is NULL");
+  if (!aligned16(X) || !aligned16(Y))
+    return fail(GNF4_ERR_INVALID_ARG, "X and Y must be 16-byte aligned");
+  GemmArgs a;
+  a.w = to_kernel(w);
+  a.X = X;
+  a.gather = gather;
+  a.offsets = offsets;
+  a.perm = perm;
+  a.active = active;
+  a.n_active = n_active;
+  a.T = T;
+  a.k = k;
+  a.Y = Y;
+  const int64_t rows = (int64_t)T * k;
+  hipError_t e;
+  if (rows <= kGemvMaxRows && w->K <= 16384)
+    e = launch_gemv(a, (hipStream_t)stream);
+  else if (w->K % 64 == 0)
+    e = launch_mfma(a, (hipStream_t)stream);
+  else if (w->K <= 16384)
+    e = launch_gemv(a, (hipStream_t)stream);
+  else
+    return fail(GNF4_ERR_UNSUPPORTED, "MXFP4 with K %% 64 != 0 and K > 16384");
+  return device_status(e, "grouped GEMM launch");
+}
+
+gnf4_status gnf4_combine(const float *Y, const int32_t *inv, const float *topk_w, int32_t T,
+                         int32_t k, int32_t N, float *out, gnf4_stream_t stream) {
+  if (k < 1 || k > 64) return fail(GNF4_ERR_INVALID_ARG, "k = %d outside [1, 64]", k);
+  if (T < 0) return fail(GNF4_ERR_INVALID_ARG, "T = %d is negative", T);
+  if (N < 4 || N % 4 || N > GNF4_MAX_N)
+    return fail(GNF4_ERR_INVALID_ARG, "N = %d must be a positive multiple of 4 up to %d", N,
+                GNF4_MAX_N);
+  if ((int64_t)T * k >= ((int64_t)1 << 31) - 1024)
+    return fail(GNF4_ERR_INVALID_ARG, "T*k too large");
+  if (T == 0) return ok();
+  if (!Y || !inv || !topk_w || !out) return fail(GNF4_ERR_INVALID_ARG, "a pointer argument is NULL");
+  if (!aligned16(Y) || !aligned16(out))
+    return fail(GNF4_ERR_INVALID_ARG, "Y and out must be 16-byte aligned");
+  return device_status(launch_combine(Y, inv, topk_w, T, k, N, out, (hipStream_t)stream),
+                       "combine launch");
+}
+
+gnf4_status gnf4_dequant(const gnf4_weights *w, int32_t e, float *out, gnf4_stream_t stream) {
+  gnf4_status st = check_weights(w);
+  if (st != GNF4_OK) return st;
+  if (e < 0 || e >= w->E) return fail(GNF4_ERR_INVALID_ARG, "expert %d outside [0, %d)", e, w->E);
+  if (!out) return fail(GNF4_ERR_INVALID_ARG, "out is NULL");
+  if ((int64_t)w->N * w->K / 32 > 0x7fffffffLL * 256)
+    return fail(GNF4_ERR_UNSUPPORTED, "expert too large");
+  Weights k = to_kernel(w);
+  return device_status(launch_dequant(k, e, out, (hipStream_t)stream), "dequant launch");
+}
+
+gnf4_status gnf4_quantize(int32_t format, const float *W, int32_t rows, int32_t K, uint8_t *codes,
+                          void *scales, float *scales2, gnf4_stream_t stream) {
+  if (format < GNF4_NF4 || format > GNF4_MXFP4)
+    return fail(GNF4_ERR_INVALID_ARG, "unknown format %d", format);
+  const int blk = format == GNF4_MXFP4 ? 32 : 64;
+  if (K < blk || K % blk || K > GNF4_MAX_K)
+    return fail(GNF4_ERR_INVALID_ARG, "K = %d must be a positive multiple of %d up to %d", K, blk,
+                GNF4_MAX_K);
+  if (rows < 0) return fail(GNF4_ERR_INVALID_ARG, "rows = %d is negative", rows);
+  if (rows == 0) return ok();
+  if (!W || !codes || !scales) return fail(GNF4_ERR_INVALID_ARG, "a pointer argument is NULL");
+  if (format == GNF4_NF4_DQ && !scales2) return fail(GNF4_ERR_INVALID_ARG, "NF4_DQ needs scales2");
+  if (!aligned16(codes) || ((uintptr_t)W & 3u))
+    return fail(GNF4_ERR_INVALID_ARG, "codes must be 16-byte and W 4-byte aligned");
+  if ((int64_t)rows * (K / 32) > 0x7fffffffLL * 200)
+    return fail(GNF4_ERR_UNSUPPORTED, "weight tensor too large");
+  return device_status(launch_quantize(format, W, rows, K, codes, scales, scales2,
+                                       (hipStream_t)stream),
+                       "quantize launch");
+}
+
+void gnf4_nf4_codebook(float out[16]) {
+  if (!out) return;
+  for (int i = 0; i < 16; ++i) {
+    uint32_t b = kNF4Bits[i];
+    std::memcpy(&out[i], &b, 4);
+  }
+}
+
+const char *gnf4_last_error(void) { return g_err; }
+
+const char *gnf4_build_id(void) { return "gnf4 " GNF4_REVISION " gfx950"; }
+
+}  // extern "C"

@@ -1,0 +1,139 @@
+// Shared device-side definitions for the gnf4 kernels (gfx950 / CDNA4).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/gnf4.h"
+
+namespace gnf4 {
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+// NF4 codebook, float32 bit patterns, index = 4-bit code. These are the 16
+// NormalFloat-4 values of the QLoRA construction (8 positive and 7 negative
+// N(0,1) quantiles from offset (1-1/30 + 1-1/32)/2, an exact zero, normalised
+// to [-1, 1]) rounded to float32.
+static constexpr uint32_t kNF4Bits[16] = {
+    0xbf800000u, 0xbf3239b1u, 0xbf066b2eu, 0xbeca329eu, 0xbe91a24bu, 0xbe3d353du,
+    0xbdba7869u, 0x00000000u, 0x3da2fb01u, 0x3e24cadfu, 0x3e7c04dau, 0x3ead0336u,
+    0x3ee1a4b5u, 0x3f1007a9u, 0x3f3913b0u, 0x3f800000u};
+
+// bfloat16 of each codebook value (round to nearest even of kNF4Bits).
+__host__ __device__ constexpr uint32_t bf16_rne(uint32_t f) {
+  return (f + 0x7fffu + ((f >> 16) & 1u)) >> 16;
+}
+
+// e2m1 magnitudes by the low three code bits.
+static constexpr float kE2M1[8] = {0.0f, 0.5f, 1.0f, 1.5f, 2.0f, 3.0f, 4.0f, 6.0f};
+
+// float32 value 2^(s-127) of an e8m0 byte: s = 0 is the subnormal 2^-127,
+// s = 255 is NaN.
+__device__ __forceinline__ float e8m0_to_f32(uint32_t s) {
+  uint32_t bits = (s == 0u) ? 0x00400000u : (s == 255u ? 0x7fc00000u : (s << 23));
+  return __builtin_bit_cast(float, bits);
+}
+
+// Kernel-side view of the weights.
+struct Weights {
+  int32_t format, E, N, K;
+  const uint8_t *codes;
+  const void *scales;
+  const float *scales2;
+};
+
+struct GemmArgs {
+  Weights w;
+  const uint16_t *X;
+  int32_t gather;
+  const int32_t *offsets;
+  const int32_t *perm;
+  const int32_t *active;
+  const int32_t *n_active;
+  int32_t T, k;
+  float *Y;
+};
+
+// NF4 byte -> two bf16 codebook values as one dword (element 2i, the high
+// nibble, in the low half): the operand layout of v_dot2 and of the MFMA
+// fragments, where consecutive K values sit low half first.
+__host__ __device__ constexpr uint32_t nf4_pair(uint32_t byte) {
+  return bf16_rne(kNF4Bits[byte >> 4]) | (bf16_rne(kNF4Bits[byte & 15u]) << 16);
+}
+
+// LDS decode table of NF4 byte pairs, replicated once per lane of a wave so
+// that every lane reads its own bank: entry b of copy c lives at byte offset
+// b * 256 + c * 4. 256 entries x 64 copies x 4 B = 64 KiB.
+constexpr int kLutCopies = 64;
+constexpr int kLutWords = 256 * kLutCopies;
+
+// bf16 of codebook value q (0..15) without memory: the 16 values packed into
+// four 64-bit constants.
+__device__ __forceinline__ uint32_t nf4_bf16(uint32_t q) {
+  constexpr uint64_t w0 = (uint64_t)bf16_rne(kNF4Bits[0]) | ((uint64_t)bf16_rne(kNF4Bits[1]) << 16) |
+                          ((uint64_t)bf16_rne(kNF4Bits[2]) << 32) | ((uint64_t)bf16_rne(kNF4Bits[3]) << 48);
+  constexpr uint64_t w1 = (uint64_t)bf16_rne(kNF4Bits[4]) | ((uint64_t)bf16_rne(kNF4Bits[5]) << 16) |
+                          ((uint64_t)bf16_rne(kNF4Bits[6]) << 32) | ((uint64_t)bf16_rne(kNF4Bits[7]) << 48);
+  constexpr uint64_t w2 = (uint64_t)bf16_rne(kNF4Bits[8]) | ((uint64_t)bf16_rne(kNF4Bits[9]) << 16) |
+                          ((uint64_t)bf16_rne(kNF4Bits[10]) << 32) | ((uint64_t)bf16_rne(kNF4Bits[11]) << 48);
+  constexpr uint64_t w3 = (uint64_t)bf16_rne(kNF4Bits[12]) | ((uint64_t)bf16_rne(kNF4Bits[13]) << 16) |
+                          ((uint64_t)bf16_rne(kNF4Bits[14]) << 32) | ((uint64_t)bf16_rne(kNF4Bits[15]) << 48);
+  const uint64_t w = (q < 8u) ? ((q < 4u) ? w0 : w1) : ((q < 12u) ? w2 : w3);
+  return (uint32_t)(w >> ((q & 3u) * 16u)) & 0xffffu;
+}
+
+// Fill the table with a 256-thread workgroup. Thread t writes 16-byte groups
+// g = t + 256 i (i = 0..15), i.e. 4 copies of entry b = g / 16 = t / 16 + 16 i.
+// For that entry the high nibble (element 2i of the pair) is i and the low
+// nibble is t / 16, so each thread decodes one value and ORs in constants;
+// consecutive lanes write consecutive 16-byte groups (no bank conflicts).
+__device__ __forceinline__ void fill_nf4_lut_256(uint32_t *lut, int tid) {
+  const uint32_t lo = nf4_bf16((uint32_t)tid >> 4) << 16;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const uint32_t v = bf16_rne(kNF4Bits[i]) | lo;
+    *reinterpret_cast<uint4 *>(lut + (tid + 256 * i) * 4) = make_uint4(v, v, v, v);
+  }
+}
+
+// Byte offset into the table for byte i (0..3) of dword w, for this lane:
+// v_perm_b32 places byte i of w in bits 8..15 and this lane's copy offset
+// (lane * 4, < 256) in bits 0..7, so one instruction forms the address.
+__device__ __forceinline__ uint32_t lut_addr(uint32_t w, uint32_t lane4, int i) {
+  return __builtin_amdgcn_perm(w, lane4, 0x0c0c0000u | ((4u + (uint32_t)i) << 8));
+}
+
+__device__ __forceinline__ uint32_t lut_read(const uint32_t *lut, uint32_t byte_off) {
+  return *reinterpret_cast<const uint32_t *>(reinterpret_cast<const char *>(lut) + byte_off);
+}
+
+// MXFP4 byte i (0..3) of dword w -> two bf16 (low nibble first), times scale.
+template <int I>
+__device__ __forceinline__ uint32_t fp4_pair(uint32_t w, float scale) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, I));
+}
+
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                         __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+// Host-side launchers (one per kernel family), defined in the .hip files.
+hipError_t launch_route(const int32_t *ids, int32_t T, int32_t k, int32_t E, int32_t *counts,
+                        int32_t *offsets, int32_t *perm, int32_t *inv, int32_t *active,
+                        int32_t *n_active, int32_t *bad, hipStream_t s);
+hipError_t launch_gemv(const GemmArgs &a, hipStream_t s);
+hipError_t launch_mfma(const GemmArgs &a, hipStream_t s);
+hipError_t launch_combine(const float *Y, const int32_t *inv, const float *w, int32_t T,
+                          int32_t k, int32_t N, float *out, hipStream_t s);
+hipError_t launch_dequant(const Weights &w, int32_t e, float *out, hipStream_t s);
+hipError_t launch_quantize(int32_t fmt, const float *W, int32_t rows, int32_t K, uint8_t *codes,
+                           void *scales, float *scales2, hipStream_t s);
+
+// Number of compute units of the current device (cached per device).
+int device_cu_count();
+
+}  // namespace gnf4

@@ -1,0 +1,214 @@
+"""Python binding of libgnf4 (ctypes): argument marshalling only.
+
+Every step of the path runs in the HIP library; this module checks tensor
+placement, allocates outputs with torch (device memory is torch's), passes raw
+device pointers and torch's current HIP stream, and raises on a non-OK status.
+There is no fallback: if the library is missing or a call fails, it raises.
+
+Names follow the C ABI in include/gnf4.h: route, grouped_gemm, combine,
+dequant, quantize, nf4_codebook, last_error, build_id.
+"""
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgnf4.so")
+
+NF4, NF4_DQ, MXFP4 = 0, 1, 2
+FORMATS = {"nf4": NF4, "nf4_dq": NF4_DQ, "mxfp4": MXFP4}
+STATUS = {0: "OK", 1: "INVALID_ARG", 2: "UNSUPPORTED", 4: "DEVICE"}
+
+# Every entry point declared in include/gnf4.h.
+EXPORTS = ("gnf4_route", "gnf4_grouped_gemm", "gnf4_combine", "gnf4_dequant", "gnf4_quantize",
+           "gnf4_nf4_codebook", "gnf4_last_error", "gnf4_build_id")
+
+
+class Gnf4Error(RuntimeError):
+    def __init__(self, status, what):
+        super().__init__("%s failed with %s: %s" % (what, STATUS.get(status, status), last_error()))
+        self.status = status
+
+
+class CWeights(ctypes.Structure):
+    _fields_ = [("format", ctypes.c_int32), ("E", ctypes.c_int32), ("N", ctypes.c_int32),
+                ("K", ctypes.c_int32), ("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p),
+                ("scales2", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def lib():
+    """Load libgnf4.so (built in-tree by bit_mixture_experts_topk_amd.build)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libgnf4.so is not built; run `python -m bit_mixture_experts_topk_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I, S = ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p
+        L.gnf4_route.argtypes = [P, I, I, I, P, P, P, P, P, P, P, S]
+        L.gnf4_grouped_gemm.argtypes = [ctypes.POINTER(CWeights), P, I, P, P, P, P, I, I, P, S]
+        L.gnf4_combine.argtypes = [P, P, P, I, I, I, P, S]
+        L.gnf4_dequant.argtypes = [ctypes.POINTER(CWeights), I, P, S]
+        L.gnf4_quantize.argtypes = [I, P, I, I, P, P, P, S]
+        L.gnf4_nf4_codebook.argtypes = [ctypes.POINTER(ctypes.c_float)]
+        L.gnf4_nf4_codebook.restype = None
+        L.gnf4_last_error.restype = ctypes.c_char_p
+        L.gnf4_build_id.restype = ctypes.c_char_p
+        for name in ("gnf4_route", "gnf4_grouped_gemm", "gnf4_combine", "gnf4_dequant", "gnf4_quantize"):
+            getattr(L, name).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def last_error():
+    return lib().gnf4_last_error().decode()
+
+
+def build_id():
+    return lib().gnf4_build_id().decode()
+
+
+def nf4_codebook():
+    buf = (ctypes.c_float * 16)()
+    lib().gnf4_nf4_codebook(buf)
+    return [buf[i] for i in range(16)]
+
+
+def _check(status, what):
+    if status != 0:
+        raise Gnf4Error(status, what)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dev(t, dtype, name):
+    if not (t.is_cuda and t.dtype == dtype and t.is_contiguous()):
+        raise ValueError("%s must be a contiguous %s CUDA tensor" % (name, dtype))
+    return t
+
+
+@dataclass
+class PackedWeights:
+    """Packed experts of one projection: W [E, N, K] in a 4-bit format."""
+    format: int
+    E: int
+    N: int
+    K: int
+    codes: torch.Tensor                  # uint8 [E, N, K/2]
+    scales: torch.Tensor                 # float32 / int8 / uint8 per format
+    scales2: Optional[torch.Tensor] = None
+
+    def cstruct(self):
+        return CWeights(self.format, self.E, self.N, self.K, self.codes.data_ptr(),
+                        self.scales.data_ptr(),
+                        self.scales2.data_ptr() if self.scales2 is not None else None)
+
+    def nbytes(self):
+        n = self.codes.numel() + self.scales.numel() * self.scales.element_size()
+        if self.scales2 is not None:
+            n += self.scales2.numel() * 4
+        return n
+
+
+def empty_packed(fmt, E, N, K, device="cuda"):
+    fmt = FORMATS.get(fmt, fmt)
+    codes = torch.empty((E, N, K // 2), dtype=torch.uint8, device=device)
+    scales2 = None
+    if fmt == MXFP4:
+        scales = torch.empty((E, N, K // 32), dtype=torch.uint8, device=device)
+    elif fmt == NF4:
+        scales = torch.empty((E, N, K // 64), dtype=torch.float32, device=device)
+    else:
+        scales = torch.empty((E, N, K // 64), dtype=torch.int8, device=device)
+        nb = E * N * (K // 64)
+        scales2 = torch.empty(((nb + 255) // 256,), dtype=torch.float32, device=device)
+    return PackedWeights(fmt, E, N, K, codes, scales, scales2)
+
+
+def quantize(fmt, W, out=None):
+    """Pack float32 W [E, N, K] (CUDA) with gnf4_quantize."""
+    fmt = FORMATS.get(fmt, fmt)
+    _dev(W, torch.float32, "W")
+    E, N, K = W.shape
+    pw = out if out is not None else empty_packed(fmt, E, N, K, W.device)
+    _check(lib().gnf4_quantize(fmt, _ptr(W), E * N, K, _ptr(pw.codes), _ptr(pw.scales),
+                               _ptr(pw.scales2), _stream()), "gnf4_quantize")
+    return pw
+
+
+def quantize_into(fmt, W, pw, e0):
+    """Pack float32 W [n, N, K] into experts [e0, e0 + n) of pw."""
+    fmt = FORMATS.get(fmt, fmt)
+    _dev(W, torch.float32, "W")
+    n, N, K = W.shape
+    if fmt == NF4_DQ:
+        raise ValueError("NF4_DQ groups span experts; quantize the whole layer at once")
+    codes = pw.codes[e0:e0 + n]
+    scales = pw.scales[e0:e0 + n]
+    _check(lib().gnf4_quantize(fmt, _ptr(W), n * N, K, _ptr(codes), _ptr(scales), None, _stream()),
+           "gnf4_quantize")
+
+
+def route_buffers(T, k, E, device="cuda"):
+    """Output buffers for route(): counts, offsets, perm, inv, active, n_active, bad."""
+    i32 = dict(dtype=torch.int32, device=device)
+    return {"counts": torch.empty(E, **i32), "offsets": torch.empty(E + 1, **i32),
+            "perm": torch.empty(max(T * k, 1), **i32), "inv": torch.empty(max(T * k, 1), **i32),
+            "active": torch.empty(E, **i32), "n_active": torch.empty(1, **i32),
+            "bad": torch.empty(1, **i32)}
+
+
+def route(topk_ids, E, out=None):
+    """Route int32 topk_ids [T, k] (CUDA) over E experts; returns a dict of tensors."""
+    _dev(topk_ids, torch.int32, "topk_ids")
+    T, k = topk_ids.shape
+    r = dict(out) if out is not None else route_buffers(T, k, E, topk_ids.device)
+    _check(lib().gnf4_route(_ptr(topk_ids), T, k, E, _ptr(r["counts"]), _ptr(r["offsets"]),
+                            _ptr(r["perm"]), _ptr(r["inv"]), _ptr(r["active"]),
+                            _ptr(r["n_active"]), _ptr(r["bad"]), _stream()), "gnf4_route")
+    r["perm"] = r["perm"][:T * k]
+    r["inv"] = r["inv"][:T * k]
+    return r
+
+
+def grouped_gemm(w, X, gather, r, T, k, Y=None):
+    """Y [T*k, N] float32 = grouped GEMM of bf16 X over the routed rows."""
+    if not (X.is_cuda and X.is_contiguous() and X.element_size() == 2):
+        raise ValueError("X must be a contiguous bf16 (or 16-bit bit pattern) CUDA tensor")
+    if Y is None:
+        Y = torch.empty((max(T * k, 1), w.N), dtype=torch.float32, device=X.device)
+    cw = w.cstruct()
+    _check(lib().gnf4_grouped_gemm(ctypes.byref(cw), _ptr(X), gather, _ptr(r["offsets"]),
+                                   _ptr(r["perm"]), _ptr(r["active"]), _ptr(r["n_active"]),
+                                   T, k, _ptr(Y), _stream()), "gnf4_grouped_gemm")
+    return Y
+
+
+def combine(Y, inv, topk_w, T, k, out=None):
+    _dev(Y, torch.float32, "Y")
+    _dev(topk_w, torch.float32, "topk_w")
+    N = Y.shape[1]
+    if out is None:
+        out = torch.empty((max(T, 1), N), dtype=torch.float32, device=Y.device)
+    _check(lib().gnf4_combine(_ptr(Y), _ptr(inv), _ptr(topk_w), T, k, N, _ptr(out), _stream()),
+           "gnf4_combine")
+    return out
+
+
+def dequant(w, e):
+    out = torch.empty((w.N, w.K), dtype=torch.float32, device=w.codes.device)
+    cw = w.cstruct()
+    _check(lib().gnf4_dequant(ctypes.byref(cw), e, _ptr(out), _stream()), "gnf4_dequant")
+    return out

@@ -1,0 +1,156 @@
+/* gnf4.h -- grouped 4-bit mixture-of-experts GEMM for AMD MI355X (gfx950).
+ *
+ * The operation. A mixture-of-experts layer whose experts are stored 4-bit
+ * packed: one call computes every active expert's matmul directly on the
+ * packed bytes, decoding the 16-entry codebook in registers, without writing
+ * dequantized bf16 weights anywhere (Jordan Anderson,
+ * jordananderson-pages.pages.dev, section "grouped-nf4-gemm & experts-4bit",
+ * first bullet; GitHub profile pjordanandrsn, grouped-nf4-gemm bullets). The
+ * packed bytes are consumed as stored: NF4 on the bitsandbytes layout and
+ * MXFP4 on a checkpoint's released bytes (same section, third bullet).
+ *
+ * A layer step is three calls on one stream:
+ *   gnf4_route          top-k expert ids -> per-expert row segments
+ *   gnf4_grouped_gemm   Y[p] = A[p] . W[expert(p)]^T for every routed row p
+ *   gnf4_combine        out[t] = sum_j w[t,j] * Y[inv[t*k+j]]
+ *
+ * Conventions for every entry point:
+ *  - All array pointers are DEVICE pointers owned by the caller; the library
+ *    never frees or retains them and allocates no device memory.
+ *  - Calls are asynchronous on `stream` (a hipStream_t; NULL = the null
+ *    stream) and never synchronize with the host.
+ *  - Arguments are validated on the host before anything is launched; a
+ *    failure returns a non-zero status, launches nothing and leaves the
+ *    reason in gnf4_last_error() (per calling thread).
+ *  - Two calls that write the same outputs race unless ordered by the
+ *    caller's streams; the library keeps no state between calls apart from
+ *    the per-thread error text.
+ *
+ * Weight layout. The experts of a layer are one fused [E, N, K] parameter
+ * (Jordan Anderson, jordananderson.work, experts4bit-qlora entry, first
+ * bullet) computing Y = X . W[e]^T (N output features, K input features):
+ *   codes   uint8 [E][N][K/2], two 4-bit codes per byte along K.
+ *           NF4 / NF4_DQ: element 2i in the HIGH nibble (bitsandbytes order).
+ *           MXFP4:        element 2i in the LOW nibble (gpt-oss byte order).
+ *   scales  NF4:    float32 absmax [E][N][K/64]
+ *           NF4_DQ: int8 q8 [E][N][K/64]; absmax = fp32(q8 * scales2[b/256])
+ *                   where b is the flat block index e*N*(K/64) + n*(K/64) + j
+ *           MXFP4:  uint8 e8m0 [E][N][K/32]; scale 2^(s-127), s = 255 is NaN
+ *   scales2 NF4_DQ only: float32 [ceil(E*N*(K/64)/256)]; else NULL.
+ * NF4 codebook: the 16 NormalFloat-4 values (QLoRA construction) in float32,
+ * readable with gnf4_nf4_codebook().
+ */
+#ifndef GNF4_H
+#define GNF4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t *gnf4_stream_t; /* identical to hipStream_t */
+
+typedef enum {
+  GNF4_OK = 0,
+  GNF4_ERR_INVALID_ARG = 1, /* null pointer, bad size, misalignment */
+  GNF4_ERR_UNSUPPORTED = 2, /* valid but outside what the kernels handle */
+  GNF4_ERR_DEVICE = 4       /* a HIP call or launch failed */
+} gnf4_status;
+
+typedef enum { GNF4_NF4 = 0, GNF4_NF4_DQ = 1, GNF4_MXFP4 = 2 } gnf4_format;
+
+typedef struct {
+  int32_t format;         /* gnf4_format */
+  int32_t E, N, K;        /* experts, output features, input features */
+  const uint8_t *codes;   /* [E][N][K/2], 16-byte aligned */
+  const void *scales;     /* see the layout above */
+  const float *scales2;   /* NF4_DQ only, else NULL */
+} gnf4_weights;
+
+/* Limits checked on the host. */
+#define GNF4_MAX_EXPERTS 1024
+#define GNF4_MAX_K 65536
+#define GNF4_MAX_N 262144
+
+/* gnf4_route -- group the flat top-k assignments f = t*k + j by expert.
+ *
+ * Computes a counting sort of topk_ids (int32 [T][k], row-major):
+ *   counts[e]   number of assignments with id e                   int32 [E]
+ *   offsets     exclusive prefix sum of counts, offsets[E] = total int32 [E+1]
+ *   perm[p]     for p in [offsets[e], offsets[e+1]): the flat indices f with
+ *               id e in ascending f (stable); -1 for p >= offsets[E]  int32 [T*k]
+ *   inv[f]      the p with perm[p] = f; -1 for a dropped assignment int32 [T*k]
+ *   active      ascending experts with counts > 0, then -1        int32 [E]
+ *   n_active    number of active experts                          int32 [1]
+ *   bad_id_flag set to 1 if any id lies outside [0, E) (such entries are
+ *               dropped), else 0                                   int32 [1]
+ * The result is deterministic (no order-dependent atomics). T = 0 is a valid
+ * no-op apart from zeroing counts/offsets/n_active/bad_id_flag and filling
+ * active with -1. Duplicate ids within a token are routed as separate rows.
+ * Limits: 1 <= E <= GNF4_MAX_EXPERTS, 1 <= k <= 64, 0 <= T, T*k < 2^31.
+ * The pages describe the kernel running one launch for all active experts
+ * behind a real router (section cited at the top); the grouping itself is
+ * this library's reading. */
+gnf4_status gnf4_route(const int32_t *topk_ids, int32_t T, int32_t k, int32_t E,
+                       int32_t *counts, int32_t *offsets, int32_t *perm, int32_t *inv,
+                       int32_t *active, int32_t *n_active, int32_t *bad_id_flag,
+                       gnf4_stream_t stream);
+
+/* gnf4_grouped_gemm -- one launch for all active experts.
+ *
+ * For every expert e and routed row p in [offsets[e], offsets[e+1]):
+ *   Y[p][n] = sum_k A[p][k] * W'[e][n][k]       (float32 accumulate)
+ * A[p] = X[perm[p] / k] when gather = 1 (X is bf16 [T][K], the token
+ * activations) and A[p] = X[p] when gather = 0 (X is bf16 [T*k][K], already
+ * in routed order, e.g. the second projection's input). Rows p >= offsets[E]
+ * of Y are not written. W' is the packed weight decoded in registers: NF4 as
+ * bf16(codebook) with the float32 absmax applied to each 64-value partial
+ * sum, MXFP4 exactly (e2m1 * 2^(s-127)). The route outputs (offsets, perm,
+ * active, n_active) must come from gnf4_route with the same T, k, E.
+ * X: uint16 bf16 bits, 16-byte aligned. Y: float32 [T*k][N], 16-byte aligned.
+ * The path (wavefront GEMV for decode, LDS-staged bf16 MFMA for prefill) is
+ * chosen from T*k on the host; nothing is read back from the device. */
+gnf4_status gnf4_grouped_gemm(const gnf4_weights *w, const uint16_t *X, int32_t gather,
+                              const int32_t *offsets, const int32_t *perm,
+                              const int32_t *active, const int32_t *n_active,
+                              int32_t T, int32_t k, float *Y, gnf4_stream_t stream);
+
+/* gnf4_combine -- weighted top-k combine back to tokens.
+ *   out[t][n] = sum_{j=0..k-1} topk_w[t][j] * Y[inv[t*k+j]][n]
+ * float32, j ascending, an assignment with inv = -1 contributes nothing.
+ * Y float32 [T*k][N] (16-byte aligned), inv int32 [T*k], topk_w float32
+ * [T][k], out float32 [T][N] (16-byte aligned). N % 4 == 0. */
+gnf4_status gnf4_combine(const float *Y, const int32_t *inv, const float *topk_w,
+                         int32_t T, int32_t k, int32_t N, float *out, gnf4_stream_t stream);
+
+/* gnf4_dequant -- decode expert e of w to float32 out [N][K] (test aid).
+ * NF4: fp32(c[q] * absmax); NF4_DQ: fp32(c[q] * fp32(q8 * scale2));
+ * MXFP4: e2m1(q) * 2^(s-127), exact (s = 255 gives NaN). */
+gnf4_status gnf4_dequant(const gnf4_weights *w, int32_t e, float *out, gnf4_stream_t stream);
+
+/* gnf4_quantize -- pack float32 weights W [rows][K] (rows = E*N) into the
+ * layout above: NF4 / NF4_DQ block 64 with nearest-code rounding (ties to
+ * the lower code, decided in float64), NF4_DQ with linear int8 absmax and
+ * one float32 scale per 256 blocks, MXFP4 by the OCP MX rule (shared
+ * exponent floor(log2 amax) - 2, round to nearest even, saturate at 6).
+ * W must be finite. codes uint8 [rows][K/2]; scales as the format says;
+ * scales2 float32 [ceil(rows*(K/64)/256)] for NF4_DQ, else ignored. */
+gnf4_status gnf4_quantize(int32_t format, const float *W, int32_t rows, int32_t K,
+                          uint8_t *codes, void *scales, float *scales2, gnf4_stream_t stream);
+
+/* The 16 NF4 codebook values used by every kernel (host copy, float32). */
+void gnf4_nf4_codebook(float out[16]);
+
+/* Thread-local text describing the last non-OK status ("" if none). */
+const char *gnf4_last_error(void);
+
+/* Source revision and target of this build, e.g. "gnf4 1a2b3c4 gfx950". */
+const char *gnf4_build_id(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GNF4_H */

@@ -176,3 +176,23 @@ def random_rows(cfg, rows, N, seed=0, extra=0):
     """float32 [rows, N] N(0,1) matrix (stand-in expert outputs for combine tests)."""
     g = rng(seed, cfg.config_id, T_Y, 0, extra)
     return g.standard_normal((rows, N), dtype=np.float32)
+
+
+def small_layer(E, N, K, T, k, seed=0, distinct=True, gather=1):
+    """A small seeded layer for parity tests at arbitrary shapes.
+
+    Returns dict(W float32 [E, N, K] ~ N(0, 0.02), X bf16 bits ([T, K] when
+    gather else [T*k, K]), ids int32 [T, k], tw float32 [T, k]).
+    distinct: each token picks k different experts (else ids are drawn with
+    replacement, so duplicates occur).
+    """
+    g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 99, E, N, K, T, k])))
+    W = g.standard_normal((E, N, K), dtype=np.float32) * np.float32(W_STD)
+    rows = T if gather else T * k
+    X = f32_to_bf16_bits(g.standard_normal((rows, K), dtype=np.float32))
+    if distinct:
+        ids = np.stack([g.permutation(E)[:k] for _ in range(T)]) if T else np.zeros((0, k))
+    else:
+        ids = g.integers(0, E, size=(T, k))
+    tw = g.random((T, k)).astype(np.float32)
+    return {"W": W, "X": X, "ids": np.asarray(ids, dtype=np.int32).reshape(T, k), "tw": tw}

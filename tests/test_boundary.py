@@ -1,0 +1,124 @@
+"""The C-ABI library loads, exports every declared entry point and rejects
+invalid arguments on the host, before any HIP call (runs without a GPU)."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from oracle import nf4
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gnf4.h")
+
+gnf4 = pytest.importorskip("bit_mixture_experts_topk_amd.gnf4")
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(gnf4.LIB_PATH):
+        pytest.fail("libgnf4.so is not built (run python -m bit_mixture_experts_topk_amd.build)")
+    return gnf4.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gnf4_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_surface():
+    assert declared_functions() == sorted(gnf4.EXPORTS)
+
+
+def test_every_declared_symbol_is_exported(L):
+    for name in declared_functions():
+        assert hasattr(L, name), name
+
+
+def test_build_id(L):
+    bid = gnf4.build_id()
+    assert bid.startswith("gnf4 ") and bid.endswith("gfx950")
+
+
+def test_codebook_matches_oracle(L):
+    got = np.array(gnf4.nf4_codebook(), dtype=np.float32)
+    assert np.array_equal(got.view(np.uint32), nf4.codebook().view(np.uint32))
+
+
+def weights(fmt=0, E=4, N=8, K=64, codes=0x1000, scales=0x2000, scales2=None):
+    return gnf4.CWeights(fmt, E, N, K, codes, scales, scales2)
+
+
+INVALID = 1
+
+
+@pytest.mark.parametrize("kw,msg", [
+    (dict(fmt=7), "unknown format"),
+    (dict(E=0), "E = 0"),
+    (dict(E=2000), "E = 2000"),
+    (dict(N=0), "N = 0"),
+    (dict(K=96), "K = 96"),
+    (dict(fmt=2, K=48), "K = 48"),
+    (dict(codes=0), "NULL"),
+    (dict(codes=0x1008), "16-byte"),
+    (dict(fmt=1), "scales2"),
+])
+def test_gemm_rejects_bad_weights(L, kw, msg):
+    w = weights(**kw)
+    st = L.gnf4_grouped_gemm(ctypes.byref(w), 0x3000, 1, 0x4000, 0x4000, 0x4000, 0x4000, 1, 1,
+                             0x5000, None)
+    assert st == INVALID and msg in gnf4.last_error()
+
+
+def test_gemm_rejects_bad_call_args(L):
+    w = weights()
+    st = L.gnf4_grouped_gemm(ctypes.byref(w), 0x3000, 2, 0x4000, 0x4000, 0x4000, 0x4000, 1, 1, 0x5000, None)
+    assert st == INVALID and "gather" in gnf4.last_error()
+    st = L.gnf4_grouped_gemm(ctypes.byref(w), 0x3008, 1, 0x4000, 0x4000, 0x4000, 0x4000, 1, 1, 0x5000, None)
+    assert st == INVALID and "aligned" in gnf4.last_error()
+    st = L.gnf4_grouped_gemm(ctypes.byref(w), None, 1, 0x4000, 0x4000, 0x4000, 0x4000, 1, 1, 0x5000, None)
+    assert st == INVALID and "NULL" in gnf4.last_error()
+    st = L.gnf4_grouped_gemm(ctypes.byref(w), 0x3000, 1, 0x4000, 0x4000, 0x4000, 0x4000, 1, 65, 0x5000, None)
+    assert st == INVALID and "k = 65" in gnf4.last_error()
+    st = L.gnf4_grouped_gemm(None, 0x3000, 1, 0x4000, 0x4000, 0x4000, 0x4000, 1, 1, 0x5000, None)
+    assert st == INVALID and "descriptor" in gnf4.last_error()
+
+
+def test_gemm_empty_is_ok(L):
+    w = weights()
+    assert L.gnf4_grouped_gemm(ctypes.byref(w), None, 1, None, None, None, None, 0, 2, None, None) == 0
+    assert gnf4.last_error() == ""
+
+
+def test_route_rejects(L):
+    p = 0x1000
+    assert L.gnf4_route(p, 4, 8, 0, p, p, p, p, p, p, p, None) == INVALID
+    assert "E = 0" in gnf4.last_error()
+    assert L.gnf4_route(p, 4, 0, 8, p, p, p, p, p, p, p, None) == INVALID
+    assert L.gnf4_route(p, -1, 2, 8, p, p, p, p, p, p, p, None) == INVALID
+    assert L.gnf4_route(None, 4, 2, 8, p, p, p, p, p, p, p, None) == INVALID
+    assert L.gnf4_route(p, 4, 2, 8, p, None, p, p, p, p, p, None) == INVALID
+
+
+def test_combine_rejects(L):
+    p = 0x1000
+    assert L.gnf4_combine(p, p, p, 2, 2, 6, p, None) == INVALID
+    assert L.gnf4_combine(p, p, p, 2, 0, 8, p, None) == INVALID
+    assert L.gnf4_combine(0x1004, p, p, 2, 2, 8, p, None) == INVALID
+    assert L.gnf4_combine(None, p, p, 2, 2, 8, p, None) == INVALID
+    assert L.gnf4_combine(None, None, None, 0, 2, 8, None, None) == 0
+
+
+def test_dequant_and_quantize_reject(L):
+    w = weights()
+    assert L.gnf4_dequant(ctypes.byref(w), 4, 0x1000, None) == INVALID
+    assert "expert 4" in gnf4.last_error()
+    assert L.gnf4_dequant(ctypes.byref(w), 0, None, None) == INVALID
+    assert L.gnf4_quantize(0, 0x1000, 4, 100, 0x2000, 0x3000, None, None) == INVALID
+    assert L.gnf4_quantize(1, 0x1000, 4, 64, 0x2000, 0x3000, None, None) == INVALID
+    assert L.gnf4_quantize(5, 0x1000, 4, 64, 0x2000, 0x3000, None, None) == INVALID
+    assert L.gnf4_quantize(0, 0x1000, 4, 64, 0x2008, 0x3000, None, None) == INVALID
+    assert L.gnf4_quantize(0, None, 0, 64, None, None, None, None) == 0

@@ -1,0 +1,121 @@
+"""GPU parity, bit-exact: dequantization, quantization and routing."""
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import mxfp4, nf4, routing
+
+from .gpu_util import FMT_ID, check_route, gnf4, oracle_pack, packed_to_device, say
+
+pytestmark = pytest.mark.gpu
+
+ABSMAX = np.array([0.0, 1.0, 2.0 ** -20, 0.0371, 3.5e-39, 1e-45, np.finfo(np.float32).max, 0.06],
+                  dtype=np.float32)
+
+
+def test_dequant_nf4_every_byte_and_absmax():
+    g = gnf4()
+    # expert 0: row r uses absmax ABSMAX[r % 8]; bytes cycle through 0..255
+    N, K = 16, 512
+    codes = (np.arange(N * K // 2) % 256).astype(np.uint8).reshape(1, N, K // 2)
+    scales = np.resize(ABSMAX, N * K // 64).reshape(1, N, K // 64).astype(np.float32)
+    say("dequant nf4 all bytes")
+    pw = packed_to_device(g, "nf4", codes, scales, None, 1, N, K)
+    got = g.dequant(pw, 0).cpu().numpy()
+    with np.errstate(over="ignore"):
+        ref = nf4.dequantize(codes[0], scales[0], K)
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+
+
+def test_dequant_nf4_dq():
+    g = gnf4()
+    W = synth.small_layer(3, 40, 192, 1, 1, seed=5)["W"]
+    codes, q8, s2 = nf4.quantize_dq(W)
+    pw = packed_to_device(g, "nf4_dq", codes, q8, s2, 3, 40, 192)
+    for e in range(3):
+        say("dequant nf4_dq expert", e)
+        got = g.dequant(pw, e).cpu().numpy()
+        a = nf4.dq_absmax(q8, s2).reshape(3, 40, 3)[e]
+        ref = nf4.dequantize(codes[e], a, 192)
+        assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+
+
+def test_dequant_mxfp4_every_scale_and_code():
+    g = gnf4()
+    N, K = 256, 32
+    row = mxfp4.pack(np.tile(np.arange(16, dtype=np.uint8), 2))
+    codes = np.tile(row, (N, 1)).reshape(1, N, K // 2)
+    scales = np.arange(256, dtype=np.uint8).reshape(1, N, 1)
+    say("dequant mxfp4 all scales")
+    pw = packed_to_device(g, "mxfp4", codes, scales, None, 1, N, K)
+    got = g.dequant(pw, 0).cpu().numpy()
+    ref = mxfp4.dequantize(codes[0], scales[0], K)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan].view(np.uint32), ref[~nan].view(np.uint32))
+
+
+def adversarial_weights(fmt, E=2, N=24, K=256):
+    W = synth.small_layer(E, N, K, 1, 1, seed=11)["W"].copy()
+    flat = W.reshape(-1, 64 if fmt != "mxfp4" else 32)
+    flat[0] = 0.0                                   # all-zero block
+    flat[1] = 1e-40                                 # subnormal block
+    flat[2, :] = -0.0
+    flat[3] *= 1e30                                 # large magnitudes
+    c = nf4.codebook().astype(np.float64)
+    mids = (c[:-1] + c[1:]) / 2
+    ties = [np.float32(m) for m in mids if float(np.float32(m)) == m]
+    flat[4, 0] = 1.0
+    for j, v in enumerate(ties):
+        flat[4, 1 + j] = v                          # exact NF4 midpoints (absmax 1)
+    if fmt == "mxfp4":
+        flat[5] = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 7.0, -0.25, -5.0] * 3 + [6.0, 4.0],
+                           dtype=np.float32)       # e2m1 ties with scale 2^0
+    return W
+
+
+@pytest.mark.parametrize("fmt", ["nf4", "nf4_dq", "mxfp4"])
+def test_quantize_matches_oracle(fmt):
+    g = gnf4()
+    for W in (adversarial_weights(fmt), synth.small_layer(4, 96, 2880 if fmt == "mxfp4" else 1536,
+                                                          1, 1, seed=3)["W"]):
+        E, N, K = W.shape
+        say("quantize", fmt, W.shape)
+        pw = g.quantize(fmt, torch.from_numpy(W).cuda())
+        codes, scales, scales2 = oracle_pack(fmt, W)
+        assert np.array_equal(pw.codes.cpu().numpy().reshape(-1), codes.reshape(-1))
+        assert np.array_equal(pw.scales.cpu().numpy().reshape(-1).view(np.uint8),
+                              np.ascontiguousarray(scales).reshape(-1).view(np.uint8))
+        if scales2 is not None:
+            assert np.array_equal(pw.scales2.cpu().numpy().view(np.uint32), scales2.view(np.uint32))
+
+
+ROUTE_CASES = [("tiny", 16), ("olmoe", 1), ("olmoe", 512), ("qwen30", 1), ("qwen30", 8),
+               ("qwen30", 2048), ("qwen235", 1), ("qwen235", 4096), ("gptoss", 1), ("gptoss", 2048),
+               ("mixtral", 2048)]
+
+
+@pytest.mark.parametrize("name,T", ROUTE_CASES)
+def test_route_workloads(name, T):
+    g = gnf4()
+    cfg = synth.CONFIGS[name]
+    ids, _ = synth.routing_inputs(cfg, T)
+    say("route", name, T)
+    r = g.route(torch.from_numpy(ids).cuda(), cfg.E)
+    check_route(r, routing.route(ids, cfg.E), T * cfg.k)
+    r2 = g.route(torch.from_numpy(ids).cuda(), cfg.E)
+    for key in r:
+        assert torch.equal(r[key], r2[key]), key       # deterministic
+
+
+@pytest.mark.parametrize("E,T,k", [(1, 5, 1), (7, 33, 3), (1024, 100, 8), (300, 4000, 8), (5, 0, 4)])
+def test_route_edge_cases(E, T, k):
+    g = gnf4()
+    rs = np.random.default_rng(E * 1000 + T)
+    ids = rs.integers(-2, E + 2, size=(T, k)).astype(np.int32)   # duplicates and bad ids
+    say("route edge", E, T, k)
+    r = g.route(torch.from_numpy(ids).cuda().reshape(T, k), E)
+    ref = routing.route(ids, E)
+    check_route(r, ref, T * k)
