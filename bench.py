@@ -49,7 +49,44 @@ def parse():
     ap.add_argument("--only", choices=["decode", "prefill"], default=None)
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
+    ap.add_argument("--kernel-only", choices=["decode", "prefill"], default=None,
+                    help="launch only the gate_up grouped GEMM of one step, --steps times "
+                         "(for hardware-counter passes); prints no JSON")
+    ap.add_argument("--proj", default=None, help="projection for --kernel-only (default gate_up)")
     return ap.parse_args()
+
+
+def kernel_only(args):
+    """One grouped-GEMM launch shape, repeated: the unit that counter passes measure."""
+    import torch
+
+    import synth
+    from bit_mixture_experts_topk_amd import gnf4
+    gnf4.lib()
+    cfg = synth.CONFIGS[args.config]
+    proj = cfg.proj(args.proj) if args.proj else cfg.projs[0]
+    T = min(cfg.Ts) if args.kernel_only == "decode" else max(cfg.Ts)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(17 * cfg.config_id + 1)
+    pw = gnf4.empty_packed(cfg.fmt, cfg.E, proj.N, proj.K)
+    W = torch.randn((cfg.E, proj.N, proj.K), generator=g, device="cuda") * 0.02
+    gnf4.quantize(cfg.fmt, W, pw)
+    del W
+    ids, _ = synth.routing_inputs(cfg, T)
+    rows = T if proj.gather else T * cfg.k
+    X = torch.from_numpy(synth.activations(cfg, rows, proj.K, synth.T_X, 0, T).view(np.int16)).cuda()
+    r = gnf4.route(torch.from_numpy(ids).cuda(), cfg.E)
+    Y = torch.empty((T * cfg.k, proj.N), dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    for _ in range(args.steps):
+        gnf4.grouped_gemm(pw, X, proj.gather, r, T, cfg.k, Y)
+    if args.calib_copy:
+        a = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+        b = torch.empty_like(a)
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print("kernel-only %s %s %s T=%d x%d done" % (cfg.name, proj.name, args.kernel_only, T,
+                                                  args.steps), file=sys.stderr, flush=True)
 
 
 def packed_bytes_per_expert(pw):
@@ -179,12 +216,21 @@ def time_kernel(torch, gnf4, slots, steps, warmup):
         gnf4.grouped_gemm(sl.layer.projs[0], sl.X, 1, sl.r, sl.T, cfg.k, sl.Y[0])
         evs[i][1].record()
     torch.cuda.synchronize()
-    ms = np.array([a.elapsed_time(b) for a, b in evs])
+    # The same event pair with nothing between: its mean is the cost of the
+    # event packets themselves, subtracted from every kernel measurement.
+    empty = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+             for _ in range(steps)]
+    for a, b in empty:
+        a.record()
+        b.record()
+    torch.cuda.synchronize()
+    overhead = float(np.mean([a.elapsed_time(b) for a, b in empty]))
+    ms = np.array([a.elapsed_time(b) for a, b in evs]) - overhead
     byts = np.array([slots[i % len(slots)].n_active * slots[i % len(slots)].layer.projs[0].nbytes()
                      // cfg.E for i in range(steps)], dtype=np.float64)
     fl = np.array([2.0 * slots[i % len(slots)].T * cfg.k * slots[i % len(slots)].layer.projs[0].N
                    * slots[i % len(slots)].layer.projs[0].K for i in range(steps)])
-    return float(ms.mean()), float(byts.mean()), float(fl.mean())
+    return float(ms.mean()), float(byts.mean()), float(fl.mean()), overhead
 
 
 def cpu_baseline(cfg, T):
@@ -253,6 +299,9 @@ def main():
         print("bench.py measures one GPU: this build has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
         sys.exit(2)
+    if args.kernel_only:
+        kernel_only(args)
+        return
     import torch
 
     import synth
@@ -283,9 +332,10 @@ def main():
         for sl in slots:
             sl.capture(torch, gnf4)
         dt, byts, _ = time_steps(torch, slots, args.steps, args.warmup)
-        kms, kbytes, _ = time_kernel(torch, gnf4, slots, args.steps, args.warmup)
+        kms, kbytes, _, ovh = time_kernel(torch, gnf4, slots, args.steps, args.warmup)
         out["decode"] = dict(T=T_dec, ms_per_step=dt * 1e3, gbs=byts / dt / 1e9,
-                             kernel_us=kms * 1e3, kernel_bytes=kbytes, copies=copies)
+                             kernel_us=kms * 1e3, kernel_bytes=kbytes, copies=copies,
+                             event_us=ovh * 1e3)
         del slots, layers
         torch.cuda.empty_cache()
     if prefill_ok:
@@ -297,7 +347,7 @@ def main():
             sl.capture(torch, gnf4)
         steps = max(10, args.steps // 10)
         dt, byts, fl = time_steps(torch, slots, steps, max(2, args.warmup // 5))
-        kms, kbytes, kfl = time_kernel(torch, gnf4, slots, steps, max(2, args.warmup // 5))
+        kms, kbytes, kfl, _ = time_kernel(torch, gnf4, slots, steps, max(2, args.warmup // 5))
         out["prefill"] = dict(T=T_pre, ms_per_step=dt * 1e3, tflops=fl / dt / 1e12,
                               kernel_us=kms * 1e3, kernel_flops=kfl, copies=copies)
         del slots, layers
@@ -327,6 +377,7 @@ def main():
                               "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
                               "kernel": "gemv_kernel (gate_up, T=%d)" % d["T"],
                               "kernel_us": round(d["kernel_us"], 3),
+                              "event_overhead_us": round(d["event_us"], 3),
                               "bytes_per_launch": int(d["kernel_bytes"])}
         result["decode"] = {"step_us": round(d["ms_per_step"] * 1e3, 3),
                             "pct_hbm_peak_step": round(100 * d["gbs"] / HBM_PEAK_GBS, 2),

@@ -89,8 +89,10 @@ static Weights to_kernel(const gnf4_weights *w) {
   return k;
 }
 
-// Decode path for T*k routed rows at or below this count.
+// Decode path for T*k routed rows at or below this count, and the largest K
+// its register-resident token slices cover.
 constexpr int kGemvMaxRows = 64;
+constexpr int kGemvMaxK = 8192;
 
 }  // namespace gnf4
 
@@ -145,14 +147,14 @@ gnf4_status gnf4_grouped_gemm(const gnf4_weights *w, const uint16_t *X, int32_t 
   a.Y = Y;
   const int64_t rows = (int64_t)T * k;
   hipError_t e;
-  if (rows <= kGemvMaxRows && w->K <= 16384)
+  if (rows <= kGemvMaxRows && w->K <= kGemvMaxK)
     e = launch_gemv(a, (hipStream_t)stream);
   else if (w->K % 64 == 0)
     e = launch_mfma(a, (hipStream_t)stream);
-  else if (w->K <= 16384)
+  else if (w->K <= kGemvMaxK)
     e = launch_gemv(a, (hipStream_t)stream);
   else
-    return fail(GNF4_ERR_UNSUPPORTED, "MXFP4 with K %% 64 != 0 and K > 16384");
+    return fail(GNF4_ERR_UNSUPPORTED, "MXFP4 with K %% 64 != 0 needs K <= %d", kGemvMaxK);
   return device_status(e, "grouped GEMM launch");
 }
 

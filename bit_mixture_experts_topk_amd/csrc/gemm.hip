@@ -85,7 +85,7 @@ struct GemvUnroll {
 
 template <int FMT, int MT, int C>
 __global__ __launch_bounds__(kThreads, 2) void gemv_kernel(GemmArgs a, int L_log2,
-                                                           int items_per_expert) {
+                                                           int items_per_expert, int max_slots) {
   constexpr int U = GemvUnroll<MT, C>::value;
   constexpr bool kLut = FMT != GNF4_MXFP4;
   __shared__ uint32_t lut[kLut ? kLutWords : 1];
@@ -97,39 +97,42 @@ __global__ __launch_bounds__(kThreads, 2) void gemv_kernel(GemmArgs a, int L_log
   const int li = lane & (L - 1), seg = lane >> L_log2;
   const int N = a.w.N, K = a.w.K, KCH = K >> 5;
   const int rows_per_item = 4 * RW * U;
-  const int nact = *a.n_active;
-  const int64_t nitems = (int64_t)nact * items_per_expert;
+  const int64_t nitems = (int64_t)max_slots * items_per_expert;
   bool lut_ready = !kLut;
+
+  uint4 q[U][C];
+  float sc[U][C];
+  // All code and scale loads of one item (rows n0 + (u*4 + wave)*RW + seg).
+#define GNF4_GEMV_LOAD_ROWS()                                                             \
+  _Pragma("unroll") for (int u = 0; u < U; ++u) {                                        \
+    const int r = n0 + (u * 4 + wave) * RW + seg;                                         \
+    const int64_t row = (int64_t)e * N + r;                                               \
+    _Pragma("unroll") for (int c = 0; c < C; ++c) {                                      \
+      const int ch = li + c * L;                                                          \
+      if (r < N && ch < KCH) {                                                            \
+        q[u][c] = *reinterpret_cast<const uint4 *>(a.w.codes + row * (K / 2) + ch * 16);  \
+        sc[u][c] = chunk_scale<FMT>(a.w, row, ch);                                        \
+      } else {                                                                            \
+        q[u][c] = make_uint4(0u, 0u, 0u, 0u);                                             \
+        sc[u][c] = 0.f;                                                                   \
+      }                                                                                   \
+    }                                                                                     \
+  }
 
   for (int64_t item = blockIdx.x; item < nitems; item += gridDim.x) {
     const int slot = (int)(item / items_per_expert);
     const int ib = (int)(item - (int64_t)slot * items_per_expert);
+    // The only load the weight stream waits for: the expert of this slot
+    // (-1 past the active count).
     const int e = a.active[slot];
+    if (e < 0) continue;
+    const int n0 = ib * rows_per_item;
+    GNF4_GEMV_LOAD_ROWS();
     const int p0 = a.offsets[e];
     const int m = a.offsets[e + 1] - p0;
-    const int n0 = ib * rows_per_item;
 
     for (int tg = 0; tg < m; tg += MT) {
-      // Weight rows first: every code and scale load of this item is issued
-      // before anything waits.
-      uint4 q[U][C];
-      float sc[U][C];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int r = n0 + (u * 4 + wave) * RW + seg;
-        const int64_t row = (int64_t)e * N + r;
-#pragma unroll
-        for (int c = 0; c < C; ++c) {
-          const int ch = li + c * L;
-          if (r < N && ch < KCH) {
-            q[u][c] = *reinterpret_cast<const uint4 *>(a.w.codes + row * (K / 2) + ch * 16);
-            sc[u][c] = chunk_scale<FMT>(a.w, row, ch);
-          } else {
-            q[u][c] = make_uint4(0u, 0u, 0u, 0u);
-            sc[u][c] = 0.f;
-          }
-        }
-      }
+      if (tg > 0) GNF4_GEMV_LOAD_ROWS();   // more tokens than MT: stream the rows again
 
       // Token slices in registers: x[t][c][i] holds the bf16 pair for K values
       // 32*ch + 2i, +1 of chunk ch = li + c*L.
@@ -210,6 +213,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemv_kernel(GemmArgs a, int L_log
       }
     }
   }
+#undef GNF4_GEMV_LOAD_ROWS
 }
 
 // ===================================================================== MFMA
@@ -313,31 +317,36 @@ __global__ __launch_bounds__(kThreads, 2) void mfma_kernel(GemmArgs a, int n_til
 
   // Two-slot rings (slot 0 holds even steps, slot 1 odd steps), as separate
   // named arrays so that they stay in registers.
-  static_assert(kALoads == 2, "");
+  static_assert(kALoads == 2, "A staging holds two 16-byte segments per thread (BM = 64)");
   uint4 areg0_0, areg0_1, areg1_0, areg1_1;
   uint4 bq0[TN], bq1[TN];
-  float bs0[TN], bs1[TN];
+  uint2 bs0[TN], bs1[TN];   // raw block-scale bits (x; NF4_DQ: y = scale2)
 
 #define GNF4_LOAD_A(KB, DST)                                                              \
   DST##_0 = *reinterpret_cast<const uint4 *>(xsrc[0] + (KB) * 64);                       \
   DST##_1 = *reinterpret_cast<const uint4 *>(xsrc[1] + (KB) * 64);
-#define GNF4_LOAD_B(KB, BQ, BS)                                                           \
+#define GNF4_LOAD_B(KB, BQ)                                                               \
+  _Pragma("unroll") for (int tn = 0; tn < TN; ++tn)                                      \
+      BQ[tn] = *reinterpret_cast<const uint4 *>(bsrc[tn] + (KB) * 32);
+#define GNF4_LOAD_S(KB, BS)                                                               \
   _Pragma("unroll") for (int tn = 0; tn < TN; ++tn) {                                    \
-    BQ[tn] = *reinterpret_cast<const uint4 *>(bsrc[tn] + (KB) * 32);                      \
+    /* raw scale bits only: converting here would wait for the load */                  \
     if constexpr (FMT == GNF4_MXFP4) {                                                    \
-      BS[tn] = e8m0_to_f32(                                                               \
-          reinterpret_cast<const uint8_t *>(a.w.scales)[brow[tn] * (K / 32) + 2 * (KB) + g]); \
+      BS[tn].x = reinterpret_cast<const uint8_t *>(a.w.scales)[brow[tn] * (K / 32) + 2 * (KB) + g]; \
     } else if constexpr (FMT == GNF4_NF4) {                                               \
-      BS[tn] = reinterpret_cast<const float *>(a.w.scales)[brow[tn] * (K / 64) + (KB)];   \
+      BS[tn].x = reinterpret_cast<const uint32_t *>(a.w.scales)[brow[tn] * (K / 64) + (KB)]; \
     } else {                                                                              \
       const int64_t blk = brow[tn] * (K / 64) + (KB);                                     \
-      BS[tn] = (float)reinterpret_cast<const int8_t *>(a.w.scales)[blk] * a.w.scales2[blk >> 8]; \
+      BS[tn].x = (uint32_t)(int32_t)reinterpret_cast<const int8_t *>(a.w.scales)[blk];    \
+      BS[tn].y = __builtin_bit_cast(uint32_t, a.w.scales2[blk >> 8]);                     \
     }                                                                                     \
   }
 
-  GNF4_LOAD_B(0, bq0, bs0);
+  GNF4_LOAD_B(0, bq0);
+  GNF4_LOAD_S(0, bs0);
   GNF4_LOAD_A(0, areg0);
-  GNF4_LOAD_B(min(1, nkb - 1), bq1, bs1);
+  GNF4_LOAD_B(min(1, nkb - 1), bq1);
+  GNF4_LOAD_S(min(1, nkb - 1), bs1);
   GNF4_LOAD_A(min(1, nkb - 1), areg1);
   if constexpr (kLut) fill_nf4_lut_256(lut, tid);
   As[0][sdst[0]] = areg0_0; As[0][sdst[1]] = areg0_1;
@@ -346,12 +355,18 @@ __global__ __launch_bounds__(kThreads, 2) void mfma_kernel(GemmArgs a, int n_til
   // entries (refilled with step KB + 2); AN: the next step's A staging.
 #define GNF4_MFMA_STEP(KB, S, AC, AN, BQ, BS)                                             \
   {                                                                                       \
+    /* no instruction crosses a step boundary: a decode hoisted into the */              \
+    /* previous step would wait on loads issued only one step earlier */                 \
+    __builtin_amdgcn_sched_barrier(0);                                                    \
     __syncthreads(); /* As[S] holds step KB; As[S ^ 1] is no longer read */               \
+    __builtin_amdgcn_sched_barrier(0);                                                    \
     bf16x8_t bf[TN][4];                                                                   \
     float scl[TN];                                                                        \
     _Pragma("unroll") for (int tn = 0; tn < TN; ++tn) {                                  \
       const uint32_t qw[4] = {BQ[tn].x, BQ[tn].y, BQ[tn].z, BQ[tn].w};                    \
-      scl[tn] = BS[tn];                                                                   \
+      if constexpr (FMT == GNF4_MXFP4) scl[tn] = e8m0_to_f32(BS[tn].x);                   \
+      else if constexpr (FMT == GNF4_NF4) scl[tn] = __builtin_bit_cast(float, BS[tn].x);  \
+      else scl[tn] = (float)(int32_t)BS[tn].x * __builtin_bit_cast(float, BS[tn].y);      \
       _Pragma("unroll") for (int j = 0; j < 4; ++j) {                                    \
         uint32_t d[4];                                                                    \
         if constexpr (kLut) {                                                             \
@@ -368,31 +383,50 @@ __global__ __launch_bounds__(kThreads, 2) void mfma_kernel(GemmArgs a, int n_til
     }                                                                                     \
     {                                                                                     \
       const int kn = min((KB) + 2, nkb - 1);                                              \
-      GNF4_LOAD_B(kn, BQ, BS);                                                            \
+      GNF4_LOAD_B(kn, BQ);                                                                \
       GNF4_LOAD_A(kn, AC);                                                                \
     }                                                                                     \
     const uint4 *Ab = As[S];                                                              \
+    bf16x8_t af[TM][4];                                                                   \
     _Pragma("unroll") for (int tm = 0; tm < TM; ++tm) {                                  \
       const int r = tm * 32 + nn;                                                         \
-      bf16x8_t af[4];                                                                     \
-      _Pragma("unroll") for (int j = 0; j < 4; ++j) af[j] =                              \
+      _Pragma("unroll") for (int j = 0; j < 4; ++j) af[tm][j] =                          \
           __builtin_bit_cast(bf16x8_t, Ab[r * 8 + ((4 * g + j) ^ (r & 7))]);              \
-      _Pragma("unroll") for (int tn = 0; tn < TN; ++tn) {                                \
-        if constexpr (kLut) {                                                             \
-          f32x16_t P = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[0], bf[tn][0],          \
-                                                               f32x16_t{}, 0, 0, 0);      \
-          P = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[1], bf[tn][1], P, 0, 0, 0);      \
-          P = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[2], bf[tn][2], P, 0, 0, 0);      \
-          P = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[3], bf[tn][3], P, 0, 0, 0);      \
-          _Pragma("unroll") for (int r2 = 0; r2 < 16; ++r2) acc[tm][tn][r2] =            \
-              __builtin_fmaf(scl[tn], P[r2], acc[tm][tn][r2]);                            \
-        } else {                                                                          \
-          _Pragma("unroll") for (int j = 0; j < 4; ++j) acc[tm][tn] =                    \
-              __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[j], bf[tn][j], acc[tm][tn], 0, 0, 0); \
+    }                                                                                     \
+    if constexpr (kLut) {                                                                 \
+      /* tiles in order t = tn * TM + tm; partials alternate between two register */     \
+      /* sets so the scale FMAs of one tile overlap the MFMAs of the next */             \
+      f32x16_t Pp[2];                                                                     \
+      _Pragma("unroll") for (int t = 0; t < TM * TN; ++t) {                              \
+        const int tm = t % TM, tn = t / TM;                                               \
+        f32x16_t P = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[tm][0], bf[tn][0],        \
+                                                             f32x16_t{}, 0, 0, 0);        \
+        P = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[tm][1], bf[tn][1], P, 0, 0, 0);    \
+        P = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[tm][2], bf[tn][2], P, 0, 0, 0);    \
+        P = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[tm][3], bf[tn][3], P, 0, 0, 0);    \
+        if (t > 0) {                                                                      \
+          const int pm = (t - 1) % TM, pn = (t - 1) / TM;                                 \
+          _Pragma("unroll") for (int r2 = 0; r2 < 16; ++r2) acc[pm][pn][r2] =            \
+              __builtin_fmaf(scl[pn], Pp[(t - 1) & 1][r2], acc[pm][pn][r2]);              \
         }                                                                                 \
+        Pp[t & 1] = P;                                                                    \
       }                                                                                   \
+      {                                                                                   \
+        constexpr int t = TM * TN - 1;                                                    \
+        const int pm = t % TM, pn = t / TM;                                               \
+        _Pragma("unroll") for (int r2 = 0; r2 < 16; ++r2) acc[pm][pn][r2] =              \
+            __builtin_fmaf(scl[pn], Pp[t & 1][r2], acc[pm][pn][r2]);                      \
+      }                                                                                   \
+    } else {                                                                              \
+      _Pragma("unroll") for (int tn = 0; tn < TN; ++tn)                                  \
+      _Pragma("unroll") for (int tm = 0; tm < TM; ++tm)                                  \
+      _Pragma("unroll") for (int j = 0; j < 4; ++j) acc[tm][tn] =                        \
+          __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[tm][j], bf[tn][j], acc[tm][tn], 0, 0, 0); \
     }                                                                                     \
     As[(S) ^ 1][sdst[0]] = AN##_0; As[(S) ^ 1][sdst[1]] = AN##_1;                          \
+    /* the scales of step KB + 2 are loaded after this step's last use of BS, so */      \
+    /* the loop-carried register is refilled in place */                                  \
+    GNF4_LOAD_S(min((KB) + 2, nkb - 1), BS);                                              \
   }
 
   int kb = 0;
@@ -404,6 +438,7 @@ __global__ __launch_bounds__(kThreads, 2) void mfma_kernel(GemmArgs a, int n_til
 #undef GNF4_MFMA_STEP
 #undef GNF4_LOAD_A
 #undef GNF4_LOAD_B
+#undef GNF4_LOAD_S
 
   // ---- store: C fragment register r = 4i + j holds row 8i + 4g + j, column nn
 #pragma unroll
@@ -439,7 +474,7 @@ static hipError_t gemv_go(const GemmArgs &a, int L_log2, int max_slots, hipStrea
   const int64_t grid = std::min<int64_t>(upper, 2LL * device_cu_count());
   if (grid <= 0) return hipSuccess;
   hipLaunchKernelGGL((gemv_kernel<FMT, MT, C>), dim3((unsigned)grid), dim3(kThreads), 0, s, a,
-                     L_log2, items);
+                     L_log2, items, max_slots);
   return hipGetLastError();
 }
 
@@ -449,9 +484,7 @@ static hipError_t gemv_pick_c(const GemmArgs &a, int C, int L_log2, int max_slot
     case 1: return gemv_go<FMT, MT, 1>(a, L_log2, max_slots, s);
     case 2: if constexpr (MT <= 4) return gemv_go<FMT, MT, 2>(a, L_log2, max_slots, s); break;
     case 3: if constexpr (MT <= 2) return gemv_go<FMT, MT, 3>(a, L_log2, max_slots, s); break;
-    case 4: if constexpr (MT <= 2) return gemv_go<FMT, MT, 4>(a, L_log2, max_slots, s); break;
-    case 6: if constexpr (MT <= 1) return gemv_go<FMT, MT, 6>(a, L_log2, max_slots, s); break;
-    case 8: if constexpr (MT <= 1) return gemv_go<FMT, MT, 8>(a, L_log2, max_slots, s); break;
+    case 4: if constexpr (MT <= 1) return gemv_go<FMT, MT, 4>(a, L_log2, max_slots, s); break;
   }
   return hipErrorInvalidValue;
 }
@@ -468,11 +501,12 @@ static hipError_t gemv_pick_mt(const GemmArgs &a, int MT, int C, int L_log2, int
 }
 
 // Chunks-per-lane values compiled for each token count (x registers:
-// MT * C * 16 <= 128 per lane).
+// MT * C * 16 <= 96 per lane, so that no variant spills). One token covers
+// K <= 64 lanes * 4 chunks * 32 = 8192.
 static int gemv_c_options(int MT, int *out) {
-  static const int c1[] = {1, 2, 3, 4, 6, 8}, c2[] = {1, 2, 3, 4}, c4[] = {1, 2}, c8[] = {1};
+  static const int c1[] = {1, 2, 3, 4}, c2[] = {1, 2, 3}, c4[] = {1, 2}, c8[] = {1};
   const int *src = MT == 1 ? c1 : MT == 2 ? c2 : MT == 4 ? c4 : c8;
-  const int n = MT == 1 ? 6 : MT == 2 ? 4 : MT == 4 ? 2 : 1;
+  const int n = MT == 1 ? 4 : MT == 2 ? 3 : MT == 4 ? 2 : 1;
   for (int i = 0; i < n; ++i) out[i] = src[i];
   return n;
 }
