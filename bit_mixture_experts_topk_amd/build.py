@@ -34,6 +34,9 @@ def revision():
 def flags():
     return ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            # MFMA results in VGPRs: the NF4 kernels scale every partial with VALU
+            # FMAs, which cannot read accumulation registers
+            "-mllvm", "-amdgpu-mfma-vgpr-form=1",
             "-Wno-unused-command-line-argument",
             '-DGNF4_REVISION="%s"' % revision()]
 

@@ -568,11 +568,6 @@ static hipError_t mfma_go(const GemmArgs &a, hipStream_t s) {
 
 template <int FMT>
 static hipError_t mfma_pick(const GemmArgs &a, hipStream_t s) {
-  // Rows per active expert on average decides the M tile.
-  const int rows = a.T * a.k;
-  const int experts = std::min<int>(a.w.E, rows);
-  const int avg = experts > 0 ? rows / experts : 0;
-  (void)avg;
   return mfma_go<FMT, 2, 2>(a, s);
 }
 
