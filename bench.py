@@ -6,9 +6,10 @@ A step is one pass of the hot path over one batch of synthetic tokens:
 gnf4_route -> gnf4_grouped_gemm (gate_up, rows gathered from the token
 activations) -> gnf4_grouped_gemm (down, input already in routed order) ->
 gnf4_combine. Decode steps (T = 1) and prefill steps (the workload's largest
-T) are captured once per input slot as HIP graphs and replayed; successive
-steps rotate over input slots and over copies of the layer's packed weights
-so that no step finds its weights in the 256 MB Infinity Cache.
+T) are captured as HIP graphs, one per input slot and one chain holding a step
+per slot (as a model captures its layers), and replayed; successive steps
+rotate over input slots and over copies of the layer's packed weights so that
+no step finds its weights in the 256 MB Infinity Cache.
 
 Reported (one JSON line on stdout):
   value      decode packed-weight GB/s of the whole step (codes + scales of
@@ -183,54 +184,77 @@ class StepSlot:
         return sum(2.0 * self.T * self.layer.cfg.k * pw.N * pw.K for pw in self.layer.projs)
 
 
-def time_steps(torch, slots, steps, warmup):
+def capture_chain(torch, gnf4, slots):
+    """One graph holding one step per slot, in slot order: a replay runs
+    len(slots) consecutive steps with no host launch between them."""
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for sl in slots:
+            sl.run(gnf4)
+    torch.cuda.synchronize()
+    return g
+
+
+def time_steps(torch, slots, chain, steps, warmup):
+    """Time exactly `steps` steps: whole replays of the slot chain, then single
+    slot graphs for the remainder. Step i uses slot i % len(slots)."""
+    G = len(slots)
     for i in range(warmup):
-        slots[i % len(slots)].graph.replay()
+        slots[i % G].graph.replay()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(steps):
-        slots[i % len(slots)].graph.replay()
+    for _ in range(steps // G):
+        chain.replay()
+    for i in range(steps - steps % G, steps):
+        slots[i % G].graph.replay()
     torch.cuda.synchronize()
     dt = (time.perf_counter() - t0) / steps
-    per = np.mean([slots[i % len(slots)].weight_bytes() for i in range(steps)])
-    fl = np.mean([slots[i % len(slots)].flops() for i in range(steps)])
+    per = np.mean([slots[i % G].weight_bytes() for i in range(steps)])
+    fl = np.mean([slots[i % G].flops() for i in range(steps)])
     return dt, per, fl
 
 
 def time_kernel(torch, gnf4, slots, steps, warmup):
-    """Mean duration of the gate_up GEMM launch, from HIP events recorded on
-    the stream it is launched on (torch's current stream), over `steps`
-    launches rotating through the slots (route outputs already computed)."""
+    """Mean duration of the gate_up GEMM launch: `steps` launches rotating
+    through the slots (route outputs computed beforehand) are captured in one
+    graph, and HIP events recorded on the replay stream bracket its replays;
+    the mean is elapsed time / launches, so host launch cost is excluded and
+    the gaps between back-to-back launches are included."""
     for sl in slots:
         gnf4.route(sl.ids, sl.layer.cfg.E, out=sl.r)
     torch.cuda.synchronize()
     cfg = slots[0].layer.cfg
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(steps)]
-    for i in range(warmup):
-        sl = slots[i % len(slots)]
-        gnf4.grouped_gemm(sl.layer.projs[0], sl.X, 1, sl.r, sl.T, cfg.k, sl.Y[0])
-    for i in range(steps):
-        sl = slots[i % len(slots)]
-        evs[i][0].record()
-        gnf4.grouped_gemm(sl.layer.projs[0], sl.X, 1, sl.r, sl.T, cfg.k, sl.Y[0])
-        evs[i][1].record()
+    G = max(len(slots), min(steps, 64))
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        for i in range(min(warmup, G)):
+            sl = slots[i % len(slots)]
+            gnf4.grouped_gemm(sl.layer.projs[0], sl.X, 1, sl.r, sl.T, cfg.k, sl.Y[0])
     torch.cuda.synchronize()
-    # The same event pair with nothing between: its mean is the cost of the
-    # event packets themselves, subtracted from every kernel measurement.
-    empty = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-             for _ in range(steps)]
-    for a, b in empty:
-        a.record()
-        b.record()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        for i in range(G):
+            sl = slots[i % len(slots)]
+            gnf4.grouped_gemm(sl.layer.projs[0], sl.X, 1, sl.r, sl.T, cfg.k, sl.Y[0])
     torch.cuda.synchronize()
-    overhead = float(np.mean([a.elapsed_time(b) for a, b in empty]))
-    ms = np.array([a.elapsed_time(b) for a, b in evs]) - overhead
-    byts = np.array([slots[i % len(slots)].n_active * slots[i % len(slots)].layer.projs[0].nbytes()
-                     // cfg.E for i in range(steps)], dtype=np.float64)
-    fl = np.array([2.0 * slots[i % len(slots)].T * cfg.k * slots[i % len(slots)].layer.projs[0].N
-                   * slots[i % len(slots)].layer.projs[0].K for i in range(steps)])
-    return float(ms.mean()), float(byts.mean()), float(fl.mean()), overhead
+    reps = max(2, -(-steps // G))
+    with torch.cuda.stream(stream):
+        graph.replay()                                  # warm
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(reps)]
+        for a, b in evs:
+            a.record(stream)
+            graph.replay()
+            b.record(stream)
+    torch.cuda.synchronize()
+    ms = np.array([a.elapsed_time(b) for a, b in evs]) / G
+    byts = np.mean([slots[i % len(slots)].n_active * slots[i % len(slots)].layer.projs[0].nbytes()
+                    // cfg.E for i in range(G)])
+    fl = np.mean([2.0 * slots[i % len(slots)].T * cfg.k * slots[i % len(slots)].layer.projs[0].N
+                  * slots[i % len(slots)].layer.projs[0].K for i in range(G)])
+    del graph
+    return float(np.median(ms)), float(byts), float(fl), G
 
 
 def cpu_baseline(cfg, T):
@@ -331,12 +355,13 @@ def main():
                  for i in range(max(copies, 16))]
         for sl in slots:
             sl.capture(torch, gnf4)
-        dt, byts, _ = time_steps(torch, slots, args.steps, args.warmup)
-        kms, kbytes, _, ovh = time_kernel(torch, gnf4, slots, args.steps, args.warmup)
+        chain = capture_chain(torch, gnf4, slots)
+        dt, byts, _ = time_steps(torch, slots, chain, args.steps, args.warmup)
+        kms, kbytes, _, glaunch = time_kernel(torch, gnf4, slots, args.steps, args.warmup)
         out["decode"] = dict(T=T_dec, ms_per_step=dt * 1e3, gbs=byts / dt / 1e9,
                              kernel_us=kms * 1e3, kernel_bytes=kbytes, copies=copies,
-                             event_us=ovh * 1e3)
-        del slots, layers
+                             graph_launches=glaunch)
+        del slots, layers, chain
         torch.cuda.empty_cache()
     if prefill_ok:
         copies = int(min(8, max(2, np.ceil(3 * MALL_BYTES / max(layer_bytes, 1)))))
@@ -345,12 +370,13 @@ def main():
                  for i in range(copies)]
         for sl in slots:
             sl.capture(torch, gnf4)
+        chain = capture_chain(torch, gnf4, slots)
         steps = max(10, args.steps // 10)
-        dt, byts, fl = time_steps(torch, slots, steps, max(2, args.warmup // 5))
+        dt, byts, fl = time_steps(torch, slots, chain, steps, max(2, args.warmup // 5))
         kms, kbytes, kfl, _ = time_kernel(torch, gnf4, slots, steps, max(2, args.warmup // 5))
         out["prefill"] = dict(T=T_pre, ms_per_step=dt * 1e3, tflops=fl / dt / 1e12,
                               kernel_us=kms * 1e3, kernel_flops=kfl, copies=copies)
-        del slots, layers
+        del slots, layers, chain
         torch.cuda.empty_cache()
 
     if args.calib_copy:
@@ -377,7 +403,7 @@ def main():
                               "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
                               "kernel": "gemv_kernel (gate_up, T=%d)" % d["T"],
                               "kernel_us": round(d["kernel_us"], 3),
-                              "event_overhead_us": round(d["event_us"], 3),
+                              "launches_per_graph": d["graph_launches"],
                               "bytes_per_launch": int(d["kernel_bytes"])}
         result["decode"] = {"step_us": round(d["ms_per_step"] * 1e3, 3),
                             "pct_hbm_peak_step": round(100 * d["gbs"] / HBM_PEAK_GBS, 2),

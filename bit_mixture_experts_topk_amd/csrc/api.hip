@@ -74,6 +74,8 @@ static gnf4_status check_weights(const gnf4_weights *w) {
     return fail(GNF4_ERR_INVALID_ARG, "scales2 must be 4-byte aligned");
   if ((int64_t)w->E * w->N * (w->K / 2) > (int64_t)1 << 40)
     return fail(GNF4_ERR_UNSUPPORTED, "weight tensor too large");
+  if ((int64_t)w->N * (w->K / 2) >= (int64_t)1 << 32)
+    return fail(GNF4_ERR_UNSUPPORTED, "one expert's packed codes must be below 4 GiB");
   return ok();
 }
 

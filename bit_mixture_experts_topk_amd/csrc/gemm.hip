@@ -60,160 +60,323 @@ __device__ __forceinline__ float group_sum(float v, int L) {
   return v;
 }
 
-// Block scale of 32-value chunk `ch` of weight row `row` (flat e*N + n).
-template <int FMT>
-__device__ __forceinline__ float chunk_scale(const Weights &w, int64_t row, int ch) {
-  if constexpr (FMT == GNF4_MXFP4) {
-    return e8m0_to_f32(reinterpret_cast<const uint8_t *>(w.scales)[row * (w.K / 32) + ch]);
-  } else if constexpr (FMT == GNF4_NF4) {
-    return reinterpret_cast<const float *>(w.scales)[row * (w.K / 64) + (ch >> 1)];
-  } else {
-    const int64_t blk = row * (w.K / 64) + (ch >> 1);
-    return (float)reinterpret_cast<const int8_t *>(w.scales)[blk] * w.scales2[blk >> 8];
-  }
-}
-
 // ===================================================================== GEMV
 
-// Rows in flight per wave-row-slot: about 128 bytes of code loads per lane
-// outstanding for one token, fewer as the token slices take registers.
-template <int MT, int C>
-struct GemvUnroll {
-  static constexpr int raw = (MT >= 4 ? 4 : 8) / (C * (MT >= 2 ? 2 : 1));
-  static constexpr int value = raw < 1 ? 1 : raw;
-};
+// Routed rows whose source activation row the GEMV caches in LDS.
+constexpr int kGemvSrcCache = 1024;
 
-template <int FMT, int MT, int C>
-__global__ __launch_bounds__(kThreads, 2) void gemv_kernel(GemmArgs a, int L_log2,
-                                                           int items_per_expert, int max_slots) {
-  constexpr int U = GemvUnroll<MT, C>::value;
-  constexpr bool kLut = FMT != GNF4_MXFP4;
-  __shared__ uint32_t lut[kLut ? kLutWords : 1];
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const uint32_t lane4 = (uint32_t)lane << 2;
-  const int L = 1 << L_log2;
-  const int RW = 64 >> L_log2;                  // rows per wave slot
-  const int li = lane & (L - 1), seg = lane >> L_log2;
-  const int N = a.w.N, K = a.w.K, KCH = K >> 5;
-  const int rows_per_item = 4 * RW * U;
-  const int64_t nitems = (int64_t)max_slots * items_per_expert;
-  bool lut_ready = !kLut;
-
+// Per-thread register state of one GEMV item: its weight rows.
+template <int U, int C>
+struct GemvRows {
   uint4 q[U][C];
   float sc[U][C];
-  // All code and scale loads of one item (rows n0 + (u*4 + wave)*RW + seg).
-#define GNF4_GEMV_LOAD_ROWS()                                                             \
-  _Pragma("unroll") for (int u = 0; u < U; ++u) {                                        \
-    const int r = n0 + (u * 4 + wave) * RW + seg;                                         \
-    const int64_t row = (int64_t)e * N + r;                                               \
-    _Pragma("unroll") for (int c = 0; c < C; ++c) {                                      \
-      const int ch = li + c * L;                                                          \
-      if (r < N && ch < KCH) {                                                            \
-        q[u][c] = *reinterpret_cast<const uint4 *>(a.w.codes + row * (K / 2) + ch * 16);  \
-        sc[u][c] = chunk_scale<FMT>(a.w, row, ch);                                        \
-      } else {                                                                            \
-        q[u][c] = make_uint4(0u, 0u, 0u, 0u);                                             \
-        sc[u][c] = 0.f;                                                                   \
-      }                                                                                   \
-    }                                                                                     \
-  }
+};
 
-  for (int64_t item = blockIdx.x; item < nitems; item += gridDim.x) {
-    const int slot = (int)(item / items_per_expert);
-    const int ib = (int)(item - (int64_t)slot * items_per_expert);
-    // The only load the weight stream waits for: the expert of this slot
-    // (-1 past the active count).
-    const int e = a.active[slot];
-    if (e < 0) continue;
-    const int n0 = ib * rows_per_item;
-    GNF4_GEMV_LOAD_ROWS();
-    const int p0 = a.offsets[e];
-    const int m = a.offsets[e + 1] - p0;
+// Shape of the GEMV work split, fixed per launch.
+struct GemvGeom {
+  int L_log2, L, RW, li, seg, wave, KCH, rows_per_item;
+};
 
-    for (int tg = 0; tg < m; tg += MT) {
-      if (tg > 0) GNF4_GEMV_LOAD_ROWS();   // more tokens than MT: stream the rows again
-
-      // Token slices in registers: x[t][c][i] holds the bf16 pair for K values
-      // 32*ch + 2i, +1 of chunk ch = li + c*L.
-      uint32_t x[MT][C][16];
+// Issue the code and scale loads of the rows of item block n0 of expert e:
+// wave slot rows n0 + (u*4 + wave)*RW + seg, chunk li + c*L of each. Rows
+// past N and chunks past K/32 load a valid neighbour instead (no predicated
+// loads, so no load waits on an earlier one into the same registers); their
+// results are discarded where they are used. Addresses are a uniform base of
+// the item plus a 32-bit per-lane offset (one expert's packed matrix is
+// below 4 GiB).
+template <int FMT, int U, int C>
+__device__ __forceinline__ void gemv_load_rows(const GemmArgs &a, const GemvGeom &g, int e, int n0,
+                                               GemvRows<U, C> &R) {
+  const int N = a.w.N, K = a.w.K;
+  const int rmax = N - 1 - n0;
+  const int64_t row0 = (int64_t)e * N + n0;
+  const uint8_t *cb = a.w.codes + row0 * (K / 2);
+  uint32_t r[U], ch[C];
 #pragma unroll
-      for (int t = 0; t < MT; ++t) {
-        const bool has = tg + t < m;
-        const int p = p0 + tg + t;
-        const int src = has ? (a.gather ? a.perm[p] / a.k : p) : 0;
-        const uint16_t *xrow = a.X + (int64_t)src * K;
+  for (int u = 0; u < U; ++u) r[u] = (uint32_t)min((u * 4 + g.wave) * g.RW + g.seg, rmax);
 #pragma unroll
-        for (int c = 0; c < C; ++c) {
-          const int ch = li + c * L;
-          if (has && ch < KCH) {
-            const uint4 *s4 = reinterpret_cast<const uint4 *>(xrow + ch * 32);
+  for (int c = 0; c < C; ++c) ch[c] = (uint32_t)min(g.li + c * g.L, g.KCH - 1);
+  // The small scale loads go first and the code rows after them in row
+  // order, so that row u waits only for rows before it.
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const uint4 v = s4[j];
-              x[t][c][4 * j + 0] = v.x;
-              x[t][c][4 * j + 1] = v.y;
-              x[t][c][4 * j + 2] = v.z;
-              x[t][c][4 * j + 3] = v.w;
-            }
-          } else {
+  for (int u = 0; u < U; ++u) {
 #pragma unroll
-            for (int i = 0; i < 16; ++i) x[t][c][i] = 0u;
-          }
-        }
-      }
-
-      // The decode table is built once per workgroup, while the first loads
-      // are in flight.
-      if constexpr (kLut) {
-        if (!lut_ready) {
-          fill_nf4_lut_256(lut, tid);
-          __syncthreads();
-          lut_ready = true;
-        }
-      }
-
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        float acc[MT];
-#pragma unroll
-        for (int t = 0; t < MT; ++t) acc[t] = 0.f;
-#pragma unroll
-        for (int c = 0; c < C; ++c) {
-          float part[MT];
-#pragma unroll
-          for (int t = 0; t < MT; ++t) part[t] = 0.f;
-          const uint32_t qw[4] = {q[u][c].x, q[u][c].y, q[u][c].z, q[u][c].w};
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              uint32_t pair;
-              if constexpr (kLut) {
-                pair = lut_read(lut, lut_addr(qw[j], lane4, i));
-              } else {
-                if (i == 0) pair = fp4_pair<0>(qw[j], 1.0f);
-                else if (i == 1) pair = fp4_pair<1>(qw[j], 1.0f);
-                else if (i == 2) pair = fp4_pair<2>(qw[j], 1.0f);
-                else pair = fp4_pair<3>(qw[j], 1.0f);
-              }
-#pragma unroll
-              for (int t = 0; t < MT; ++t) part[t] = dot2_bf16(pair, x[t][c][4 * j + i], part[t]);
-            }
-          }
-#pragma unroll
-          for (int t = 0; t < MT; ++t) acc[t] = __builtin_fmaf(sc[u][c], part[t], acc[t]);
-        }
-        const int r = n0 + (u * 4 + wave) * RW + seg;
-#pragma unroll
-        for (int t = 0; t < MT; ++t) {
-          const float v = group_sum(acc[t], L);
-          if (li == 0 && r < N && tg + t < m) a.Y[(int64_t)(p0 + tg + t) * N + r] = v;
-        }
+    for (int c = 0; c < C; ++c) {
+      if constexpr (FMT == GNF4_MXFP4) {
+        const uint8_t *sb = reinterpret_cast<const uint8_t *>(a.w.scales) + row0 * (K / 32);
+        R.sc[u][c] = e8m0_to_f32(sb[r[u] * (uint32_t)(K / 32) + ch[c]]);
+      } else if constexpr (FMT == GNF4_NF4) {
+        const float *sb = reinterpret_cast<const float *>(a.w.scales) + row0 * (K / 64);
+        R.sc[u][c] = sb[r[u] * (uint32_t)(K / 64) + (ch[c] >> 1)];
+      } else {
+        const int64_t blk0 = row0 * (K / 64);
+        const uint32_t rb = r[u] * (uint32_t)(K / 64) + (ch[c] >> 1);
+        const int8_t q8 = reinterpret_cast<const int8_t *>(a.w.scales)[blk0 + rb];
+        R.sc[u][c] = (float)q8 * a.w.scales2[(blk0 + rb) >> 8];
       }
     }
   }
-#undef GNF4_GEMV_LOAD_ROWS
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+#pragma unroll
+    for (int c = 0; c < C; ++c)
+      R.q[u][c] = *reinterpret_cast<const uint4 *>(cb + (r[u] * (uint32_t)(K / 2) + ch[c] * 16u));
+}
+
+// Token slices in registers: x[t][c][i] holds the bf16 pair for K values
+// 32*ch + 2i, +1 of chunk ch = li + c*L, for routed rows p0 + tg + t (m >= 1
+// rows from p0). Rows past the segment and chunks past K/32 load valid
+// neighbours; their products are discarded.
+template <int MT, int C>
+__device__ __forceinline__ void gemv_load_x(const GemmArgs &a, const GemvGeom &g, const int *s_src,
+                                            bool src_cached, int p0, int tg, int m,
+                                            uint32_t (&x)[MT][C][16]) {
+  const int K = a.w.K;
+#pragma unroll
+  for (int t = 0; t < MT; ++t) {
+    const int p = p0 + min(tg + t, m - 1);
+    const int src = src_cached ? s_src[p] : (a.gather ? a.perm[p] / a.k : p);
+    const uint16_t *xrow = a.X + (int64_t)src * K;
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+      const int ch = min(g.li + c * g.L, g.KCH - 1);
+      const uint4 *s4 = reinterpret_cast<const uint4 *>(xrow + ch * 32);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint4 v = s4[j];
+        x[t][c][4 * j + 0] = v.x;
+        x[t][c][4 * j + 1] = v.y;
+        x[t][c][4 * j + 2] = v.z;
+        x[t][c][4 * j + 3] = v.w;
+      }
+    }
+  }
+}
+
+// Decode and dot with the token slices; v[u][t] is the product of wave slot
+// row u with token t, summed over its L lanes (every lane of the row group
+// holds it).
+template <int FMT, int MT, int U, int C>
+__device__ __forceinline__ void gemv_dot(const GemvGeom &g, const uint32_t *lut, uint32_t lane4,
+                                         const GemvRows<U, C> &R, const uint32_t (&x)[MT][C][16],
+                                         float (&v)[U][MT]) {
+  constexpr bool kLut = FMT != GNF4_MXFP4;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    float acc[MT];
+#pragma unroll
+    for (int t = 0; t < MT; ++t) acc[t] = 0.f;
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+      float part[MT];
+#pragma unroll
+      for (int t = 0; t < MT; ++t) part[t] = 0.f;
+      const uint32_t qw[4] = {R.q[u][c].x, R.q[u][c].y, R.q[u][c].z, R.q[u][c].w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          uint32_t pair;
+          if constexpr (kLut) {
+            pair = lut_read(lut, lut_addr(qw[j], lane4, i));
+          } else {
+            if (i == 0) pair = fp4_pair<0>(qw[j], 1.0f);
+            else if (i == 1) pair = fp4_pair<1>(qw[j], 1.0f);
+            else if (i == 2) pair = fp4_pair<2>(qw[j], 1.0f);
+            else pair = fp4_pair<3>(qw[j], 1.0f);
+          }
+#pragma unroll
+          for (int t = 0; t < MT; ++t) part[t] = dot2_bf16(pair, x[t][c][4 * j + i], part[t]);
+        }
+      }
+      // A lane past the last chunk adds exactly zero. The mask is applied to
+      // both factors with bitwise ANDs rather than a branch, which would let
+      // the compiler sink this row's loads into it.
+      const uint32_t keep = g.li + c * g.L < g.KCH ? 0xffffffffu : 0u;
+      const float s = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, R.sc[u][c]) & keep);
+#pragma unroll
+      for (int t = 0; t < MT; ++t)
+        acc[t] = __builtin_fmaf(s, __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, part[t]) & keep),
+                                acc[t]);
+    }
+#pragma unroll
+    for (int t = 0; t < MT; ++t) v[u][t] = group_sum(acc[t], g.L);
+  }
+}
+
+// Store v[u][t] to row p0 + tg + t (t < m - tg) of Y, column of wave slot row u.
+template <int MT, int U>
+__device__ __forceinline__ void gemv_store(const GemmArgs &a, const GemvGeom &g,
+                                           const float (&v)[U][MT], int n0, int p0, int tg, int m) {
+  const int N = a.w.N;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int r = n0 + (u * 4 + g.wave) * g.RW + g.seg;
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+      if (g.li == 0 && r < N && tg + t < m) a.Y[(int64_t)(p0 + tg + t) * N + r] = v[u][t];
+  }
+}
+
+// Token slice of activation row `src` (one token), chunks li + c*L (past
+// K/32: a valid neighbour, discarded by the product mask).
+template <int C>
+__device__ __forceinline__ void gemv_load_x_row(const GemmArgs &a, const GemvGeom &g, int src,
+                                                uint32_t (&x)[1][C][16]) {
+  const uint16_t *xrow = a.X + (int64_t)src * a.w.K;
+#pragma unroll
+  for (int c = 0; c < C; ++c) {
+    const int ch = min(g.li + c * g.L, g.KCH - 1);
+    const uint4 *s4 = reinterpret_cast<const uint4 *>(xrow + ch * 32);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint4 v = s4[j];
+      x[0][c][4 * j + 0] = v.x;
+      x[0][c][4 * j + 1] = v.y;
+      x[0][c][4 * j + 2] = v.z;
+      x[0][c][4 * j + 3] = v.w;
+    }
+  }
+}
+
+// GEMV: one workgroup per (active slot, row block) item, blockIdx.x = slot *
+// items_per_expert + block; each wave holds U row slots of C chunks per lane
+// in flight. The small routing arrays (offsets and the source row of every
+// routed row) are read into LDS together with the slot's expert, so that the
+// token slices and then the weight rows are issued back to back on the second
+// memory round trip; the products of each row start as soon as that row
+// has arrived while later rows are still streaming.
+template <int FMT, int MT, int C, int U>
+__global__ __launch_bounds__(kThreads, 2) void gemv_kernel(GemmArgs a, int L_log2,
+                                                           int items_per_expert) {
+  constexpr bool kLut = FMT != GNF4_MXFP4;
+  constexpr int kPer = (GNF4_MAX_EXPERTS + kThreads) / kThreads;   // offsets per thread
+  constexpr int kSrcPer = kGemvSrcCache / kThreads;
+  __shared__ uint32_t lut[kLut ? kLutWords : 1];
+  __shared__ int s_off[GNF4_MAX_EXPERTS + 1];
+  __shared__ int s_src[kGemvSrcCache];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const uint32_t lane4 = (uint32_t)lane << 2;
+  GemvGeom g;
+  g.L_log2 = L_log2;
+  g.L = 1 << L_log2;
+  g.RW = 64 >> L_log2;                          // rows per wave slot
+  g.li = lane & (g.L - 1);
+  g.seg = lane >> L_log2;
+  g.wave = tid >> 6;
+  g.KCH = a.w.K >> 5;
+  g.rows_per_item = 4 * g.RW * U;
+  const int E = a.w.E, rows = a.T * a.k;
+  const int slot = (int)(blockIdx.x / (unsigned)items_per_expert);
+  const int ib = (int)(blockIdx.x - (unsigned)slot * (unsigned)items_per_expert);
+  const bool src_cached = rows <= kGemvSrcCache;
+
+  // ---- first round trip: the expert of this slot, offsets, sources -> LDS
+  const int e = a.active[slot];
+  int vo[kPer], vs[kSrcPer];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int i = tid + j * kThreads;
+    vo[j] = i <= E ? a.offsets[i] : 0;
+  }
+#pragma unroll
+  for (int j = 0; j < kSrcPer; ++j) {
+    const int i = tid + j * kThreads;
+    vs[j] = (src_cached && i < rows) ? (a.gather ? a.perm[i] : i) : 0;
+  }
+  if constexpr (kLut) fill_nf4_lut_256(lut, tid);
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int i = tid + j * kThreads;
+    if (i <= E) s_off[i] = vo[j];
+  }
+#pragma unroll
+  for (int j = 0; j < kSrcPer; ++j) {
+    const int i = tid + j * kThreads;
+    if (src_cached && i < rows) s_src[i] = a.gather ? (vs[j] >= 0 ? vs[j] / a.k : 0) : vs[j];
+  }
+  __syncthreads();
+  if (e < 0) return;                            // slot past the active count
+
+  // ---- second round trip: token slices, then the weight rows
+  const int n0 = ib * g.rows_per_item;
+  const int p0 = s_off[e];
+  const int m = s_off[e + 1] - p0;
+  uint32_t x[MT][C][16];
+  GemvRows<U, C> R;
+  gemv_load_x<MT, C>(a, g, s_src, src_cached, p0, 0, m, x);
+  __builtin_amdgcn_sched_barrier(0);
+  gemv_load_rows<FMT, U, C>(a, g, e, n0, R);
+  __builtin_amdgcn_sched_barrier(0);
+  float v[U][MT];
+  gemv_dot<FMT, MT, U, C>(g, lut, lane4, R, x, v);
+  gemv_store<MT, U>(a, g, v, n0, p0, 0, m);
+  // more routed rows than one token group (an expert routed several times)
+  for (int tg = MT; tg < m; tg += MT) {
+    gemv_load_x<MT, C>(a, g, s_src, src_cached, p0, tg, m, x);
+    gemv_dot<FMT, MT, U, C>(g, lut, lane4, R, x, v);
+    gemv_store<MT, U>(a, g, v, n0, p0, tg, m);
+  }
+}
+
+// GEMV for one token (T = 1): the decode step of a single sequence. The
+// only load the weight stream waits for is the slot's expert. The token
+// slice is known without the routing: a gathered input has one row (token
+// 0); an input already in routed order holds the slot's row at index slot
+// whenever every lower active expert has one routed row, which the offsets
+// confirm at the end (otherwise the rows are streamed again with the right
+// slices). Offsets arrive while the products are computed.
+template <int FMT, int C, int U>
+__global__ __launch_bounds__(kThreads, 2) void gemv1_kernel(GemmArgs a, int L_log2,
+                                                            int items_per_expert) {
+  constexpr bool kLut = FMT != GNF4_MXFP4;
+  __shared__ uint32_t lut[kLut ? kLutWords : 1];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const uint32_t lane4 = (uint32_t)lane << 2;
+  GemvGeom g;
+  g.L_log2 = L_log2;
+  g.L = 1 << L_log2;
+  g.RW = 64 >> L_log2;
+  g.li = lane & (g.L - 1);
+  g.seg = lane >> L_log2;
+  g.wave = tid >> 6;
+  g.KCH = a.w.K >> 5;
+  g.rows_per_item = 4 * g.RW * U;
+  const int slot = (int)(blockIdx.x / (unsigned)items_per_expert);
+  const int ib = (int)(blockIdx.x - (unsigned)slot * (unsigned)items_per_expert);
+
+  const int e = a.active[slot];
+  uint32_t x[1][C][16];
+  gemv_load_x_row<C>(a, g, a.gather ? 0 : slot, x);
+  if constexpr (kLut) fill_nf4_lut_256(lut, tid);
+  if (e < 0) return;                            // whole workgroup: slot past the active count
+  const int n0 = ib * g.rows_per_item;
+  GemvRows<U, C> R;
+  __builtin_amdgcn_sched_barrier(0);
+  gemv_load_rows<FMT, U, C>(a, g, e, n0, R);
+  __builtin_amdgcn_sched_barrier(0);
+  const int p0 = a.offsets[e];
+  const int p1 = a.offsets[e + 1];
+  __syncthreads();                              // decode table written
+  float v[U][1];
+  gemv_dot<FMT, 1, U, C>(g, lut, lane4, R, x, v);
+  const int m = p1 - p0;
+  if (a.gather) {
+    // every routed row of this expert is token 0: same products
+    for (int t = 0; t < m; ++t) gemv_store<1, U>(a, g, v, n0, p0 + t, 0, 1);
+  } else if (m == 1 && p0 == slot) {
+    gemv_store<1, U>(a, g, v, n0, p0, 0, 1);
+  } else {
+    for (int t = 0; t < m; ++t) {               // rows streamed again (rare: repeated experts)
+      gemv_load_x_row<C>(a, g, p0 + t, x);
+      gemv_load_rows<FMT, U, C>(a, g, e, n0, R);
+      gemv_dot<FMT, 1, U, C>(g, lut, lane4, R, x, v);
+      gemv_store<1, U>(a, g, v, n0, p0 + t, 0, 1);
+    }
+  }
 }
 
 // ===================================================================== MFMA
@@ -459,55 +622,70 @@ __global__ __launch_bounds__(kThreads, 2) void mfma_kernel(GemmArgs a, int n_til
 
 // ============================================================ host launch
 
-static int floor_log2(int v) {
-  int r = 0;
-  while ((2 << r) <= v) ++r;
-  return r;
+// Rows per wave slot U compiled for each (tokens per group MT, chunks per lane
+// C): register budget U * C * 5 + MT * C * 16 per lane.
+struct GemvVariant {
+  int MT, C, nu;
+  int U[3];
+};
+static const GemvVariant kGemvVariants[] = {
+    {1, 1, 3, {4, 8, 16}}, {1, 2, 2, {4, 8, 0}}, {1, 3, 2, {2, 4, 0}}, {1, 4, 1, {2, 0, 0}},
+    {2, 1, 2, {2, 4, 0}},  {2, 2, 1, {2, 0, 0}}, {2, 3, 1, {1, 0, 0}},
+    {4, 1, 1, {2, 0, 0}},  {4, 2, 1, {1, 0, 0}}, {8, 1, 1, {2, 0, 0}},
+};
+
+// NF4_DQ rebuilds each absmax from two loads and needs more registers: its
+// rows per wave slot stop at U * C <= 8.
+static bool gemv_fits(int fmt, int C, int U) { return fmt != GNF4_NF4_DQ || C * U <= 8; }
+
+static const GemvVariant *gemv_variant(int MT, int C) {
+  for (const auto &v : kGemvVariants)
+    if (v.MT == MT && v.C == C) return &v;
+  return nullptr;
 }
 
-template <int FMT, int MT, int C>
+template <int FMT, int MT, int C, int U>
 static hipError_t gemv_go(const GemmArgs &a, int L_log2, int max_slots, hipStream_t s) {
   const int L = 1 << L_log2;
-  const int rows_per_item = 4 * (64 / L) * GemvUnroll<MT, C>::value;
+  const int rows_per_item = 4 * (64 / L) * U;
   const int items = (a.w.N + rows_per_item - 1) / rows_per_item;
-  const int64_t upper = (int64_t)max_slots * items;
-  const int64_t grid = std::min<int64_t>(upper, 2LL * device_cu_count());
+  const int64_t grid = (int64_t)max_slots * items;
   if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL((gemv_kernel<FMT, MT, C>), dim3((unsigned)grid), dim3(kThreads), 0, s, a,
-                     L_log2, items, max_slots);
+  if (grid > 0x7fffffff) return hipErrorInvalidValue;
+  if constexpr (MT == 1) {
+    if (a.T == 1) {
+      hipLaunchKernelGGL((gemv1_kernel<FMT, C, U>), dim3((unsigned)grid), dim3(kThreads), 0, s, a,
+                         L_log2, items);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((gemv_kernel<FMT, MT, C, U>), dim3((unsigned)grid), dim3(kThreads), 0, s, a,
+                     L_log2, items);
   return hipGetLastError();
 }
 
-template <int FMT, int MT>
-static hipError_t gemv_pick_c(const GemmArgs &a, int C, int L_log2, int max_slots, hipStream_t s) {
-  switch (C) {
-    case 1: return gemv_go<FMT, MT, 1>(a, L_log2, max_slots, s);
-    case 2: if constexpr (MT <= 4) return gemv_go<FMT, MT, 2>(a, L_log2, max_slots, s); break;
-    case 3: if constexpr (MT <= 2) return gemv_go<FMT, MT, 3>(a, L_log2, max_slots, s); break;
-    case 4: if constexpr (MT <= 1) return gemv_go<FMT, MT, 4>(a, L_log2, max_slots, s); break;
-  }
-  return hipErrorInvalidValue;
-}
+#define GNF4_GEMV_CASE(mt, c, u)                                                 \
+  if constexpr (FMT != GNF4_NF4_DQ || c * u <= 8)                                \
+    if (MT == mt && C == c && U == u) return gemv_go<FMT, mt, c, u>(a, L_log2, max_slots, s);
 
 template <int FMT>
-static hipError_t gemv_pick_mt(const GemmArgs &a, int MT, int C, int L_log2, int max_slots,
-                               hipStream_t s) {
-  switch (MT) {
-    case 1: return gemv_pick_c<FMT, 1>(a, C, L_log2, max_slots, s);
-    case 2: return gemv_pick_c<FMT, 2>(a, C, L_log2, max_slots, s);
-    case 4: return gemv_pick_c<FMT, 4>(a, C, L_log2, max_slots, s);
-    default: return gemv_pick_c<FMT, 8>(a, C, L_log2, max_slots, s);
-  }
+static hipError_t gemv_dispatch(const GemmArgs &a, int MT, int C, int U, int L_log2, int max_slots,
+                                hipStream_t s) {
+  GNF4_GEMV_CASE(1, 1, 4) GNF4_GEMV_CASE(1, 1, 8) GNF4_GEMV_CASE(1, 1, 16)
+  GNF4_GEMV_CASE(1, 2, 4) GNF4_GEMV_CASE(1, 2, 8) GNF4_GEMV_CASE(1, 3, 2) GNF4_GEMV_CASE(1, 3, 4)
+  GNF4_GEMV_CASE(1, 4, 2)
+  GNF4_GEMV_CASE(2, 1, 2) GNF4_GEMV_CASE(2, 1, 4) GNF4_GEMV_CASE(2, 2, 2) GNF4_GEMV_CASE(2, 3, 1)
+  GNF4_GEMV_CASE(4, 1, 2) GNF4_GEMV_CASE(4, 2, 1) GNF4_GEMV_CASE(8, 1, 2)
+  return hipErrorInvalidValue;
 }
+#undef GNF4_GEMV_CASE
 
-// Chunks-per-lane values compiled for each token count (x registers:
-// MT * C * 16 <= 96 per lane, so that no variant spills). One token covers
+// Chunks-per-lane values compiled for each token count. One token covers
 // K <= 64 lanes * 4 chunks * 32 = 8192.
 static int gemv_c_options(int MT, int *out) {
-  static const int c1[] = {1, 2, 3, 4}, c2[] = {1, 2, 3}, c4[] = {1, 2}, c8[] = {1};
-  const int *src = MT == 1 ? c1 : MT == 2 ? c2 : MT == 4 ? c4 : c8;
-  const int n = MT == 1 ? 4 : MT == 2 ? 3 : MT == 4 ? 2 : 1;
-  for (int i = 0; i < n; ++i) out[i] = src[i];
+  int n = 0;
+  for (const auto &v : kGemvVariants)
+    if (v.MT == MT) out[n++] = v.C;
   return n;
 }
 
@@ -537,6 +715,22 @@ bool gemv_shape(int K, int MT, int *L_log2, int *C) {
 
 int gemv_tokens(int T) { return T >= 5 ? 8 : (T >= 3 ? 4 : (T >= 2 ? 2 : 1)); }
 
+// Rows per wave slot: the smallest compiled U (that fits the format's
+// registers) whose grid fits the resident workgroups (two per CU), else the
+// largest that fits; 0 if none does.
+static int gemv_pick_u(const GemvVariant &v, int fmt, int N, int L_log2, int max_slots) {
+  const int64_t target = 2LL * device_cu_count();
+  int last = 0;
+  for (int i = 0; i < v.nu; ++i) {
+    if (!gemv_fits(fmt, v.C, v.U[i])) break;
+    last = v.U[i];
+    const int per = 4 * (64 >> L_log2) * v.U[i];
+    const int64_t items = (int64_t)max_slots * ((N + per - 1) / per);
+    if (items <= target) return v.U[i];
+  }
+  return last;
+}
+
 hipError_t launch_gemv(const GemmArgs &a, hipStream_t s) {
   int MT = gemv_tokens(a.T);
   int L_log2 = 6, C = 1;
@@ -544,11 +738,15 @@ hipError_t launch_gemv(const GemmArgs &a, hipStream_t s) {
     if (MT == 1) return hipErrorInvalidValue;
     MT >>= 1;
   }
+  const GemvVariant *v = gemv_variant(MT, C);
+  if (!v) return hipErrorInvalidValue;
   const int max_slots = std::min<int>(a.w.E, a.T * a.k);
+  const int U = gemv_pick_u(*v, a.w.format, a.w.N, L_log2, max_slots);
+  if (U == 0) return hipErrorInvalidValue;
   switch (a.w.format) {
-    case GNF4_NF4: return gemv_pick_mt<GNF4_NF4>(a, MT, C, L_log2, max_slots, s);
-    case GNF4_NF4_DQ: return gemv_pick_mt<GNF4_NF4_DQ>(a, MT, C, L_log2, max_slots, s);
-    default: return gemv_pick_mt<GNF4_MXFP4>(a, MT, C, L_log2, max_slots, s);
+    case GNF4_NF4: return gemv_dispatch<GNF4_NF4>(a, MT, C, U, L_log2, max_slots, s);
+    case GNF4_NF4_DQ: return gemv_dispatch<GNF4_NF4_DQ>(a, MT, C, U, L_log2, max_slots, s);
+    default: return gemv_dispatch<GNF4_MXFP4>(a, MT, C, U, L_log2, max_slots, s);
   }
 }
 

@@ -36,6 +36,8 @@ __global__ __launch_bounds__(THREADS) void route_kernel(
   __shared__ int sbad, run_c, run_a;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // With one wave all assignments fit one tile: read them once.
+  const int id0 = (THREADS == 64 && tid < n) ? ids[tid] : -1;
   for (int e = tid; e < E; e += THREADS) {
     cursor[e] = 0;
 #pragma unroll
@@ -50,7 +52,7 @@ __global__ __launch_bounds__(THREADS) void route_kernel(
 
   // Histogram of valid ids; ids outside [0, E) only raise the flag.
   for (int f = tid; f < n; f += THREADS) {
-    int e = ids[f];
+    int e = THREADS == 64 ? id0 : ids[f];
     if ((unsigned)e < (unsigned)E)
       atomicAdd(&cursor[e], 1);
     else
@@ -106,7 +108,7 @@ __global__ __launch_bounds__(THREADS) void route_kernel(
   const uint64_t lower = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   for (int base = 0; base < n; base += THREADS) {
     const int f = base + tid;
-    const int e = f < n ? ids[f] : -1;
+    const int e = THREADS == 64 ? id0 : (f < n ? ids[f] : -1);
     const bool valid = (unsigned)e < (unsigned)E;
     uint64_t match = __ballot(valid);
     for (int b = 0; b < nbits; ++b) {

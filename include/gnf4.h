@@ -69,7 +69,9 @@ typedef struct {
   const float *scales2;   /* NF4_DQ only, else NULL */
 } gnf4_weights;
 
-/* Limits checked on the host. */
+/* Limits checked on the host. Besides these, one expert's packed codes
+ * (N * K / 2 bytes) must stay below 4 GiB and all experts' below 1 TiB
+ * (GNF4_ERR_UNSUPPORTED otherwise). */
 #define GNF4_MAX_EXPERTS 1024
 #define GNF4_MAX_K 65536
 #define GNF4_MAX_N 262144

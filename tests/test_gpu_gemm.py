@@ -44,11 +44,16 @@ def test_gemm_small(fmt, shape):
 
 
 @pytest.mark.parametrize("fmt", ["nf4", "mxfp4"])
-@pytest.mark.parametrize("T,k", [(4, 4), (30, 4)])
-def test_gemm_permuted_input(fmt, T, k):
+@pytest.mark.parametrize("T,k,distinct", [(1, 4, True), (1, 6, False), (4, 4, True), (30, 4, True)])
+def test_gemm_permuted_input(fmt, T, k, distinct):
+    """Input already in routed order (the down projection). One token with
+    repeated experts puts the routed rows of later experts past their slot
+    index."""
     g = gnf4()
     E, N, K = 8, 160, 512
-    case = synth.small_layer(E, N, K, T, k, seed=2, gather=0)
+    case = synth.small_layer(E, N, K, T, k, seed=2, gather=0, distinct=distinct)
+    if not distinct:
+        assert len(np.unique(case["ids"])) < k           # the case needs a repeat
     Y, Y_ref, r_ref = run_layer_call(g, fmt, case["W"], case["X"], case["ids"], 0, k, "gather0")
     compare_rows(Y, Y_ref, r_ref, "gather=0 %s T=%d" % (fmt, T))
 
@@ -64,6 +69,35 @@ def test_gemm_duplicates_and_bad_ids(T, k):
     Y, Y_ref, r_ref = run_layer_call(g, "nf4", case["W"], case["X"], ids, 1, k, "dup/bad")
     assert r_ref["bad"][0] == 1
     compare_rows(Y, Y_ref, r_ref, "duplicates and bad ids")
+
+
+@pytest.mark.parametrize("fmt", ["nf4", "nf4_dq", "mxfp4"])
+@pytest.mark.parametrize("E,N,K,T,k", [
+    (4, 192, 4096, 1, 8),      # one token, k > E: every expert gets several copies of token 0
+    (2, 160, 512, 2, 4),       # two tokens, 4 rows per expert: more rows than a token group
+])
+def test_gemv_repeated_rows(fmt, E, N, K, T, k):
+    """Decode path with ids drawn with replacement, so an expert holds more
+    routed rows than the token slice registers cover (rows are streamed
+    again) and, for one token, every row is the same activation."""
+    g = gnf4()
+    case = synth.small_layer(E, N, K, T, k, seed=5, distinct=False)
+    Y, Y_ref, r_ref = run_layer_call(g, fmt, case["W"], case["X"], case["ids"], 1, k, "repeated")
+    compare_rows(Y, Y_ref, r_ref, "repeated rows %s E%d T%d k%d" % (fmt, E, T, k))
+
+
+@pytest.mark.parametrize("fmt", ["nf4", "mxfp4"])
+def test_gemv_more_items_than_workgroups(fmt):
+    """64 routed rows over up to 64 experts with 4096 outputs: more (expert,
+    row block) items than resident workgroups, so each workgroup walks several
+    items with the next item's rows in flight; slots past the active count end
+    the walk."""
+    g = gnf4()
+    E, N, K, T, k = 64, 4096, 64, 8, 8
+    case = synth.small_layer(E, N, K, T, k, seed=6)
+    Y, Y_ref, r_ref = run_layer_call(g, fmt, case["W"], case["X"], case["ids"], 1, k, "many items")
+    assert int(r_ref["n_active"][0]) < E            # some slots are -1
+    compare_rows(Y, Y_ref, r_ref, "many items %s" % fmt)
 
 
 def one_hot_case(fmt, T, k, E=4, N=96, K=256):
@@ -164,11 +198,12 @@ def test_byte_flip_negative_control():
     assert not within(Yb, Yr)
 
 
-@pytest.mark.parametrize("T,k,N", [(16, 2, 512), (3, 8, 2048), (130, 4, 64)])
+@pytest.mark.parametrize("T,k,N", [(16, 2, 512), (3, 8, 2048), (130, 4, 64), (5, 13, 1028),
+                                   (2, 64, 96)])
 def test_combine(T, k, N):
     g = gnf4()
     cfg = synth.CONFIGS["tiny"]
-    E = 16
+    E = max(16, k)
     rs = np.random.default_rng(T)
     ids = np.stack([rs.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
     ids[0, 0] = -1                                  # a dropped assignment
