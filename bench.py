@@ -257,6 +257,27 @@ def time_kernel(torch, gnf4, slots, steps, warmup):
     return float(np.median(ms)), float(byts), float(fl), G
 
 
+def profile_traffic(cfg_name, mode):
+    """HBM bytes per launch of the gate_up kernel from the committed rocprofv3
+    counter summary for this workload, if the GEMM source is unchanged since
+    the counters were taken (else None)."""
+    import glob
+    import hashlib
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*-gate_up-%s-%s.txt" % (cfg_name, mode)))):
+        fields = {}
+        for line in open(path):
+            if ":" in line and not line.startswith(" "):
+                key, _, val = line.partition(":")
+                fields[key.strip()] = val.strip()
+        src = fields.get("kernel_source")
+        if not src or "traffic_bytes_per_launch" not in fields:
+            continue
+        digest = hashlib.sha256(open(os.path.join(ROOT, src), "rb").read()).hexdigest()
+        if digest == fields.get("source_sha256"):
+            return int(fields["traffic_bytes_per_launch"]), os.path.relpath(path, ROOT)
+    return None, None
+
+
 def cpu_baseline(cfg, T):
     """The float64 oracle on one decode step of this workload (route, both
     projections' dequant + matmul for the routed experts, combine)."""
@@ -399,8 +420,10 @@ def main():
         result["value"] = round(d["gbs"], 2)
         result["ms_per_step"] = round(d["ms_per_step"], 5)
         ach = d["kernel_bytes"] / (d["kernel_us"] * 1e-6) / 1e9
+        traffic, tsrc = profile_traffic(cfg.name, "decode")
         result["roofline"] = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
-                              "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
+                              "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic,
+                              "traffic_unit": "HBM bytes/launch", "traffic_source": tsrc,
                               "kernel": "gemv_kernel (gate_up, T=%d)" % d["T"],
                               "kernel_us": round(d["kernel_us"], 3),
                               "launches_per_graph": d["graph_launches"],
@@ -411,12 +434,14 @@ def main():
     if "prefill" in out:
         p = out["prefill"]
         kt = p["kernel_flops"] / (p["kernel_us"] * 1e-6) / 1e12
+        ptraffic, ptsrc = profile_traffic(cfg.name, "prefill")
         result["prefill"] = {"T": p["T"], "step_ms": round(p["ms_per_step"], 4),
                              "tflops": round(p["tflops"], 2),
                              "pct_mfma_peak_step": round(100 * p["tflops"] / BF16_PEAK_TFLOPS, 2),
                              "roofline": {"bound": "mfma", "achieved": round(kt, 2),
                                           "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                                          "frac": round(kt / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                                          "frac": round(kt / BF16_PEAK_TFLOPS, 4), "traffic": ptraffic,
+                                          "traffic_unit": "HBM bytes/launch", "traffic_source": ptsrc,
                                           "kernel": "mfma_kernel (gate_up, T=%d)" % p["T"],
                                           "kernel_us": round(p["kernel_us"], 2)}}
         if "decode" not in out:
