@@ -389,6 +389,45 @@ __device__ __forceinline__ int xcd_remap(int bid, int grid) {
   return (bid & 7) * per + (bid >> 3);
 }
 
+// XOR swizzle of the 8 16-byte K segments of activation row r in LDS. An
+// MFMA A-fragment read has lanes 0..31 on 32 consecutive rows at one
+// logical segment; with r & 7 alone, rows r and r + 8 land on the same banks
+// within the lanes the LDS serves together. Folding r >> 3 in separates them.
+__device__ __forceinline__ int a_swizzle(int r) { return (r ^ (r >> 3)) & 7; }
+
+// Tile enumeration shared by the MFMA kernels: expert by expert (ascending),
+// ceil(count / BM) M tiles each, N-tile major within the expert. Returns the
+// expert of logical tile `bid` (-1 past the last tile), the first logical
+// tile of that expert and its M-tile count. Uniform per wave.
+template <int BM>
+__device__ __forceinline__ void find_tile(const GemmArgs &a, int bid, int n_tiles_n, int lane,
+                                          int &e, int &start, int &tiles) {
+  e = -1;
+  start = 0;
+  tiles = 0;
+  int base = 0;
+  for (int e0 = 0; e0 < a.w.E && e < 0; e0 += 64) {
+    const int ee = e0 + lane;
+    int t = 0;
+    if (ee < a.w.E) t = (a.offsets[ee + 1] - a.offsets[ee] + BM - 1) / BM;
+    int incl = t;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int u = __shfl_up(incl, d, 64);
+      if (lane >= d) incl += u;
+    }
+    const int lo = (base + incl - t) * n_tiles_n, hi = (base + incl) * n_tiles_n;
+    const uint64_t hit = __ballot(t > 0 && bid >= lo && bid < hi);
+    if (hit) {
+      const int src = __builtin_ctzll(hit);
+      e = e0 + src;
+      start = __shfl(lo, src, 64);
+      tiles = __shfl(t, src, 64);
+    }
+    base += __shfl(incl, 63, 64);
+  }
+}
+
 // Tile: BM = 32*TM activation rows x BN = 4*32*TN weight rows (output
 // columns). The 4 waves split N: wave w owns columns [w*32*TN, (w+1)*32*TN)
 // and all BM rows, so every weight column is decoded by exactly one wave.
@@ -406,36 +445,13 @@ __global__ __launch_bounds__(kThreads, 2) void mfma_kernel(GemmArgs a, int n_til
   __shared__ uint4 As[2][kSegs];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int E = a.w.E, N = a.w.N, K = a.w.K;
+  const int N = a.w.N, K = a.w.K;
 
-  // ---- which tile: walk experts, ceil(count/BM) M-tiles x n_tiles_n N-tiles each
-  const int bid = xcd_remap(blockIdx.x, gridDim.x);
-  int e = -1, start = 0, tiles = 0;
-  {
-    int base = 0;
-    for (int e0 = 0; e0 < E && e < 0; e0 += 64) {
-      const int ee = e0 + lane;
-      int t = 0;
-      if (ee < E) t = (a.offsets[ee + 1] - a.offsets[ee] + BM - 1) / BM;
-      int incl = t;
-#pragma unroll
-      for (int d = 1; d < 64; d <<= 1) {
-        const int u = __shfl_up(incl, d, 64);
-        if (lane >= d) incl += u;
-      }
-      const int lo = (base + incl - t) * n_tiles_n, hi = (base + incl) * n_tiles_n;
-      const uint64_t hit = __ballot(t > 0 && bid >= lo && bid < hi);
-      if (hit) {
-        const int src = __builtin_ctzll(hit);
-        e = e0 + src;
-        start = __shfl(lo, src, 64);
-        tiles = __shfl(t, src, 64);
-      }
-      base += __shfl(incl, 63, 64);
-    }
-  }
+  // ---- which tile
+  int e, start, tiles;
+  find_tile<BM>(a, xcd_remap(blockIdx.x, gridDim.x), n_tiles_n, lane, e, start, tiles);
   if (e < 0) return;                        // past the last tile (uniform per workgroup)
-  const int local = bid - start;
+  const int local = xcd_remap(blockIdx.x, gridDim.x) - start;
   const int nt = local / tiles, mt = local - nt * tiles;
   const int seg_start = a.offsets[e];
   const int count = a.offsets[e + 1] - seg_start;
@@ -454,7 +470,7 @@ __global__ __launch_bounds__(kThreads, 2) void mfma_kernel(GemmArgs a, int n_til
     const int p = row0 + min(r, rows_valid - 1);          // padding rows repeat a valid row
     const int src = a.gather ? a.perm[p] / a.k : p;
     xsrc[i] = a.X + (int64_t)src * K + sg * 8;
-    sdst[i] = r * 8 + (sg ^ (r & 7));
+    sdst[i] = r * 8 + (sg ^ a_swizzle(r));
   }
 
   // ---- B: lane (g, nn) holds K values [32g, 32g + 32) of column nn of each N sub-tile
@@ -554,23 +570,27 @@ __global__ __launch_bounds__(kThreads, 2) void mfma_kernel(GemmArgs a, int n_til
     _Pragma("unroll") for (int tm = 0; tm < TM; ++tm) {                                  \
       const int r = tm * 32 + nn;                                                         \
       _Pragma("unroll") for (int j = 0; j < 4; ++j) af[tm][j] =                          \
-          __builtin_bit_cast(bf16x8_t, Ab[r * 8 + ((4 * g + j) ^ (r & 7))]);              \
+          __builtin_bit_cast(bf16x8_t, Ab[r * 8 + ((4 * g + j) ^ a_swizzle(r))]);         \
     }                                                                                     \
     if constexpr (kLut) {                                                                 \
       /* tiles in order t = tn * TM + tm; partials alternate between two register */     \
-      /* sets so the scale FMAs of one tile overlap the MFMAs of the next */             \
+      /* sets. Each MFMA of tile t is followed by 4 of the 16 scale FMAs of tile */      \
+      /* t - 1, and the schedule is pinned to that order, so the VALU FMAs run */         \
+      /* while the MFMA pipe works on the chain instead of after it. */                  \
       f32x16_t Pp[2];                                                                     \
+      __builtin_amdgcn_sched_barrier(0);                                                  \
       _Pragma("unroll") for (int t = 0; t < TM * TN; ++t) {                              \
         const int tm = t % TM, tn = t / TM;                                               \
-        f32x16_t P = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[tm][0], bf[tn][0],        \
-                                                             f32x16_t{}, 0, 0, 0);        \
-        P = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[tm][1], bf[tn][1], P, 0, 0, 0);    \
-        P = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[tm][2], bf[tn][2], P, 0, 0, 0);    \
-        P = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[tm][3], bf[tn][3], P, 0, 0, 0);    \
-        if (t > 0) {                                                                      \
-          const int pm = (t - 1) % TM, pn = (t - 1) / TM;                                 \
-          _Pragma("unroll") for (int r2 = 0; r2 < 16; ++r2) acc[pm][pn][r2] =            \
-              __builtin_fmaf(scl[pn], Pp[(t - 1) & 1][r2], acc[pm][pn][r2]);              \
+        const int pm = (t + TM * TN - 1) % TM, pn = ((t + TM * TN - 1) / TM) % TN;        \
+        f32x16_t P = f32x16_t{};                                                          \
+        _Pragma("unroll") for (int j = 0; j < 4; ++j) {                                  \
+          P = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[tm][j], bf[tn][j], P, 0, 0, 0);  \
+          if (t > 0) {                                                                    \
+            _Pragma("unroll") for (int r2 = 4 * j; r2 < 4 * j + 4; ++r2) acc[pm][pn][r2] = \
+                __builtin_fmaf(scl[pn], Pp[(t - 1) & 1][r2], acc[pm][pn][r2]);            \
+          }                                                                               \
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                              \
+          if (t > 0) __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);                   \
         }                                                                                 \
         Pp[t & 1] = P;                                                                    \
       }                                                                                   \
@@ -580,6 +600,7 @@ __global__ __launch_bounds__(kThreads, 2) void mfma_kernel(GemmArgs a, int n_til
         _Pragma("unroll") for (int r2 = 0; r2 < 16; ++r2) acc[pm][pn][r2] =              \
             __builtin_fmaf(scl[pn], Pp[t & 1][r2], acc[pm][pn][r2]);                      \
       }                                                                                   \
+      __builtin_amdgcn_sched_barrier(0);                                                  \
     } else {                                                                              \
       _Pragma("unroll") for (int tn = 0; tn < TN; ++tn)                                  \
       _Pragma("unroll") for (int tm = 0; tm < TM; ++tm)                                  \
@@ -617,6 +638,244 @@ __global__ __launch_bounds__(kThreads, 2) void mfma_kernel(GemmArgs a, int n_til
           const int r = tm * 32 + 8 * i + 4 * g + j;
           if (r < rows_valid) a.Y[(int64_t)(row0 + r) * N + col] = acc[tm][tn][4 * i + j];
         }
+    }
+}
+
+// ======================================== MFMA 16x16x32, full-line weight loads (NF4)
+
+// The NF4 prefill kernel. Tile 64 activation rows x 256 weight columns per
+// workgroup; wave w owns columns [64w, 64w + 64) as four 16-column tiles and
+// all 64 rows as four 16-row tiles, with v_mfma_f32_16x16x32_bf16.
+//
+// Weights advance in stages of 128 K values (two NF4 blocks = one 64-byte
+// line per column). Lane L loads 16 bytes, piece p = L >> 4 of the stage, of
+// column L & 15 of a column tile: one load instruction covers 16 whole
+// lines, and the data already sits in the B operand's lanes (column L & 15,
+// K group L >> 4). Pieces 0-1 are block 0 and pieces 2-3 block 1; two
+// v_permlane32_swap per tile exchange dwords 2-3 of the low lanes with dwords
+// 0-1 of the high lanes, after which every lane holds two dwords of each
+// block: block-local K values 32 (p & 1) + 16 (p >> 1) + 8 j + i for MFMA j
+// of the block (i < 8). The activation fragments are read from LDS at the
+// same K values, so each block's two MFMAs form a partial that the block's
+// absmax scales before accumulation, as in mfma_kernel.
+//
+// Absmax values are read 8 blocks per column at a time: lane (p, c) holds
+// blocks 2p, 2p + 1 of the window for column c, and each block's value
+// reaches the 4 lanes of its column through ds_bpermute. Activation rows are
+// staged through LDS per block as in mfma_kernel. All global reads are
+// buffer loads: a uniform base per expert (or the activation tensor) plus a
+// fixed 32-bit lane offset and a uniform step offset; reads past a column's
+// last block fall on the next column or past the buffer (zero) and are not
+// used.
+__device__ __forceinline__ int k16_seg(int p, int j) { return 4 * (p & 1) + 2 * (p >> 1) + j; }
+
+constexpr int kBufferDword3 = 0x00020000;   // raw buffer, 32-bit data format
+
+template <int FMT>
+__global__ __launch_bounds__(kThreads, 2) void mfma16_kernel(GemmArgs a, int n_tiles_n,
+                                                             uint32_t x_bytes) {
+  static_assert(FMT == GNF4_NF4, "float32 absmax");
+  constexpr int BM = 64, BN = 256;
+  __shared__ uint32_t lut[kLutWords];
+  __shared__ uint4 As[2][BM * 8];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int N = a.w.N, K = a.w.K;
+  int e, start, tiles;
+  const int bid = xcd_remap(blockIdx.x, gridDim.x);
+  find_tile<BM>(a, bid, n_tiles_n, lane, e, start, tiles);
+  if (e < 0) return;
+  const int local = bid - start;
+  const int nt = local / tiles, mt = local - nt * tiles;
+  const int seg_start = a.offsets[e];
+  const int count = a.offsets[e + 1] - seg_start;
+  const int row0 = seg_start + mt * BM;
+  const int rows_valid = min(BM, count - mt * BM);
+  const int nb = nt * BN + wave * 64;           // this wave's first column
+  const int p = lane >> 4, c16 = lane & 15;
+  const uint32_t lane4 = (uint32_t)lane << 2;
+  const int nkb = K / 64;
+  const int nst = (nkb + 1) / 2;
+
+  const int64_t erow = (int64_t)e * N;
+  const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)(a.w.codes + erow * (K / 2)), (short)0, (int)((uint32_t)N * (uint32_t)(K / 2)),
+      kBufferDword3);
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)(reinterpret_cast<const float *>(a.w.scales) + erow * (K / 64)), (short)0,
+      (int)((uint32_t)N * (uint32_t)(K / 16)), kBufferDword3);
+  const __amdgpu_buffer_rsrc_t rx =
+      __builtin_amdgcn_make_buffer_rsrc((void *)a.X, (short)0, (int)x_bytes, kBufferDword3);
+
+  // ---- A staging (per 64-K block): byte offsets of this thread's two
+  // 16-byte segments in X, and their LDS slots
+  uint32_t xoff[2];
+  int sdst[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int idx = tid + i * kThreads;
+    const int r = idx >> 3, sg = idx & 7;
+    const int pr = row0 + min(r, rows_valid - 1);
+    const int src = a.gather ? a.perm[pr] / a.k : pr;
+    xoff[i] = (uint32_t)src * (uint32_t)(K * 2) + (uint32_t)sg * 16u;
+    sdst[i] = r * 8 + (sg ^ a_swizzle(r));
+  }
+
+  // ---- weight columns (ragged N: clamped, never stored)
+  uint32_t coff[4], soff[4];
+#pragma unroll
+  for (int ct = 0; ct < 4; ++ct) {
+    const uint32_t col = (uint32_t)min(nb + ct * 16 + c16, N - 1);
+    coff[ct] = col * (uint32_t)(K / 2) + 16u * (uint32_t)p;
+    soff[ct] = col * (uint32_t)(K / 16) + 8u * (uint32_t)p;
+  }
+
+  f32x4_t acc[4][4];
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) acc[rt][ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  uint4 qs0[4], qs1[4];               // stage slots (even / odd stages), raw codes
+  uint4 ar0_0, ar0_1, ar1_0, ar1_1;   // A staging ring (even / odd blocks)
+  uint2 sw[4], sn[4];                 // absmax window (current / next): blocks 2p, 2p+1
+
+#define GNF4_LOAD_STAGE(S, Q)                                                             \
+  {                                                                                       \
+    const int so_ = 64 * min((S), nst - 1);                                               \
+    _Pragma("unroll") for (int ct = 0; ct < 4; ++ct)                                     \
+        Q[ct] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rc, coff[ct], so_, 0)); \
+  }
+#define GNF4_LOAD_A(KB, DST)                                                              \
+  {                                                                                       \
+    const int so_ = 128 * min((KB), nkb - 1);                                             \
+    DST##_0 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, xoff[0], so_, 0)); \
+    DST##_1 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, xoff[1], so_, 0)); \
+  }
+#define GNF4_LOAD_WINDOW(W)                                                               \
+  _Pragma("unroll") for (int ct = 0; ct < 4; ++ct)                                       \
+      sn[ct] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rs, soff[ct], 32 * (W), 0));
+
+  GNF4_LOAD_WINDOW(0);
+  GNF4_LOAD_STAGE(0, qs0);
+  GNF4_LOAD_A(0, ar0);
+  GNF4_LOAD_A(1, ar1);
+  GNF4_LOAD_STAGE(1, qs1);
+  fill_nf4_lut_256(lut, tid);
+  As[0][sdst[0]] = ar0_0;
+  As[0][sdst[1]] = ar0_1;
+
+  // The two B fragments of block B of column tile CT (dwords x, y for block
+  // 0, z, w for block 1 after the swap).
+#define GNF4_DECODE(Q, B, CT, FB)                                                         \
+  {                                                                                       \
+    const uint32_t w0_ = (B) == 0 ? Q[CT].x : Q[CT].z;                                    \
+    const uint32_t w1_ = (B) == 0 ? Q[CT].y : Q[CT].w;                                    \
+    uint32_t d_[8];                                                                       \
+    _Pragma("unroll") for (int i = 0; i < 4; ++i) d_[i] = lut_read(lut, lut_addr(w0_, lane4, i)); \
+    _Pragma("unroll") for (int i = 0; i < 4; ++i) d_[4 + i] = lut_read(lut, lut_addr(w1_, lane4, i)); \
+    FB[0] = __builtin_bit_cast(bf16x8_t, make_uint4(d_[0], d_[1], d_[2], d_[3]));         \
+    FB[1] = __builtin_bit_cast(bf16x8_t, make_uint4(d_[4], d_[5], d_[6], d_[7]));         \
+  }
+
+  // One 64-K block KB = 2 S + B of stage S, codes in Q. AC: this block's A
+  // staging registers (refilled with block KB + 2); AN: block KB + 1's.
+#define GNF4_BLOCK(S, B, Q, AC, AN)                                                       \
+  {                                                                                       \
+    const int kb = 2 * (S) + (B);                                                         \
+    __builtin_amdgcn_sched_barrier(0);                                                    \
+    __syncthreads(); /* As[kb & 1] holds block kb; As[(kb & 1) ^ 1] is free */            \
+    __builtin_amdgcn_sched_barrier(0);                                                    \
+    if ((B) == 0) {                                                                       \
+      if (((S) & 3) == 0) {                                                               \
+        _Pragma("unroll") for (int ct = 0; ct < 4; ++ct) sw[ct] = sn[ct];                \
+        GNF4_LOAD_WINDOW(((S) >> 2) + 1);                                                 \
+      }                                                                                   \
+      _Pragma("unroll") for (int ct = 0; ct < 4; ++ct) {                                 \
+        auto r0 = __builtin_amdgcn_permlane32_swap(Q[ct].x, Q[ct].z, false, false);      \
+        auto r1 = __builtin_amdgcn_permlane32_swap(Q[ct].y, Q[ct].w, false, false);      \
+        Q[ct] = make_uint4(r0[0], r1[0], r0[1], r1[1]);                                   \
+      }                                                                                   \
+    }                                                                                     \
+    /* absmax of block kb for this lane's column: window slot kb & 7, held by */         \
+    /* lane group (kb & 7) >> 1 = S & 3, element kb & 1 = B */                            \
+    float scl[4];                                                                         \
+    {                                                                                     \
+      const int src = (16 * ((S) & 3) + c16) << 2;                                        \
+      _Pragma("unroll") for (int ct = 0; ct < 4; ++ct)                                   \
+        scl[ct] = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(                \
+            src, (int)((B) == 0 ? sw[ct].x : sw[ct].y)));                                 \
+    }                                                                                     \
+    GNF4_LOAD_A(kb + 2, AC);                                                              \
+    const uint4 *Ab = As[kb & 1];                                                         \
+    bf16x8_t af[4][2];                                                                    \
+    _Pragma("unroll") for (int rt = 0; rt < 4; ++rt) {                                   \
+      const int r = rt * 16 + c16;                                                        \
+      _Pragma("unroll") for (int j = 0; j < 2; ++j) af[rt][j] =                          \
+          __builtin_bit_cast(bf16x8_t, Ab[r * 8 + (k16_seg(p, j) ^ a_swizzle(r))]);       \
+    }                                                                                     \
+    /* column tiles in turn: the decode of tile ct + 1 is issued before tile */           \
+    /* ct's MFMAs; tiles t = ct * 4 + rt, the 4 scale FMAs of tile t - 1 follow */        \
+    /* tile t's MFMAs so the VALU work overlaps the MFMA pipe */                          \
+    bf16x8_t fb[2][2];                                                                    \
+    GNF4_DECODE(Q, B, 0, fb[0]);                                                          \
+    f32x4_t Pp[2];                                                                        \
+    _Pragma("unroll") for (int ct = 0; ct < 4; ++ct) {                                   \
+      __builtin_amdgcn_sched_barrier(0);                                                  \
+      if (ct < 3) GNF4_DECODE(Q, B, ct + 1, fb[(ct + 1) & 1]);                            \
+      _Pragma("unroll") for (int rt = 0; rt < 4; ++rt) {                                 \
+        const int t = ct * 4 + rt;                                                        \
+        const int pr = (t + 15) & 3, pc = ((t + 15) >> 2) & 3;                            \
+        f32x4_t P = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[rt][0], fb[ct & 1][0],      \
+                                                            f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0); \
+        P = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[rt][1], fb[ct & 1][1], P, 0, 0, 0);  \
+        if (t > 0) {                                                                      \
+          _Pragma("unroll") for (int r2 = 0; r2 < 4; ++r2) acc[pr][pc][r2] =             \
+              __builtin_fmaf(scl[pc], Pp[(t - 1) & 1][r2], acc[pr][pc][r2]);              \
+        }                                                                                 \
+        Pp[t & 1] = P;                                                                    \
+      }                                                                                   \
+    }                                                                                     \
+    __builtin_amdgcn_sched_barrier(0);                                                    \
+    /* stage S + 2 reuses this stage's slot once block 1 is decoded */                   \
+    if ((B) == 1) GNF4_LOAD_STAGE((S) + 2, Q);                                            \
+    _Pragma("unroll") for (int r2 = 0; r2 < 4; ++r2) acc[3][3][r2] =                     \
+        __builtin_fmaf(scl[3], Pp[1][r2], acc[3][3][r2]);                                 \
+    __builtin_amdgcn_sched_barrier(0);                                                    \
+    As[(kb & 1) ^ 1][sdst[0]] = AN##_0;                                                   \
+    As[(kb & 1) ^ 1][sdst[1]] = AN##_1;                                                   \
+  }
+
+  // stages in pairs (slot qs0 even, qs1 odd); a trailing odd block ends early
+  int S = 0;
+  for (; S + 1 < nst; S += 2) {
+    GNF4_BLOCK(S, 0, qs0, ar0, ar1);
+    GNF4_BLOCK(S, 1, qs0, ar1, ar0);
+    GNF4_BLOCK(S + 1, 0, qs1, ar0, ar1);
+    if (2 * (S + 1) + 1 < nkb) GNF4_BLOCK(S + 1, 1, qs1, ar1, ar0);
+  }
+  if (S < nst) {
+    GNF4_BLOCK(S, 0, qs0, ar0, ar1);
+    if (2 * S + 1 < nkb) GNF4_BLOCK(S, 1, qs0, ar1, ar0);
+  }
+#undef GNF4_BLOCK
+#undef GNF4_DECODE
+#undef GNF4_LOAD_WINDOW
+#undef GNF4_LOAD_A
+#undef GNF4_LOAD_STAGE
+
+  // ---- store: register r of a 16x16 tile holds row 4 p + r, column c16
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) {
+      const int col = nb + ct * 16 + c16;
+      if (col >= N) continue;
+#pragma unroll
+      for (int r2 = 0; r2 < 4; ++r2) {
+        const int r = rt * 16 + 4 * p + r2;
+        if (r < rows_valid) a.Y[(int64_t)(row0 + r) * N + col] = acc[rt][ct][r2];
+      }
     }
 }
 
@@ -764,8 +1023,29 @@ static hipError_t mfma_go(const GemmArgs &a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Bytes of the activation tensor the GEMM reads (gathered: T rows, else T*k).
+static int64_t x_bytes(const GemmArgs &a) {
+  return (a.gather ? (int64_t)a.T : (int64_t)a.T * a.k) * a.w.K * 2;
+}
+
+static hipError_t mfma16_go(const GemmArgs &a, hipStream_t s) {
+  constexpr int BM = 64, BN = 256;
+  const int rows = a.T * a.k;
+  const int n_tiles_n = (a.w.N + BN - 1) / BN;
+  const int64_t m_tiles = (rows + BM - 1) / BM + std::min<int>(a.w.E, rows);
+  int64_t grid = m_tiles * n_tiles_n;
+  grid = (grid + 7) / 8 * 8;
+  if (grid <= 0) return hipSuccess;
+  hipLaunchKernelGGL((mfma16_kernel<GNF4_NF4>), dim3((unsigned)grid), dim3(kThreads), 0, s, a,
+                     n_tiles_n, (uint32_t)x_bytes(a));
+  return hipGetLastError();
+}
+
 template <int FMT>
 static hipError_t mfma_pick(const GemmArgs &a, hipStream_t s) {
+  // the 16x16x32 kernel addresses activations with 32-bit buffer offsets
+  if constexpr (FMT == GNF4_NF4)
+    if (x_bytes(a) < ((int64_t)1 << 32)) return mfma16_go(a, s);
   return mfma_go<FMT, 2, 2>(a, s);
 }
 
