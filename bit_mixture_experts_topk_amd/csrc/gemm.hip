@@ -671,13 +671,17 @@ __device__ __forceinline__ int k16_seg(int p, int j) { return 4 * (p & 1) + 2 * 
 
 constexpr int kBufferDword3 = 0x00020000;   // raw buffer, 32-bit data format
 
-template <int FMT>
+template <int FMT, int RT>
 __global__ __launch_bounds__(kThreads, 2) void mfma16_kernel(GemmArgs a, int n_tiles_n,
                                                              uint32_t x_bytes) {
-  static_assert(FMT == GNF4_NF4, "float32 absmax");
-  constexpr int BM = 64, BN = 256;
-  __shared__ uint32_t lut[kLutWords];
-  __shared__ uint4 As[2][BM * 8];
+  static_assert(FMT == GNF4_NF4 || FMT == GNF4_MXFP4, "float32 absmax or e8m0 scales");
+  constexpr bool kNF4 = FMT == GNF4_NF4;
+  constexpr int BM = 16 * RT, BN = 256;
+  static_assert(RT >= 1 && RT <= 5, "16 to 80 rows");
+  constexpr int kSegs = BM * 8;                 // 16-byte A segments per block
+  constexpr int kALoads = (kSegs + kThreads - 1) / kThreads;
+  __shared__ uint32_t lut[kNF4 ? kLutWords : 1];
+  __shared__ uint4 As[2][kSegs];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int N = a.w.N, K = a.w.K;
@@ -701,19 +705,21 @@ __global__ __launch_bounds__(kThreads, 2) void mfma16_kernel(GemmArgs a, int n_t
   const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
       (void *)(a.w.codes + erow * (K / 2)), (short)0, (int)((uint32_t)N * (uint32_t)(K / 2)),
       kBufferDword3);
+  // NF4: float32 absmax [N][K/64]; MXFP4: e8m0 bytes [N][K/32]
+  const uint32_t scale_row = kNF4 ? (uint32_t)(K / 16) : (uint32_t)(K / 32);
   const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-      (void *)(reinterpret_cast<const float *>(a.w.scales) + erow * (K / 64)), (short)0,
-      (int)((uint32_t)N * (uint32_t)(K / 16)), kBufferDword3);
+      (void *)(reinterpret_cast<const uint8_t *>(a.w.scales) + erow * scale_row), (short)0,
+      (int)((uint32_t)N * scale_row), kBufferDword3);
   const __amdgpu_buffer_rsrc_t rx =
       __builtin_amdgcn_make_buffer_rsrc((void *)a.X, (short)0, (int)x_bytes, kBufferDword3);
 
   // ---- A staging (per 64-K block): byte offsets of this thread's two
   // 16-byte segments in X, and their LDS slots
-  uint32_t xoff[2];
-  int sdst[2];
+  uint32_t xoff[kALoads];
+  int sdst[kALoads];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int idx = tid + i * kThreads;
+  for (int i = 0; i < kALoads; ++i) {
+    const int idx = min(tid + i * kThreads, kSegs - 1);   // a surplus thread repeats the last slot
     const int r = idx >> 3, sg = idx & 7;
     const int pr = row0 + min(r, rows_valid - 1);
     const int src = a.gather ? a.perm[pr] / a.k : pr;
@@ -721,24 +727,27 @@ __global__ __launch_bounds__(kThreads, 2) void mfma16_kernel(GemmArgs a, int n_t
     sdst[i] = r * 8 + (sg ^ a_swizzle(r));
   }
 
-  // ---- weight columns (ragged N: clamped, never stored)
+  // ---- weight columns (ragged N: clamped, never stored). NF4 scale offset:
+  // blocks 2p, 2p + 1 of an 8-block window; MXFP4: the 32-K group (p & 1) of
+  // a block, the block index coming from the step offset.
   uint32_t coff[4], soff[4];
 #pragma unroll
   for (int ct = 0; ct < 4; ++ct) {
     const uint32_t col = (uint32_t)min(nb + ct * 16 + c16, N - 1);
     coff[ct] = col * (uint32_t)(K / 2) + 16u * (uint32_t)p;
-    soff[ct] = col * (uint32_t)(K / 16) + 8u * (uint32_t)p;
+    soff[ct] = kNF4 ? col * scale_row + 8u * (uint32_t)p : col * scale_row + (uint32_t)(p & 1);
   }
 
-  f32x4_t acc[4][4];
+  f32x4_t acc[RT][4];
 #pragma unroll
-  for (int rt = 0; rt < 4; ++rt)
+  for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) acc[rt][ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   uint4 qs0[4], qs1[4];               // stage slots (even / odd stages), raw codes
-  uint4 ar0_0, ar0_1, ar1_0, ar1_1;   // A staging ring (even / odd blocks)
-  uint2 sw[4], sn[4];                 // absmax window (current / next): blocks 2p, 2p+1
+  uint4 ar0[kALoads], ar1[kALoads];   // A staging ring (even / odd blocks)
+  uint2 sw[4], sn[4];                 // NF4 absmax window (current / next): blocks 2p, 2p+1
+  uint32_t sb0[4], sb1[4];            // MXFP4 scale bytes ring (even / odd blocks)
 
 #define GNF4_LOAD_STAGE(S, Q)                                                             \
   {                                                                                       \
@@ -749,47 +758,67 @@ __global__ __launch_bounds__(kThreads, 2) void mfma16_kernel(GemmArgs a, int n_t
 #define GNF4_LOAD_A(KB, DST)                                                              \
   {                                                                                       \
     const int so_ = 128 * min((KB), nkb - 1);                                             \
-    DST##_0 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, xoff[0], so_, 0)); \
-    DST##_1 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, xoff[1], so_, 0)); \
+    _Pragma("unroll") for (int i = 0; i < kALoads; ++i)                                  \
+        DST[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, xoff[i], so_, 0)); \
   }
+#define GNF4_STORE_A(SLOT, SRC)                                                           \
+  _Pragma("unroll") for (int i = 0; i < kALoads; ++i) As[SLOT][sdst[i]] = SRC[i];
 #define GNF4_LOAD_WINDOW(W)                                                               \
   _Pragma("unroll") for (int ct = 0; ct < 4; ++ct)                                       \
       sn[ct] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rs, soff[ct], 32 * (W), 0));
+#define GNF4_LOAD_SBYTES(KB, SB)                                                          \
+  _Pragma("unroll") for (int ct = 0; ct < 4; ++ct)                                       \
+      SB[ct] = __builtin_amdgcn_raw_buffer_load_b8(rs, soff[ct], 2 * min((KB), nkb - 1), 0);
 
-  GNF4_LOAD_WINDOW(0);
+  if constexpr (kNF4) {
+    GNF4_LOAD_WINDOW(0);
+  } else {
+    GNF4_LOAD_SBYTES(0, sb0);
+    GNF4_LOAD_SBYTES(1, sb1);
+  }
   GNF4_LOAD_STAGE(0, qs0);
   GNF4_LOAD_A(0, ar0);
   GNF4_LOAD_A(1, ar1);
   GNF4_LOAD_STAGE(1, qs1);
-  fill_nf4_lut_256(lut, tid);
-  As[0][sdst[0]] = ar0_0;
-  As[0][sdst[1]] = ar0_1;
+  if constexpr (kNF4) fill_nf4_lut_256(lut, tid);
+  GNF4_STORE_A(0, ar0);
 
   // The two B fragments of block B of column tile CT (dwords x, y for block
-  // 0, z, w for block 1 after the swap).
-#define GNF4_DECODE(Q, B, CT, FB)                                                         \
+  // 0, z, w for block 1 after the swap). MXFP4: the scale SC of the lane's
+  // 32-K group is applied by the conversion (exact).
+#define GNF4_DECODE(Q, B, CT, FB, SC)                                                     \
   {                                                                                       \
     const uint32_t w0_ = (B) == 0 ? Q[CT].x : Q[CT].z;                                    \
     const uint32_t w1_ = (B) == 0 ? Q[CT].y : Q[CT].w;                                    \
     uint32_t d_[8];                                                                       \
-    _Pragma("unroll") for (int i = 0; i < 4; ++i) d_[i] = lut_read(lut, lut_addr(w0_, lane4, i)); \
-    _Pragma("unroll") for (int i = 0; i < 4; ++i) d_[4 + i] = lut_read(lut, lut_addr(w1_, lane4, i)); \
+    if constexpr (kNF4) {                                                                 \
+      _Pragma("unroll") for (int i = 0; i < 4; ++i) d_[i] = lut_read(lut, lut_addr(w0_, lane4, i)); \
+      _Pragma("unroll") for (int i = 0; i < 4; ++i) d_[4 + i] = lut_read(lut, lut_addr(w1_, lane4, i)); \
+    } else {                                                                              \
+      d_[0] = fp4_pair<0>(w0_, SC); d_[1] = fp4_pair<1>(w0_, SC);                         \
+      d_[2] = fp4_pair<2>(w0_, SC); d_[3] = fp4_pair<3>(w0_, SC);                         \
+      d_[4] = fp4_pair<0>(w1_, SC); d_[5] = fp4_pair<1>(w1_, SC);                         \
+      d_[6] = fp4_pair<2>(w1_, SC); d_[7] = fp4_pair<3>(w1_, SC);                         \
+    }                                                                                     \
     FB[0] = __builtin_bit_cast(bf16x8_t, make_uint4(d_[0], d_[1], d_[2], d_[3]));         \
     FB[1] = __builtin_bit_cast(bf16x8_t, make_uint4(d_[4], d_[5], d_[6], d_[7]));         \
   }
 
   // One 64-K block KB = 2 S + B of stage S, codes in Q. AC: this block's A
-  // staging registers (refilled with block KB + 2); AN: block KB + 1's.
-#define GNF4_BLOCK(S, B, Q, AC, AN)                                                       \
+  // staging registers (refilled with block KB + 2); AN: block KB + 1's. SB:
+  // this block's MXFP4 scale bytes (refilled with block KB + 2).
+#define GNF4_BLOCK(S, B, Q, AC, AN, SB)                                                   \
   {                                                                                       \
     const int kb = 2 * (S) + (B);                                                         \
     __builtin_amdgcn_sched_barrier(0);                                                    \
     __syncthreads(); /* As[kb & 1] holds block kb; As[(kb & 1) ^ 1] is free */            \
     __builtin_amdgcn_sched_barrier(0);                                                    \
     if ((B) == 0) {                                                                       \
-      if (((S) & 3) == 0) {                                                               \
-        _Pragma("unroll") for (int ct = 0; ct < 4; ++ct) sw[ct] = sn[ct];                \
-        GNF4_LOAD_WINDOW(((S) >> 2) + 1);                                                 \
+      if constexpr (kNF4) {                                                               \
+        if (((S) & 3) == 0) {                                                             \
+          _Pragma("unroll") for (int ct = 0; ct < 4; ++ct) sw[ct] = sn[ct];              \
+          GNF4_LOAD_WINDOW(((S) >> 2) + 1);                                               \
+        }                                                                                 \
       }                                                                                   \
       _Pragma("unroll") for (int ct = 0; ct < 4; ++ct) {                                 \
         auto r0 = __builtin_amdgcn_permlane32_swap(Q[ct].x, Q[ct].z, false, false);      \
@@ -797,76 +826,92 @@ __global__ __launch_bounds__(kThreads, 2) void mfma16_kernel(GemmArgs a, int n_t
         Q[ct] = make_uint4(r0[0], r1[0], r0[1], r1[1]);                                   \
       }                                                                                   \
     }                                                                                     \
-    /* absmax of block kb for this lane's column: window slot kb & 7, held by */         \
-    /* lane group (kb & 7) >> 1 = S & 3, element kb & 1 = B */                            \
+    /* NF4: absmax of block kb for this lane's column: window slot kb & 7, held */       \
+    /* by lane group (kb & 7) >> 1 = S & 3, element kb & 1 = B. MXFP4: the scale */       \
+    /* of the lane's own 32-K group, loaded two blocks ahead */                           \
     float scl[4];                                                                         \
-    {                                                                                     \
+    if constexpr (kNF4) {                                                                 \
       const int src = (16 * ((S) & 3) + c16) << 2;                                        \
       _Pragma("unroll") for (int ct = 0; ct < 4; ++ct)                                   \
         scl[ct] = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(                \
             src, (int)((B) == 0 ? sw[ct].x : sw[ct].y)));                                 \
+    } else {                                                                              \
+      _Pragma("unroll") for (int ct = 0; ct < 4; ++ct) scl[ct] = e8m0_to_f32(SB[ct] & 0xffu); \
+      GNF4_LOAD_SBYTES(kb + 2, SB);                                                       \
     }                                                                                     \
     GNF4_LOAD_A(kb + 2, AC);                                                              \
     const uint4 *Ab = As[kb & 1];                                                         \
-    bf16x8_t af[4][2];                                                                    \
-    _Pragma("unroll") for (int rt = 0; rt < 4; ++rt) {                                   \
+    bf16x8_t af[RT][2];                                                                   \
+    _Pragma("unroll") for (int rt = 0; rt < RT; ++rt) {                                  \
       const int r = rt * 16 + c16;                                                        \
       _Pragma("unroll") for (int j = 0; j < 2; ++j) af[rt][j] =                          \
           __builtin_bit_cast(bf16x8_t, Ab[r * 8 + (k16_seg(p, j) ^ a_swizzle(r))]);       \
     }                                                                                     \
     /* column tiles in turn: the decode of tile ct + 1 is issued before tile */           \
-    /* ct's MFMAs; tiles t = ct * 4 + rt, the 4 scale FMAs of tile t - 1 follow */        \
-    /* tile t's MFMAs so the VALU work overlaps the MFMA pipe */                          \
+    /* ct's MFMAs. NF4: tiles t = ct * 4 + rt, the 4 scale FMAs of tile t - 1 */          \
+    /* follow tile t's MFMAs so the VALU work overlaps the MFMA pipe; MXFP4 */            \
+    /* accumulates in the MFMAs */                                                        \
     bf16x8_t fb[2][2];                                                                    \
-    GNF4_DECODE(Q, B, 0, fb[0]);                                                          \
+    GNF4_DECODE(Q, B, 0, fb[0], scl[0]);                                                  \
     f32x4_t Pp[2];                                                                        \
     _Pragma("unroll") for (int ct = 0; ct < 4; ++ct) {                                   \
       __builtin_amdgcn_sched_barrier(0);                                                  \
-      if (ct < 3) GNF4_DECODE(Q, B, ct + 1, fb[(ct + 1) & 1]);                            \
-      _Pragma("unroll") for (int rt = 0; rt < 4; ++rt) {                                 \
-        const int t = ct * 4 + rt;                                                        \
-        const int pr = (t + 15) & 3, pc = ((t + 15) >> 2) & 3;                            \
-        f32x4_t P = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[rt][0], fb[ct & 1][0],      \
-                                                            f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0); \
-        P = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[rt][1], fb[ct & 1][1], P, 0, 0, 0);  \
-        if (t > 0) {                                                                      \
-          _Pragma("unroll") for (int r2 = 0; r2 < 4; ++r2) acc[pr][pc][r2] =             \
-              __builtin_fmaf(scl[pc], Pp[(t - 1) & 1][r2], acc[pr][pc][r2]);              \
+      if (ct < 3) GNF4_DECODE(Q, B, ct + 1, fb[(ct + 1) & 1], scl[ct + 1]);              \
+      _Pragma("unroll") for (int rt = 0; rt < RT; ++rt) {                                \
+        if constexpr (kNF4) {                                                             \
+          constexpr int kT = RT * 4;                                                      \
+          const int t = ct * RT + rt;                                                     \
+          const int pr = (t + kT - 1) % RT, pc = ((t + kT - 1) / RT) % 4;                 \
+          f32x4_t P = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[rt][0], fb[ct & 1][0],    \
+                                                              f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0); \
+          P = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[rt][1], fb[ct & 1][1], P, 0, 0, 0); \
+          if (t > 0) {                                                                    \
+            _Pragma("unroll") for (int r2 = 0; r2 < 4; ++r2) acc[pr][pc][r2] =           \
+                __builtin_fmaf(scl[pc], Pp[(t - 1) & 1][r2], acc[pr][pc][r2]);            \
+          }                                                                               \
+          Pp[t & 1] = P;                                                                  \
+        } else {                                                                          \
+          acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[rt][0], fb[ct & 1][0],  \
+                                                                acc[rt][ct], 0, 0, 0);    \
+          acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[rt][1], fb[ct & 1][1],  \
+                                                                acc[rt][ct], 0, 0, 0);    \
         }                                                                                 \
-        Pp[t & 1] = P;                                                                    \
       }                                                                                   \
     }                                                                                     \
     __builtin_amdgcn_sched_barrier(0);                                                    \
     /* stage S + 2 reuses this stage's slot once block 1 is decoded */                   \
     if ((B) == 1) GNF4_LOAD_STAGE((S) + 2, Q);                                            \
-    _Pragma("unroll") for (int r2 = 0; r2 < 4; ++r2) acc[3][3][r2] =                     \
-        __builtin_fmaf(scl[3], Pp[1][r2], acc[3][3][r2]);                                 \
+    if constexpr (kNF4) {                                                                 \
+      _Pragma("unroll") for (int r2 = 0; r2 < 4; ++r2) acc[RT - 1][3][r2] =              \
+          __builtin_fmaf(scl[3], Pp[(RT * 4 - 1) & 1][r2], acc[RT - 1][3][r2]);           \
+    }                                                                                     \
     __builtin_amdgcn_sched_barrier(0);                                                    \
-    As[(kb & 1) ^ 1][sdst[0]] = AN##_0;                                                   \
-    As[(kb & 1) ^ 1][sdst[1]] = AN##_1;                                                   \
+    GNF4_STORE_A((kb & 1) ^ 1, AN);                                                       \
   }
 
   // stages in pairs (slot qs0 even, qs1 odd); a trailing odd block ends early
   int S = 0;
   for (; S + 1 < nst; S += 2) {
-    GNF4_BLOCK(S, 0, qs0, ar0, ar1);
-    GNF4_BLOCK(S, 1, qs0, ar1, ar0);
-    GNF4_BLOCK(S + 1, 0, qs1, ar0, ar1);
-    if (2 * (S + 1) + 1 < nkb) GNF4_BLOCK(S + 1, 1, qs1, ar1, ar0);
+    GNF4_BLOCK(S, 0, qs0, ar0, ar1, sb0);
+    GNF4_BLOCK(S, 1, qs0, ar1, ar0, sb1);
+    GNF4_BLOCK(S + 1, 0, qs1, ar0, ar1, sb0);
+    if (2 * (S + 1) + 1 < nkb) GNF4_BLOCK(S + 1, 1, qs1, ar1, ar0, sb1);
   }
   if (S < nst) {
-    GNF4_BLOCK(S, 0, qs0, ar0, ar1);
-    if (2 * S + 1 < nkb) GNF4_BLOCK(S, 1, qs0, ar1, ar0);
+    GNF4_BLOCK(S, 0, qs0, ar0, ar1, sb0);
+    if (2 * S + 1 < nkb) GNF4_BLOCK(S, 1, qs0, ar1, ar0, sb1);
   }
 #undef GNF4_BLOCK
 #undef GNF4_DECODE
+#undef GNF4_LOAD_SBYTES
 #undef GNF4_LOAD_WINDOW
+#undef GNF4_STORE_A
 #undef GNF4_LOAD_A
 #undef GNF4_LOAD_STAGE
 
   // ---- store: register r of a 16x16 tile holds row 4 p + r, column c16
 #pragma unroll
-  for (int rt = 0; rt < 4; ++rt)
+  for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) {
       const int col = nb + ct * 16 + c16;
@@ -1028,15 +1073,16 @@ static int64_t x_bytes(const GemmArgs &a) {
   return (a.gather ? (int64_t)a.T : (int64_t)a.T * a.k) * a.w.K * 2;
 }
 
+template <int FMT, int RT>
 static hipError_t mfma16_go(const GemmArgs &a, hipStream_t s) {
-  constexpr int BM = 64, BN = 256;
+  constexpr int BM = 16 * RT, BN = 256;
   const int rows = a.T * a.k;
   const int n_tiles_n = (a.w.N + BN - 1) / BN;
   const int64_t m_tiles = (rows + BM - 1) / BM + std::min<int>(a.w.E, rows);
   int64_t grid = m_tiles * n_tiles_n;
   grid = (grid + 7) / 8 * 8;
   if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL((mfma16_kernel<GNF4_NF4>), dim3((unsigned)grid), dim3(kThreads), 0, s, a,
+  hipLaunchKernelGGL((mfma16_kernel<FMT, RT>), dim3((unsigned)grid), dim3(kThreads), 0, s, a,
                      n_tiles_n, (uint32_t)x_bytes(a));
   return hipGetLastError();
 }
@@ -1044,8 +1090,9 @@ static hipError_t mfma16_go(const GemmArgs &a, hipStream_t s) {
 template <int FMT>
 static hipError_t mfma_pick(const GemmArgs &a, hipStream_t s) {
   // the 16x16x32 kernel addresses activations with 32-bit buffer offsets
-  if constexpr (FMT == GNF4_NF4)
-    if (x_bytes(a) < ((int64_t)1 << 32)) return mfma16_go(a, s);
+  if constexpr (FMT == GNF4_NF4 || FMT == GNF4_MXFP4) {
+    if (x_bytes(a) < ((int64_t)1 << 32)) return mfma16_go<FMT, 4>(a, s);
+  }
   return mfma_go<FMT, 2, 2>(a, s);
 }
 
