@@ -56,6 +56,25 @@ def dequant_expert(fmt, codes, scales, scales2, e, N, K):
     raise ValueError("unknown format %r" % (fmt,))
 
 
+def dequant_rows(fmt, codes, scales, scales2, e, rows, N, K):
+    """float32 [len(rows), K]: rows `rows` of expert e, dequantized exactly as
+    dequant_expert does for the whole expert (same block scales, same flat
+    block index for NF4_DQ), without decoding the other rows."""
+    rows = np.asarray(rows, dtype=np.int64)
+    if fmt == "nf4":
+        return nf4.dequantize(codes[e][rows], scales[e][rows], K)
+    if fmt == "nf4_dq":
+        nb = K // nf4.BLOCK
+        q8 = np.asarray(scales).reshape(-1)
+        s2 = np.asarray(scales2, dtype=np.float32)
+        blk = ((e * N + rows)[:, None] * nb + np.arange(nb)[None, :]).reshape(-1)
+        a = (q8[blk].astype(np.float64) * s2[blk // nf4.DQ_GROUP].astype(np.float64)).astype(np.float32)
+        return nf4.dequantize(codes[e][rows], a.reshape(len(rows), nb), K)
+    if fmt == "mxfp4":
+        return mxfp4.dequantize(codes[e][rows], scales[e][rows], K)
+    raise ValueError("unknown format %r" % (fmt,))
+
+
 def grouped_gemm(fmt, codes, scales, scales2, X_bits, gather, offsets, perm, k, N, K):
     """Y float64 [rows, N] of the grouped GEMM (rows = T*k).
 

@@ -51,6 +51,7 @@ T_LOGITS = 4
 T_X_DOWN = 5
 T_W_SINGLE = 6
 T_Y = 7
+T_PACKED = 8
 
 
 @dataclass(frozen=True)
@@ -196,3 +197,34 @@ def small_layer(E, N, K, T, k, seed=0, distinct=True, gather=1):
         ids = g.integers(0, E, size=(T, k))
     tw = g.random((T, k)).astype(np.float32)
     return {"W": W, "X": X, "ids": np.asarray(ids, dtype=np.int32).reshape(T, k), "tw": tw}
+
+
+def packed_weights(cfg, proj, seed=0):
+    """Packed weights of one projection drawn directly as stored bytes, for
+    full-size parity checks where quantizing a whole layer on the CPU would
+    take minutes. No quantizer is involved: every code byte is uniform over
+    0..255 (all 16 codes equally likely in both nibbles), and the scales are
+    drawn in the range a quantized N(0, 0.02) layer produces.
+
+    Returns (codes uint8 [E, N, K/2], scales, scales2):
+      nf4:    scales float32 [E, N, K/64] ~ U(0.02, 0.08), scales2 None
+      nf4_dq: scales int8 [E, N, K/64] ~ U{1..127}, scales2 float32
+              [ceil(E*N*K/64 / 256)] ~ U(2e-4, 6e-4)
+      mxfp4:  scales uint8 e8m0 [E, N, K/32] ~ U{118..124} (2^-9 .. 2^-3),
+              scales2 None
+    """
+    E, N, K = cfg.E, proj.N, proj.K
+    g = rng(seed, cfg.config_id, T_PACKED, 0, proj.tensor_id)
+    codes = g.integers(0, 256, size=(E, N, K // 2), dtype=np.uint8)
+    if cfg.fmt == "nf4":
+        scales = g.uniform(0.02, 0.08, size=(E, N, K // 64)).astype(np.float32)
+        return codes, scales, None
+    if cfg.fmt == "nf4_dq":
+        scales = g.integers(1, 128, size=(E, N, K // 64), dtype=np.int8)
+        groups = -(-(E * N * (K // 64)) // 256)
+        scales2 = g.uniform(2e-4, 6e-4, size=groups).astype(np.float32)
+        return codes, scales, scales2
+    if cfg.fmt == "mxfp4":
+        scales = g.integers(118, 125, size=(E, N, K // 32), dtype=np.uint8)
+        return codes, scales, None
+    raise ValueError("unknown format %r" % (cfg.fmt,))

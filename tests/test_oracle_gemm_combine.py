@@ -11,6 +11,7 @@
 """
 
 import numpy as np
+import pytest
 
 import synth
 from oracle import combine, grouped_gemm, mxfp4, nf4, routing
@@ -155,3 +156,33 @@ def test_byte_flip_negative_control():
     assert not within(bad, ref)
     max_rel, _ = errors(bad, ref)
     assert max_rel > 2e-2
+
+
+@pytest.mark.parametrize("name,projname", [("olmoe", "down"), ("qwen30", "down"), ("gptoss", "down")])
+def test_dequant_rows_matches_expert_rows(name, projname):
+    """The row-subset dequant used by the full-size parity tests decodes
+    exactly the rows the whole-expert dequant decodes (including the flat
+    block index of the double-quantized absmax)."""
+    cfg = synth.CONFIGS[name]
+    proj = cfg.proj(projname)
+    codes, scales, scales2 = synth.packed_weights(cfg, proj)
+    E, N, K = cfg.E, proj.N, proj.K
+    for e in (0, E - 1):
+        rows = np.array([0, 1, N // 2, N - 1])
+        full = grouped_gemm.dequant_expert(cfg.fmt, codes, scales, scales2, e, N, K)
+        part = grouped_gemm.dequant_rows(cfg.fmt, codes, scales, scales2, e, rows, N, K)
+        assert np.array_equal(full[rows], part)
+
+
+def test_packed_weights_are_seeded_and_in_range():
+    cfg = synth.CONFIGS["qwen30"]
+    proj = cfg.proj("down")
+    a = synth.packed_weights(cfg, proj)
+    b = synth.packed_weights(cfg, proj)
+    assert all(np.array_equal(x, y) for x, y in zip(a, b))
+    codes, q8, s2 = a
+    assert codes.shape == (cfg.E, proj.N, proj.K // 2) and codes.dtype == np.uint8
+    assert q8.dtype == np.int8 and q8.min() >= 1
+    assert s2.shape == (-(-(cfg.E * proj.N * (proj.K // 64)) // 256),)
+    codes, e8, _ = synth.packed_weights(synth.CONFIGS["gptoss"], synth.CONFIGS["gptoss"].proj("down"))
+    assert e8.min() >= 118 and e8.max() <= 124
