@@ -257,6 +257,14 @@ def time_kernel(torch, gnf4, slots, steps, warmup):
     return float(np.median(ms)), float(byts), float(fl), G
 
 
+def gemm_kernel_name(cfg, T):
+    """The HIP kernel gnf4_grouped_gemm runs for this workload's gate_up call
+    (the library picks it from T*k and the format)."""
+    if T * cfg.k <= 64:
+        return "gemv1_kernel" if T == 1 else "gemv_kernel"
+    return "mfma16_kernel" if cfg.fmt in ("nf4", "mxfp4") else "mfma_kernel"
+
+
 def profile_traffic(cfg_name, mode):
     """HBM bytes per launch of the gate_up kernel from the committed rocprofv3
     counter summary for this workload, if the GEMM source is unchanged since
@@ -424,7 +432,7 @@ def main():
         result["roofline"] = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
                               "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic,
                               "traffic_unit": "HBM bytes/launch", "traffic_source": tsrc,
-                              "kernel": "gemv_kernel (gate_up, T=%d)" % d["T"],
+                              "kernel": "%s (gate_up, T=%d)" % (gemm_kernel_name(cfg, d["T"]), d["T"]),
                               "kernel_us": round(d["kernel_us"], 3),
                               "launches_per_graph": d["graph_launches"],
                               "bytes_per_launch": int(d["kernel_bytes"])}
@@ -442,7 +450,7 @@ def main():
                                           "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                                           "frac": round(kt / BF16_PEAK_TFLOPS, 4), "traffic": ptraffic,
                                           "traffic_unit": "HBM bytes/launch", "traffic_source": ptsrc,
-                                          "kernel": "mfma_kernel (gate_up, T=%d)" % p["T"],
+                                          "kernel": "%s (gate_up, T=%d)" % (gemm_kernel_name(cfg, p["T"]), p["T"]),
                                           "kernel_us": round(p["kernel_us"], 2)}}
         if "decode" not in out:
             result["value"] = round(p["tflops"], 3)
