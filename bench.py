@@ -262,7 +262,7 @@ def gemm_kernel_name(cfg, T):
     (the library picks it from T*k and the format)."""
     if T * cfg.k <= 64:
         return "gemv1_kernel" if T == 1 else "gemv_kernel"
-    return "mfma16_kernel" if cfg.fmt in ("nf4", "mxfp4") else "mfma_kernel"
+    return "mfma16_kernel"
 
 
 def profile_traffic(cfg_name, mode):

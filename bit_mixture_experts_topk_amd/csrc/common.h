@@ -11,7 +11,6 @@ namespace gnf4 {
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
-typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 // NF4 codebook, float32 bit patterns, index = 4-bit code. These are the 16
 // NormalFloat-4 values of the QLoRA construction (8 positive and 7 negative

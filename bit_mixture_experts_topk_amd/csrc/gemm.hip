@@ -17,15 +17,16 @@
 //    the block scale is applied once per 32-value chunk. Rows are reduced
 //    across their lanes with DPP and permlane swaps.
 //
-//  * mfma_kernel (prefill; a dense contraction per expert). Each workgroup
-//    owns a BM x BN tile of one expert (tiles enumerated expert by expert,
+//  * mfma16_kernel (prefill; a dense contraction per expert). Each workgroup
+//    owns a 64 x 256 tile of one expert (tiles enumerated expert by expert,
 //    N-tile major, then M-tile; the enumeration is XCD-aware so tiles that
 //    share weight columns run on one XCD's L2). Gathered activation rows are
 //    staged in LDS (double buffered, XOR-swizzled 16-byte segments); each
-//    wave decodes its weight columns straight into MFMA B fragments and runs
-//    v_mfma_f32_32x32x16_bf16. NF4: the bf16 codebook enters the MFMA and
-//    the float32 absmax scales each 64-value partial before accumulation.
-//    MXFP4: the e8m0 scale is folded into the (exact) bf16 decode.
+//    wave loads whole 64-byte lines of its weight columns, decodes them
+//    straight into MFMA B fragments and runs v_mfma_f32_16x16x32_bf16.
+//    NF4 / NF4_DQ: the bf16 codebook enters the MFMA and the float32 absmax
+//    scales each 64-value partial before accumulation. MXFP4: the e8m0 scale
+//    is folded into the (exact) bf16 decode.
 #include <algorithm>
 #include <type_traits>
 
@@ -395,7 +396,7 @@ __device__ __forceinline__ int xcd_remap(int bid, int grid) {
 // within the lanes the LDS serves together. Folding r >> 3 in separates them.
 __device__ __forceinline__ int a_swizzle(int r) { return (r ^ (r >> 3)) & 7; }
 
-// Tile enumeration shared by the MFMA kernels: expert by expert (ascending),
+// Tile enumeration of the MFMA kernel: expert by expert (ascending),
 // ceil(count / BM) M tiles each, N-tile major within the expert. Returns the
 // expert of logical tile `bid` (-1 past the last tile), the first logical
 // tile of that expert and its M-tile count. Uniform per wave.
@@ -428,222 +429,9 @@ __device__ __forceinline__ void find_tile(const GemmArgs &a, int bid, int n_tile
   }
 }
 
-// Tile: BM = 32*TM activation rows x BN = 4*32*TN weight rows (output
-// columns). The 4 waves split N: wave w owns columns [w*32*TN, (w+1)*32*TN)
-// and all BM rows, so every weight column is decoded by exactly one wave.
-// K advances 64 values (one NF4 block, two MXFP4 blocks) per step; A and B
-// are prefetched two steps ahead (register staging, A double-buffered in LDS).
-template <int FMT, int TM, int TN>
-__global__ __launch_bounds__(kThreads, 2) void mfma_kernel(GemmArgs a, int n_tiles_n) {
-  constexpr int BM = 32 * TM;
-  constexpr int BN = 4 * 32 * TN;
-  constexpr bool kLut = FMT != GNF4_MXFP4;
-  constexpr int kSegs = BM * 8;              // 16-byte A segments per K step
-  constexpr int kALoads = kSegs / kThreads;  // per thread
-  static_assert(kSegs % kThreads == 0, "BM must be a multiple of 32");
-  __shared__ uint32_t lut[kLut ? kLutWords : 1];
-  __shared__ uint4 As[2][kSegs];
+// ======================================== MFMA 16x16x32, full-line weight loads
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int N = a.w.N, K = a.w.K;
-
-  // ---- which tile
-  int e, start, tiles;
-  find_tile<BM>(a, xcd_remap(blockIdx.x, gridDim.x), n_tiles_n, lane, e, start, tiles);
-  if (e < 0) return;                        // past the last tile (uniform per workgroup)
-  const int local = xcd_remap(blockIdx.x, gridDim.x) - start;
-  const int nt = local / tiles, mt = local - nt * tiles;
-  const int seg_start = a.offsets[e];
-  const int count = a.offsets[e + 1] - seg_start;
-  const int row0 = seg_start + mt * BM;
-  const int rows_valid = min(BM, count - mt * BM);
-  const int n0 = nt * BN + wave * 32 * TN;  // this wave's first column
-  const uint32_t lane4 = (uint32_t)lane << 2;
-
-  // ---- A (gathered activation rows): per-thread sources, fixed over K
-  const uint16_t *xsrc[kALoads];
-  int sdst[kALoads];
-#pragma unroll
-  for (int i = 0; i < kALoads; ++i) {
-    const int idx = tid + i * kThreads;
-    const int r = idx >> 3, sg = idx & 7;
-    const int p = row0 + min(r, rows_valid - 1);          // padding rows repeat a valid row
-    const int src = a.gather ? a.perm[p] / a.k : p;
-    xsrc[i] = a.X + (int64_t)src * K + sg * 8;
-    sdst[i] = r * 8 + (sg ^ a_swizzle(r));
-  }
-
-  // ---- B: lane (g, nn) holds K values [32g, 32g + 32) of column nn of each N sub-tile
-  const int g = lane >> 5, nn = lane & 31;
-  const uint8_t *bsrc[TN];
-  int64_t brow[TN];
-#pragma unroll
-  for (int tn = 0; tn < TN; ++tn) {
-    const int n = min(n0 + tn * 32 + nn, N - 1);           // ragged N: clamp, never stored
-    brow[tn] = (int64_t)e * N + n;
-    bsrc[tn] = a.w.codes + brow[tn] * (K / 2) + g * 16;
-  }
-
-  const int nkb = K / 64;
-
-  f32x16_t acc[TM][TN];
-#pragma unroll
-  for (int tm = 0; tm < TM; ++tm)
-#pragma unroll
-    for (int tn = 0; tn < TN; ++tn)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[tm][tn][r] = 0.f;
-
-  // Two-slot rings (slot 0 holds even steps, slot 1 odd steps), as separate
-  // named arrays so that they stay in registers.
-  static_assert(kALoads == 2, "A staging holds two 16-byte segments per thread (BM = 64)");
-  uint4 areg0_0, areg0_1, areg1_0, areg1_1;
-  uint4 bq0[TN], bq1[TN];
-  uint2 bs0[TN], bs1[TN];   // raw block-scale bits (x; NF4_DQ: y = scale2)
-
-#define GNF4_LOAD_A(KB, DST)                                                              \
-  DST##_0 = *reinterpret_cast<const uint4 *>(xsrc[0] + (KB) * 64);                       \
-  DST##_1 = *reinterpret_cast<const uint4 *>(xsrc[1] + (KB) * 64);
-#define GNF4_LOAD_B(KB, BQ)                                                               \
-  _Pragma("unroll") for (int tn = 0; tn < TN; ++tn)                                      \
-      BQ[tn] = *reinterpret_cast<const uint4 *>(bsrc[tn] + (KB) * 32);
-#define GNF4_LOAD_S(KB, BS)                                                               \
-  _Pragma("unroll") for (int tn = 0; tn < TN; ++tn) {                                    \
-    /* raw scale bits only: converting here would wait for the load */                  \
-    if constexpr (FMT == GNF4_MXFP4) {                                                    \
-      BS[tn].x = reinterpret_cast<const uint8_t *>(a.w.scales)[brow[tn] * (K / 32) + 2 * (KB) + g]; \
-    } else if constexpr (FMT == GNF4_NF4) {                                               \
-      BS[tn].x = reinterpret_cast<const uint32_t *>(a.w.scales)[brow[tn] * (K / 64) + (KB)]; \
-    } else {                                                                              \
-      const int64_t blk = brow[tn] * (K / 64) + (KB);                                     \
-      BS[tn].x = (uint32_t)(int32_t)reinterpret_cast<const int8_t *>(a.w.scales)[blk];    \
-      BS[tn].y = __builtin_bit_cast(uint32_t, a.w.scales2[blk >> 8]);                     \
-    }                                                                                     \
-  }
-
-  GNF4_LOAD_B(0, bq0);
-  GNF4_LOAD_S(0, bs0);
-  GNF4_LOAD_A(0, areg0);
-  GNF4_LOAD_B(min(1, nkb - 1), bq1);
-  GNF4_LOAD_S(min(1, nkb - 1), bs1);
-  GNF4_LOAD_A(min(1, nkb - 1), areg1);
-  if constexpr (kLut) fill_nf4_lut_256(lut, tid);
-  As[0][sdst[0]] = areg0_0; As[0][sdst[1]] = areg0_1;
-
-  // One K step. S: ring slot of this step; AC/BQ/BS: this step's ring
-  // entries (refilled with step KB + 2); AN: the next step's A staging.
-#define GNF4_MFMA_STEP(KB, S, AC, AN, BQ, BS)                                             \
-  {                                                                                       \
-    /* no instruction crosses a step boundary: a decode hoisted into the */              \
-    /* previous step would wait on loads issued only one step earlier */                 \
-    __builtin_amdgcn_sched_barrier(0);                                                    \
-    __syncthreads(); /* As[S] holds step KB; As[S ^ 1] is no longer read */               \
-    __builtin_amdgcn_sched_barrier(0);                                                    \
-    bf16x8_t bf[TN][4];                                                                   \
-    float scl[TN];                                                                        \
-    _Pragma("unroll") for (int tn = 0; tn < TN; ++tn) {                                  \
-      const uint32_t qw[4] = {BQ[tn].x, BQ[tn].y, BQ[tn].z, BQ[tn].w};                    \
-      if constexpr (FMT == GNF4_MXFP4) scl[tn] = e8m0_to_f32(BS[tn].x);                   \
-      else if constexpr (FMT == GNF4_NF4) scl[tn] = __builtin_bit_cast(float, BS[tn].x);  \
-      else scl[tn] = (float)(int32_t)BS[tn].x * __builtin_bit_cast(float, BS[tn].y);      \
-      _Pragma("unroll") for (int j = 0; j < 4; ++j) {                                    \
-        uint32_t d[4];                                                                    \
-        if constexpr (kLut) {                                                             \
-          _Pragma("unroll") for (int i = 0; i < 4; ++i) d[i] =                           \
-              lut_read(lut, lut_addr(qw[j], lane4, i));                                   \
-        } else {                                                                          \
-          d[0] = fp4_pair<0>(qw[j], scl[tn]);                                             \
-          d[1] = fp4_pair<1>(qw[j], scl[tn]);                                             \
-          d[2] = fp4_pair<2>(qw[j], scl[tn]);                                             \
-          d[3] = fp4_pair<3>(qw[j], scl[tn]);                                             \
-        }                                                                                 \
-        bf[tn][j] = __builtin_bit_cast(bf16x8_t, make_uint4(d[0], d[1], d[2], d[3]));     \
-      }                                                                                   \
-    }                                                                                     \
-    {                                                                                     \
-      const int kn = min((KB) + 2, nkb - 1);                                              \
-      GNF4_LOAD_B(kn, BQ);                                                                \
-      GNF4_LOAD_A(kn, AC);                                                                \
-    }                                                                                     \
-    const uint4 *Ab = As[S];                                                              \
-    bf16x8_t af[TM][4];                                                                   \
-    _Pragma("unroll") for (int tm = 0; tm < TM; ++tm) {                                  \
-      const int r = tm * 32 + nn;                                                         \
-      _Pragma("unroll") for (int j = 0; j < 4; ++j) af[tm][j] =                          \
-          __builtin_bit_cast(bf16x8_t, Ab[r * 8 + ((4 * g + j) ^ a_swizzle(r))]);         \
-    }                                                                                     \
-    if constexpr (kLut) {                                                                 \
-      /* tiles in order t = tn * TM + tm; partials alternate between two register */     \
-      /* sets. Each MFMA of tile t is followed by 4 of the 16 scale FMAs of tile */      \
-      /* t - 1, and the schedule is pinned to that order, so the VALU FMAs run */         \
-      /* while the MFMA pipe works on the chain instead of after it. */                  \
-      f32x16_t Pp[2];                                                                     \
-      __builtin_amdgcn_sched_barrier(0);                                                  \
-      _Pragma("unroll") for (int t = 0; t < TM * TN; ++t) {                              \
-        const int tm = t % TM, tn = t / TM;                                               \
-        const int pm = (t + TM * TN - 1) % TM, pn = ((t + TM * TN - 1) / TM) % TN;        \
-        f32x16_t P = f32x16_t{};                                                          \
-        _Pragma("unroll") for (int j = 0; j < 4; ++j) {                                  \
-          P = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[tm][j], bf[tn][j], P, 0, 0, 0);  \
-          if (t > 0) {                                                                    \
-            _Pragma("unroll") for (int r2 = 4 * j; r2 < 4 * j + 4; ++r2) acc[pm][pn][r2] = \
-                __builtin_fmaf(scl[pn], Pp[(t - 1) & 1][r2], acc[pm][pn][r2]);            \
-          }                                                                               \
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                              \
-          if (t > 0) __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);                   \
-        }                                                                                 \
-        Pp[t & 1] = P;                                                                    \
-      }                                                                                   \
-      {                                                                                   \
-        constexpr int t = TM * TN - 1;                                                    \
-        const int pm = t % TM, pn = t / TM;                                               \
-        _Pragma("unroll") for (int r2 = 0; r2 < 16; ++r2) acc[pm][pn][r2] =              \
-            __builtin_fmaf(scl[pn], Pp[t & 1][r2], acc[pm][pn][r2]);                      \
-      }                                                                                   \
-      __builtin_amdgcn_sched_barrier(0);                                                  \
-    } else {                                                                              \
-      _Pragma("unroll") for (int tn = 0; tn < TN; ++tn)                                  \
-      _Pragma("unroll") for (int tm = 0; tm < TM; ++tm)                                  \
-      _Pragma("unroll") for (int j = 0; j < 4; ++j) acc[tm][tn] =                        \
-          __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[tm][j], bf[tn][j], acc[tm][tn], 0, 0, 0); \
-    }                                                                                     \
-    As[(S) ^ 1][sdst[0]] = AN##_0; As[(S) ^ 1][sdst[1]] = AN##_1;                          \
-    /* the scales of step KB + 2 are loaded after this step's last use of BS, so */      \
-    /* the loop-carried register is refilled in place */                                  \
-    GNF4_LOAD_S(min((KB) + 2, nkb - 1), BS);                                              \
-  }
-
-  int kb = 0;
-  for (; kb + 1 < nkb; kb += 2) {
-    GNF4_MFMA_STEP(kb, 0, areg0, areg1, bq0, bs0);
-    GNF4_MFMA_STEP(kb + 1, 1, areg1, areg0, bq1, bs1);
-  }
-  if (kb < nkb) GNF4_MFMA_STEP(kb, 0, areg0, areg1, bq0, bs0);
-#undef GNF4_MFMA_STEP
-#undef GNF4_LOAD_A
-#undef GNF4_LOAD_B
-#undef GNF4_LOAD_S
-
-  // ---- store: C fragment register r = 4i + j holds row 8i + 4g + j, column nn
-#pragma unroll
-  for (int tm = 0; tm < TM; ++tm)
-#pragma unroll
-    for (int tn = 0; tn < TN; ++tn) {
-      const int col = n0 + tn * 32 + nn;
-      if (col >= N) continue;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int r = tm * 32 + 8 * i + 4 * g + j;
-          if (r < rows_valid) a.Y[(int64_t)(row0 + r) * N + col] = acc[tm][tn][4 * i + j];
-        }
-    }
-}
-
-// ======================================== MFMA 16x16x32, full-line weight loads (NF4)
-
-// The NF4 prefill kernel. Tile 64 activation rows x 256 weight columns per
+// The prefill kernel for all three formats. Tile 64 activation rows x 256 weight columns per
 // workgroup; wave w owns columns [64w, 64w + 64) as four 16-column tiles and
 // all 64 rows as four 16-row tiles, with v_mfma_f32_16x16x32_bf16.
 //
@@ -657,30 +445,38 @@ __global__ __launch_bounds__(kThreads, 2) void mfma_kernel(GemmArgs a, int n_til
 // block: block-local K values 32 (p & 1) + 16 (p >> 1) + 8 j + i for MFMA j
 // of the block (i < 8). The activation fragments are read from LDS at the
 // same K values, so each block's two MFMAs form a partial that the block's
-// absmax scales before accumulation, as in mfma_kernel.
+// absmax scales before accumulation.
 //
 // Absmax values are read 8 blocks per column at a time: lane (p, c) holds
 // blocks 2p, 2p + 1 of the window for column c, and each block's value
-// reaches the 4 lanes of its column through ds_bpermute. Activation rows are
-// staged through LDS per block as in mfma_kernel. All global reads are
+// reaches the 4 lanes of its column through ds_bpermute. NF4_DQ loads the two
+// int8 values and their second-level scales with the window and forms the
+// float32 absmax when the window comes into use. MXFP4 instead has each lane
+// read the e8m0 scale of its own 32-K group per block and pass it to the
+// conversion, which makes a scaled partial unnecessary. Activation rows are
+// staged through LDS per block, double buffered. All global reads are
 // buffer loads: a uniform base per expert (or the activation tensor) plus a
 // fixed 32-bit lane offset and a uniform step offset; reads past a column's
 // last block fall on the next column or past the buffer (zero) and are not
-// used.
+// used. Activation tensors of 4 GiB or more (BIGX) are read with 64-bit
+// addresses instead; their rows and blocks are clamped in range either way.
 __device__ __forceinline__ int k16_seg(int p, int j) { return 4 * (p & 1) + 2 * (p >> 1) + j; }
 
 constexpr int kBufferDword3 = 0x00020000;   // raw buffer, 32-bit data format
 
-template <int FMT, int RT>
+template <int FMT, int RT, bool BIGX>
 __global__ __launch_bounds__(kThreads, 2) void mfma16_kernel(GemmArgs a, int n_tiles_n,
                                                              uint32_t x_bytes) {
-  static_assert(FMT == GNF4_NF4 || FMT == GNF4_MXFP4, "float32 absmax or e8m0 scales");
-  constexpr bool kNF4 = FMT == GNF4_NF4;
+  // NF4 and NF4_DQ decode through the table and scale each block's partial;
+  // MXFP4 folds its scale into the conversion.
+  constexpr bool kLut = FMT != GNF4_MXFP4;
+  constexpr bool kDQ = FMT == GNF4_NF4_DQ;
+  constexpr bool kWin = kLut;                   // absmax handled in 8-block windows
   constexpr int BM = 16 * RT, BN = 256;
   static_assert(RT >= 1 && RT <= 5, "16 to 80 rows");
   constexpr int kSegs = BM * 8;                 // 16-byte A segments per block
   constexpr int kALoads = (kSegs + kThreads - 1) / kThreads;
-  __shared__ uint32_t lut[kNF4 ? kLutWords : 1];
+  __shared__ uint32_t lut[kLut ? kLutWords : 1];
   __shared__ uint4 As[2][kSegs];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -705,17 +501,22 @@ __global__ __launch_bounds__(kThreads, 2) void mfma16_kernel(GemmArgs a, int n_t
   const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
       (void *)(a.w.codes + erow * (K / 2)), (short)0, (int)((uint32_t)N * (uint32_t)(K / 2)),
       kBufferDword3);
-  // NF4: float32 absmax [N][K/64]; MXFP4: e8m0 bytes [N][K/32]
-  const uint32_t scale_row = kNF4 ? (uint32_t)(K / 16) : (uint32_t)(K / 32);
+  // NF4: float32 absmax [N][K/64]; NF4_DQ: int8 [N][K/64]; MXFP4: e8m0 bytes [N][K/32]
+  const uint32_t scale_row = kDQ ? (uint32_t)(K / 64) : kWin ? (uint32_t)(K / 16) : (uint32_t)(K / 32);
   const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
       (void *)(reinterpret_cast<const uint8_t *>(a.w.scales) + erow * scale_row), (short)0,
       (int)((uint32_t)N * scale_row), kBufferDword3);
-  const __amdgpu_buffer_rsrc_t rx =
-      __builtin_amdgcn_make_buffer_rsrc((void *)a.X, (short)0, (int)x_bytes, kBufferDword3);
+  const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)a.X, (short)0, BIGX ? 0 : (int)x_bytes, kBufferDword3);
+  // NF4_DQ second-level scales: one float32 per 256 flat blocks of the tensor
+  const __amdgpu_buffer_rsrc_t rs2 = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)a.w.scales2, (short)0,
+      kDQ ? (int)(uint32_t)((((int64_t)a.w.E * N * nkb + 255) >> 8) * 4) : 0, kBufferDword3);
 
   // ---- A staging (per 64-K block): byte offsets of this thread's two
   // 16-byte segments in X, and their LDS slots
   uint32_t xoff[kALoads];
+  const uint8_t *xptr[kALoads];
   int sdst[kALoads];
 #pragma unroll
   for (int i = 0; i < kALoads; ++i) {
@@ -723,19 +524,26 @@ __global__ __launch_bounds__(kThreads, 2) void mfma16_kernel(GemmArgs a, int n_t
     const int r = idx >> 3, sg = idx & 7;
     const int pr = row0 + min(r, rows_valid - 1);
     const int src = a.gather ? a.perm[pr] / a.k : pr;
-    xoff[i] = (uint32_t)src * (uint32_t)(K * 2) + (uint32_t)sg * 16u;
+    if constexpr (BIGX)
+      xptr[i] = reinterpret_cast<const uint8_t *>(a.X) + (int64_t)src * (K * 2) + sg * 16;
+    else
+      xoff[i] = (uint32_t)src * (uint32_t)(K * 2) + (uint32_t)sg * 16u;
     sdst[i] = r * 8 + (sg ^ a_swizzle(r));
   }
 
-  // ---- weight columns (ragged N: clamped, never stored). NF4 scale offset:
-  // blocks 2p, 2p + 1 of an 8-block window; MXFP4: the 32-K group (p & 1) of
-  // a block, the block index coming from the step offset.
+  // ---- weight columns (ragged N: clamped, never stored). NF4 and NF4_DQ
+  // scale offset: blocks 2p, 2p + 1 of an 8-block window (NF4_DQ also keeps
+  // the flat index of block 2p for its second-level scale); MXFP4: the 32-K
+  // group (p & 1) of a block, the block index coming from the step offset.
   uint32_t coff[4], soff[4];
+  int64_t fblk[4];
 #pragma unroll
   for (int ct = 0; ct < 4; ++ct) {
     const uint32_t col = (uint32_t)min(nb + ct * 16 + c16, N - 1);
     coff[ct] = col * (uint32_t)(K / 2) + 16u * (uint32_t)p;
-    soff[ct] = kNF4 ? col * scale_row + 8u * (uint32_t)p : col * scale_row + (uint32_t)(p & 1);
+    soff[ct] = kDQ ? col * scale_row + 2u * (uint32_t)p
+               : kWin ? col * scale_row + 8u * (uint32_t)p : col * scale_row + (uint32_t)(p & 1);
+    fblk[ct] = (erow + col) * nkb + 2 * p;
   }
 
   f32x4_t acc[RT][4];
@@ -746,7 +554,9 @@ __global__ __launch_bounds__(kThreads, 2) void mfma16_kernel(GemmArgs a, int n_t
 
   uint4 qs0[4], qs1[4];               // stage slots (even / odd stages), raw codes
   uint4 ar0[kALoads], ar1[kALoads];   // A staging ring (even / odd blocks)
-  uint2 sw[4], sn[4];                 // NF4 absmax window (current / next): blocks 2p, 2p+1
+  uint2 sw[4], sn[4];                 // absmax window (current / next): blocks 2p, 2p+1
+  uint32_t dn[4];                     // NF4_DQ next window: int8 absmax of blocks 2p, 2p+1
+  uint2 tn[4];                        //   and their second-level scales
   uint32_t sb0[4], sb1[4];            // MXFP4 scale bytes ring (even / odd blocks)
 
 #define GNF4_LOAD_STAGE(S, Q)                                                             \
@@ -758,19 +568,45 @@ __global__ __launch_bounds__(kThreads, 2) void mfma16_kernel(GemmArgs a, int n_t
 #define GNF4_LOAD_A(KB, DST)                                                              \
   {                                                                                       \
     const int so_ = 128 * min((KB), nkb - 1);                                             \
-    _Pragma("unroll") for (int i = 0; i < kALoads; ++i)                                  \
+    _Pragma("unroll") for (int i = 0; i < kALoads; ++i) {                                \
+      if constexpr (BIGX)                                                                 \
+        DST[i] = *reinterpret_cast<const uint4 *>(xptr[i] + so_);                         \
+      else                                                                                \
         DST[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, xoff[i], so_, 0)); \
+    }                                                                                     \
   }
 #define GNF4_STORE_A(SLOT, SRC)                                                           \
   _Pragma("unroll") for (int i = 0; i < kALoads; ++i) As[SLOT][sdst[i]] = SRC[i];
 #define GNF4_LOAD_WINDOW(W)                                                               \
-  _Pragma("unroll") for (int ct = 0; ct < 4; ++ct)                                       \
-      sn[ct] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rs, soff[ct], 32 * (W), 0));
+  _Pragma("unroll") for (int ct = 0; ct < 4; ++ct) {                                     \
+    if constexpr (kDQ) {                                                                  \
+      /* two byte loads: a 16-bit load at an odd offset would be aligned down */         \
+      dn[ct] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rs, soff[ct], 8 * (W), 0) |  \
+               ((uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rs, soff[ct], 8 * (W) + 1, 0) << 8); \
+      const int64_t f_ = fblk[ct] + 8 * (W);                                              \
+      tn[ct].x = __builtin_amdgcn_raw_buffer_load_b32(rs2, (uint32_t)(f_ >> 8) * 4u, 0, 0); \
+      tn[ct].y = __builtin_amdgcn_raw_buffer_load_b32(rs2, (uint32_t)((f_ + 1) >> 8) * 4u, 0, 0); \
+    } else {                                                                              \
+      sn[ct] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rs, soff[ct], 32 * (W), 0)); \
+    }                                                                                     \
+  }
+  // NF4_DQ: the window's absmax as float32, int8 value times its group's scale
+#define GNF4_TAKE_WINDOW()                                                                \
+  _Pragma("unroll") for (int ct = 0; ct < 4; ++ct) {                                     \
+    if constexpr (kDQ) {                                                                  \
+      sw[ct].x = __builtin_bit_cast(uint32_t, (float)(int8_t)(dn[ct] & 0xffu) *           \
+                                                  __builtin_bit_cast(float, tn[ct].x));   \
+      sw[ct].y = __builtin_bit_cast(uint32_t, (float)(int8_t)((dn[ct] >> 8) & 0xffu) *    \
+                                                  __builtin_bit_cast(float, tn[ct].y));   \
+    } else {                                                                              \
+      sw[ct] = sn[ct];                                                                    \
+    }                                                                                     \
+  }
 #define GNF4_LOAD_SBYTES(KB, SB)                                                          \
   _Pragma("unroll") for (int ct = 0; ct < 4; ++ct)                                       \
       SB[ct] = __builtin_amdgcn_raw_buffer_load_b8(rs, soff[ct], 2 * min((KB), nkb - 1), 0);
 
-  if constexpr (kNF4) {
+  if constexpr (kWin) {
     GNF4_LOAD_WINDOW(0);
   } else {
     GNF4_LOAD_SBYTES(0, sb0);
@@ -780,7 +616,7 @@ __global__ __launch_bounds__(kThreads, 2) void mfma16_kernel(GemmArgs a, int n_t
   GNF4_LOAD_A(0, ar0);
   GNF4_LOAD_A(1, ar1);
   GNF4_LOAD_STAGE(1, qs1);
-  if constexpr (kNF4) fill_nf4_lut_256(lut, tid);
+  if constexpr (kLut) fill_nf4_lut_256(lut, tid);
   GNF4_STORE_A(0, ar0);
 
   // The two B fragments of block B of column tile CT (dwords x, y for block
@@ -791,7 +627,7 @@ __global__ __launch_bounds__(kThreads, 2) void mfma16_kernel(GemmArgs a, int n_t
     const uint32_t w0_ = (B) == 0 ? Q[CT].x : Q[CT].z;                                    \
     const uint32_t w1_ = (B) == 0 ? Q[CT].y : Q[CT].w;                                    \
     uint32_t d_[8];                                                                       \
-    if constexpr (kNF4) {                                                                 \
+    if constexpr (kLut) {                                                                 \
       _Pragma("unroll") for (int i = 0; i < 4; ++i) d_[i] = lut_read(lut, lut_addr(w0_, lane4, i)); \
       _Pragma("unroll") for (int i = 0; i < 4; ++i) d_[4 + i] = lut_read(lut, lut_addr(w1_, lane4, i)); \
     } else {                                                                              \
@@ -814,9 +650,9 @@ __global__ __launch_bounds__(kThreads, 2) void mfma16_kernel(GemmArgs a, int n_t
     __syncthreads(); /* As[kb & 1] holds block kb; As[(kb & 1) ^ 1] is free */            \
     __builtin_amdgcn_sched_barrier(0);                                                    \
     if ((B) == 0) {                                                                       \
-      if constexpr (kNF4) {                                                               \
+      if constexpr (kWin) {                                                               \
         if (((S) & 3) == 0) {                                                             \
-          _Pragma("unroll") for (int ct = 0; ct < 4; ++ct) sw[ct] = sn[ct];              \
+          GNF4_TAKE_WINDOW();                                                             \
           GNF4_LOAD_WINDOW(((S) >> 2) + 1);                                               \
         }                                                                                 \
       }                                                                                   \
@@ -826,11 +662,11 @@ __global__ __launch_bounds__(kThreads, 2) void mfma16_kernel(GemmArgs a, int n_t
         Q[ct] = make_uint4(r0[0], r1[0], r0[1], r1[1]);                                   \
       }                                                                                   \
     }                                                                                     \
-    /* NF4: absmax of block kb for this lane's column: window slot kb & 7, held */       \
-    /* by lane group (kb & 7) >> 1 = S & 3, element kb & 1 = B. MXFP4: the scale */       \
-    /* of the lane's own 32-K group, loaded two blocks ahead */                           \
+    /* NF4, NF4_DQ: absmax of block kb for this lane's column: window slot */            \
+    /* kb & 7, held by lane group (kb & 7) >> 1 = S & 3, element kb & 1 = B. */            \
+    /* MXFP4: the scale of the lane's own 32-K group, loaded two blocks ahead */          \
     float scl[4];                                                                         \
-    if constexpr (kNF4) {                                                                 \
+    if constexpr (kWin) {                                                                 \
       const int src = (16 * ((S) & 3) + c16) << 2;                                        \
       _Pragma("unroll") for (int ct = 0; ct < 4; ++ct)                                   \
         scl[ct] = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(                \
@@ -858,7 +694,7 @@ __global__ __launch_bounds__(kThreads, 2) void mfma16_kernel(GemmArgs a, int n_t
       __builtin_amdgcn_sched_barrier(0);                                                  \
       if (ct < 3) GNF4_DECODE(Q, B, ct + 1, fb[(ct + 1) & 1], scl[ct + 1]);              \
       _Pragma("unroll") for (int rt = 0; rt < RT; ++rt) {                                \
-        if constexpr (kNF4) {                                                             \
+        if constexpr (kLut) {                                                             \
           constexpr int kT = RT * 4;                                                      \
           const int t = ct * RT + rt;                                                     \
           const int pr = (t + kT - 1) % RT, pc = ((t + kT - 1) / RT) % 4;                 \
@@ -881,7 +717,7 @@ __global__ __launch_bounds__(kThreads, 2) void mfma16_kernel(GemmArgs a, int n_t
     __builtin_amdgcn_sched_barrier(0);                                                    \
     /* stage S + 2 reuses this stage's slot once block 1 is decoded */                   \
     if ((B) == 1) GNF4_LOAD_STAGE((S) + 2, Q);                                            \
-    if constexpr (kNF4) {                                                                 \
+    if constexpr (kLut) {                                                                 \
       _Pragma("unroll") for (int r2 = 0; r2 < 4; ++r2) acc[RT - 1][3][r2] =              \
           __builtin_fmaf(scl[3], Pp[(RT * 4 - 1) & 1][r2], acc[RT - 1][3][r2]);           \
     }                                                                                     \
@@ -904,6 +740,7 @@ __global__ __launch_bounds__(kThreads, 2) void mfma16_kernel(GemmArgs a, int n_t
 #undef GNF4_BLOCK
 #undef GNF4_DECODE
 #undef GNF4_LOAD_SBYTES
+#undef GNF4_TAKE_WINDOW
 #undef GNF4_LOAD_WINDOW
 #undef GNF4_STORE_A
 #undef GNF4_LOAD_A
@@ -1054,26 +891,12 @@ hipError_t launch_gemv(const GemmArgs &a, hipStream_t s) {
   }
 }
 
-template <int FMT, int TM, int TN>
-static hipError_t mfma_go(const GemmArgs &a, hipStream_t s) {
-  constexpr int BM = 32 * TM, BN = 4 * 32 * TN;
-  const int rows = a.T * a.k;
-  const int n_tiles_n = (a.w.N + BN - 1) / BN;
-  const int64_t m_tiles = (rows + BM - 1) / BM + std::min<int>(a.w.E, rows);
-  int64_t grid = m_tiles * n_tiles_n;
-  grid = (grid + 7) / 8 * 8;
-  if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL((mfma_kernel<FMT, TM, TN>), dim3((unsigned)grid), dim3(kThreads), 0, s, a,
-                     n_tiles_n);
-  return hipGetLastError();
-}
-
 // Bytes of the activation tensor the GEMM reads (gathered: T rows, else T*k).
 static int64_t x_bytes(const GemmArgs &a) {
   return (a.gather ? (int64_t)a.T : (int64_t)a.T * a.k) * a.w.K * 2;
 }
 
-template <int FMT, int RT>
+template <int FMT, int RT, bool BIGX>
 static hipError_t mfma16_go(const GemmArgs &a, hipStream_t s) {
   constexpr int BM = 16 * RT, BN = 256;
   const int rows = a.T * a.k;
@@ -1082,18 +905,16 @@ static hipError_t mfma16_go(const GemmArgs &a, hipStream_t s) {
   int64_t grid = m_tiles * n_tiles_n;
   grid = (grid + 7) / 8 * 8;
   if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL((mfma16_kernel<FMT, RT>), dim3((unsigned)grid), dim3(kThreads), 0, s, a,
-                     n_tiles_n, (uint32_t)x_bytes(a));
+  hipLaunchKernelGGL((mfma16_kernel<FMT, RT, BIGX>), dim3((unsigned)grid), dim3(kThreads), 0, s,
+                     a, n_tiles_n, BIGX ? 0u : (uint32_t)x_bytes(a));
   return hipGetLastError();
 }
 
 template <int FMT>
 static hipError_t mfma_pick(const GemmArgs &a, hipStream_t s) {
-  // the 16x16x32 kernel addresses activations with 32-bit buffer offsets
-  if constexpr (FMT == GNF4_NF4 || FMT == GNF4_MXFP4) {
-    if (x_bytes(a) < ((int64_t)1 << 32)) return mfma16_go<FMT, 4>(a, s);
-  }
-  return mfma_go<FMT, 2, 2>(a, s);
+  // 32-bit buffer offsets reach activation tensors below 4 GiB
+  if (x_bytes(a) < ((int64_t)1 << 32)) return mfma16_go<FMT, 4, false>(a, s);
+  return mfma16_go<FMT, 4, true>(a, s);
 }
 
 hipError_t launch_mfma(const GemmArgs &a, hipStream_t s) {

@@ -199,6 +199,20 @@ def small_layer(E, N, K, T, k, seed=0, distinct=True, gather=1):
     return {"W": W, "X": X, "ids": np.asarray(ids, dtype=np.int32).reshape(T, k), "tw": tw}
 
 
+def wide_layer(E, N, K, T, k, R, seed=0):
+    """A layer whose activation tensor is too large to draw on the host: R
+    distinct N(0,1) rows, token t taking row t % R (the tiling is done where
+    the tensor is needed), with W float32 [E, N, K] ~ N(0, 0.02) and ids
+    int32 [T, k] drawn uniformly with replacement.
+
+    Returns dict(W, X_base bf16 bits [R, K], ids)."""
+    g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 98, E, N, K, T, k, R])))
+    W = g.standard_normal((E, N, K), dtype=np.float32) * np.float32(W_STD)
+    X_base = f32_to_bf16_bits(g.standard_normal((R, K), dtype=np.float32))
+    ids = g.integers(0, E, size=(T, k), dtype=np.int32)
+    return {"W": W, "X_base": X_base, "ids": ids}
+
+
 def packed_weights(cfg, proj, seed=0):
     """Packed weights of one projection drawn directly as stored bytes, for
     full-size parity checks where quantizing a whole layer on the CPU would
