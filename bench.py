@@ -261,7 +261,7 @@ def gemm_kernel_name(cfg, T):
     """The HIP kernel gnf4_grouped_gemm runs for this workload's gate_up call
     (the library picks it from T*k and the format)."""
     if T * cfg.k <= 64:
-        return "gemv1_kernel" if T == 1 else "gemv_kernel"
+        return "gemv1w_kernel" if T == 1 else "gemv_kernel"
     return "mfma16_kernel"
 
 

@@ -98,6 +98,19 @@ __device__ __forceinline__ void fill_nf4_lut_256(uint32_t *lut, int tid) {
   }
 }
 
+// Fill the table with a workgroup of NT threads (NT divides 4096): thread t
+// writes the 16-byte groups g = t + NT i, each 4 copies of entry g / 16.
+template <int NT>
+__device__ __forceinline__ void fill_nf4_lut(uint32_t *lut, int tid) {
+  static_assert(4096 % NT == 0, "16-byte groups per thread");
+#pragma unroll
+  for (int i = 0; i < 4096 / NT; ++i) {
+    const uint32_t grp = (uint32_t)tid + NT * i, b = grp >> 4;
+    const uint32_t v = nf4_bf16(b >> 4) | (nf4_bf16(b & 15u) << 16);
+    *reinterpret_cast<uint4 *>(lut + grp * 4) = make_uint4(v, v, v, v);
+  }
+}
+
 // Byte offset into the table for byte i (0..3) of dword w, for this lane:
 // v_perm_b32 places byte i of w in bits 8..15 and this lane's copy offset
 // (lane * 4, < 256) in bits 0..7, so one instruction forms the address.

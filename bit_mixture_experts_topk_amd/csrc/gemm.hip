@@ -76,6 +76,8 @@ struct GemvRows {
 // Shape of the GEMV work split, fixed per launch.
 struct GemvGeom {
   int L_log2, L, RW, li, seg, wave, KCH, rows_per_item;
+  int ustride;   // wave slots between a wave's consecutive row slots (4: the
+                 // workgroup's waves interleave; 1: a wave owns its rows)
 };
 
 // Issue the code and scale loads of the rows of item block n0 of expert e:
@@ -94,7 +96,7 @@ __device__ __forceinline__ void gemv_load_rows(const GemmArgs &a, const GemvGeom
   const uint8_t *cb = a.w.codes + row0 * (K / 2);
   uint32_t r[U], ch[C];
 #pragma unroll
-  for (int u = 0; u < U; ++u) r[u] = (uint32_t)min((u * 4 + g.wave) * g.RW + g.seg, rmax);
+  for (int u = 0; u < U; ++u) r[u] = (uint32_t)min((u * g.ustride + g.wave) * g.RW + g.seg, rmax);
 #pragma unroll
   for (int c = 0; c < C; ++c) ch[c] = (uint32_t)min(g.li + c * g.L, g.KCH - 1);
   // The small scale loads go first and the code rows after them in row
@@ -213,7 +215,7 @@ __device__ __forceinline__ void gemv_store(const GemmArgs &a, const GemvGeom &g,
   const int N = a.w.N;
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    const int r = n0 + (u * 4 + g.wave) * g.RW + g.seg;
+    const int r = n0 + (u * g.ustride + g.wave) * g.RW + g.seg;
 #pragma unroll
     for (int t = 0; t < MT; ++t)
       if (g.li == 0 && r < N && tg + t < m) a.Y[(int64_t)(p0 + tg + t) * N + r] = v[u][t];
@@ -267,6 +269,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemv_kernel(GemmArgs a, int L_log
   g.li = lane & (g.L - 1);
   g.seg = lane >> L_log2;
   g.wave = tid >> 6;
+  g.ustride = 4;
   g.KCH = a.w.K >> 5;
   g.rows_per_item = 4 * g.RW * U;
   const int E = a.w.E, rows = a.T * a.k;
@@ -344,6 +347,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemv1_kernel(GemmArgs a, int L_lo
   g.li = lane & (g.L - 1);
   g.seg = lane >> L_log2;
   g.wave = tid >> 6;
+  g.ustride = 4;
   g.KCH = a.w.K >> 5;
   g.rows_per_item = 4 * g.RW * U;
   const int slot = (int)(blockIdx.x / (unsigned)items_per_expert);
@@ -377,6 +381,62 @@ __global__ __launch_bounds__(kThreads, 2) void gemv1_kernel(GemmArgs a, int L_lo
       gemv_dot<FMT, 1, U, C>(g, lut, lane4, R, x, v);
       gemv_store<1, U>(a, g, v, n0, p0 + t, 0, 1);
     }
+  }
+}
+
+// Persistent GEMV for one token's gathered input (T = 1, gather = 1: one
+// activation row, every routed row of an expert gets the same products).
+// Workgroups of 1024 threads share one decode table, filled once, so that 16
+// waves per CU (4 per SIMD) hide each other's load latency: while one wave
+// decodes, the others' rows are in flight. Each wave walks its own items (a
+// slot and a block of RW * U rows) of the n_active * items_per_expert items,
+// interleaved over the CUs. Lane j holds slot j's expert and routed-row
+// range, read once: one token has at most 64 slots.
+constexpr int kGemvWaveThreads = 1024;
+
+template <int FMT, int C, int U>
+__global__ __launch_bounds__(kGemvWaveThreads, 1) void gemv1w_kernel(GemmArgs a, int L_log2,
+                                                                     int items_per_expert,
+                                                                     int max_slots) {
+  constexpr bool kLut = FMT != GNF4_MXFP4;
+  constexpr int kWaves = kGemvWaveThreads / 64;
+  __shared__ uint32_t lut[kLut ? kLutWords : 1];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const uint32_t lane4 = (uint32_t)lane << 2;
+  GemvGeom g;
+  g.L_log2 = L_log2;
+  g.L = 1 << L_log2;
+  g.RW = 64 >> L_log2;
+  g.li = lane & (g.L - 1);
+  g.seg = lane >> L_log2;
+  g.wave = 0;
+  g.ustride = 1;
+  g.KCH = a.w.K >> 5;
+  g.rows_per_item = g.RW * U;
+  const int ipe = items_per_expert;
+
+  const int nact = *a.n_active;
+  const int ej = a.active[min(lane, max_slots - 1)];   // slot lane's expert (lanes past: unused)
+  uint32_t x[1][C][16];
+  gemv_load_x_row<C>(a, g, 0, x);
+  if constexpr (kLut) fill_nf4_lut<kGemvWaveThreads>(lut, tid);
+  const int ejc = max(ej, 0);
+  const int pj0 = a.offsets[ejc], pj1 = a.offsets[ejc + 1];
+  __syncthreads();                              // decode table written
+
+  const int total = nact * ipe;
+  const int W = (int)gridDim.x * kWaves;
+  GemvRows<U, C> R;
+  float v[U][1];
+  for (int it = (tid >> 6) * (int)gridDim.x + (int)blockIdx.x; it < total; it += W) {
+    const int slot = it / ipe;
+    const int n0 = (it - slot * ipe) * g.rows_per_item;
+    gemv_load_rows<FMT, U, C>(a, g, __builtin_amdgcn_readlane(ej, slot), n0, R);
+    gemv_dot<FMT, 1, U, C>(g, lut, lane4, R, x, v);
+    const int p0 = __builtin_amdgcn_readlane(pj0, slot);
+    const int m = __builtin_amdgcn_readlane(pj1, slot) - p0;
+    for (int t = 0; t < m; ++t) gemv_store<1, U>(a, g, v, n0, p0 + t, 0, 1);
   }
 }
 
@@ -785,6 +845,28 @@ static const GemvVariant *gemv_variant(int MT, int C) {
   return nullptr;
 }
 
+// One token, gathered input: the persistent kernel, one workgroup per CU (or
+// as many as are resident at once).
+template <int FMT, int C, int U>
+static hipError_t gemv1w_go(const GemmArgs &a, int L_log2, int max_slots, hipStream_t s) {
+  static int per_cu = 0;
+  if (per_cu == 0) {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gemv1w_kernel<FMT, C, U>,
+                                                     kGemvWaveThreads, 0) != hipSuccess || n < 1)
+      n = 1;
+    per_cu = n;
+  }
+  const int rows_per_item = (64 >> L_log2) * U;
+  const int items = (a.w.N + rows_per_item - 1) / rows_per_item;
+  const int64_t waves = (int64_t)max_slots * items;
+  const int64_t grid = std::min<int64_t>((int64_t)per_cu * device_cu_count(),
+                                         (waves + kGemvWaveThreads / 64 - 1) / (kGemvWaveThreads / 64));
+  hipLaunchKernelGGL((gemv1w_kernel<FMT, C, U>), dim3((unsigned)grid),
+                     dim3(kGemvWaveThreads), 0, s, a, L_log2, items, max_slots);
+  return hipGetLastError();
+}
+
 template <int FMT, int MT, int C, int U>
 static hipError_t gemv_go(const GemmArgs &a, int L_log2, int max_slots, hipStream_t s) {
   const int L = 1 << L_log2;
@@ -794,15 +876,22 @@ static hipError_t gemv_go(const GemmArgs &a, int L_log2, int max_slots, hipStrea
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
   if constexpr (MT == 1) {
+    // one token in routed order (a gathered one takes gemv1w_kernel)
     if (a.T == 1) {
       hipLaunchKernelGGL((gemv1_kernel<FMT, C, U>), dim3((unsigned)grid), dim3(kThreads), 0, s, a,
                          L_log2, items);
       return hipGetLastError();
     }
   }
-  hipLaunchKernelGGL((gemv_kernel<FMT, MT, C, U>), dim3((unsigned)grid), dim3(kThreads), 0, s, a,
-                     L_log2, items);
-  return hipGetLastError();
+  // Two or more tokens take one token per group only when K needs 4 chunks
+  // per lane (K > 6144).
+  if constexpr (MT == 1 && C < 4) {
+    return hipErrorInvalidValue;
+  } else {
+    hipLaunchKernelGGL((gemv_kernel<FMT, MT, C, U>), dim3((unsigned)grid), dim3(kThreads), 0, s, a,
+                       L_log2, items);
+    return hipGetLastError();
+  }
 }
 
 #define GNF4_GEMV_CASE(mt, c, u)                                                 \
@@ -872,7 +961,33 @@ static int gemv_pick_u(const GemvVariant &v, int fmt, int N, int L_log2, int max
   return last;
 }
 
+// Rows per wave slot of the one-token gathered kernel for C chunks per lane
+// (measured fastest on the workload shapes, and free of register spills).
+template <int FMT>
+static hipError_t gemv1w_dispatch(const GemmArgs &a, int C, int L_log2, int max_slots,
+                                  hipStream_t s) {
+  switch (C) {
+    case 1: return gemv1w_go<FMT, 1, 4>(a, L_log2, max_slots, s);
+    case 2: return gemv1w_go<FMT, 2, 4>(a, L_log2, max_slots, s);
+    case 3: return gemv1w_go<FMT, 3, 2>(a, L_log2, max_slots, s);
+    case 4:
+      if constexpr (FMT == GNF4_NF4_DQ) return gemv1w_go<FMT, 4, 1>(a, L_log2, max_slots, s);
+      else return gemv1w_go<FMT, 4, 2>(a, L_log2, max_slots, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 hipError_t launch_gemv(const GemmArgs &a, hipStream_t s) {
+  if (a.T == 1 && a.gather) {
+    int L_log2 = 6, C = 1;
+    if (!gemv_shape(a.w.K, 1, &L_log2, &C)) return hipErrorInvalidValue;
+    const int max_slots = std::min<int>(a.w.E, a.k);
+    switch (a.w.format) {
+      case GNF4_NF4: return gemv1w_dispatch<GNF4_NF4>(a, C, L_log2, max_slots, s);
+      case GNF4_NF4_DQ: return gemv1w_dispatch<GNF4_NF4_DQ>(a, C, L_log2, max_slots, s);
+      default: return gemv1w_dispatch<GNF4_MXFP4>(a, C, L_log2, max_slots, s);
+    }
+  }
   int MT = gemv_tokens(a.T);
   int L_log2 = 6, C = 1;
   while (!gemv_shape(a.w.K, MT, &L_log2, &C)) {

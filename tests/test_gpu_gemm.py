@@ -58,17 +58,23 @@ def test_gemm_permuted_input(fmt, T, k, distinct):
     compare_rows(Y, Y_ref, r_ref, "gather=0 %s T=%d" % (fmt, T))
 
 
-@pytest.mark.parametrize("T,k", [(6, 4), (50, 4)])
-def test_gemm_duplicates_and_bad_ids(T, k):
+@pytest.mark.parametrize("fmt", ["nf4", "mxfp4"])
+@pytest.mark.parametrize("T,k", [(1, 8), (6, 4), (50, 4)])
+def test_gemm_duplicates_and_bad_ids(fmt, T, k):
+    """Repeated experts (several routed rows share one expert's products, or
+    one expert's weights serve several token rows) and dropped ids; T = 1
+    is the one-token gathered kernel."""
     g = gnf4()
     E, N, K = 5, 128, 256
     case = synth.small_layer(E, N, K, T, k, seed=3, distinct=False)
     ids = case["ids"].copy()
     ids[0, 0] = -1
     ids[-1, -1] = E + 3
-    Y, Y_ref, r_ref = run_layer_call(g, "nf4", case["W"], case["X"], ids, 1, k, "dup/bad")
+    valid = ids[(ids >= 0) & (ids < E)]
+    assert len(np.unique(valid)) < len(valid)            # the case needs a repeat
+    Y, Y_ref, r_ref = run_layer_call(g, fmt, case["W"], case["X"], ids, 1, k, "dup/bad")
     assert r_ref["bad"][0] == 1
-    compare_rows(Y, Y_ref, r_ref, "duplicates and bad ids")
+    compare_rows(Y, Y_ref, r_ref, "duplicates and bad ids %s T=%d" % (fmt, T))
 
 
 @pytest.mark.parametrize("fmt", ["nf4", "nf4_dq", "mxfp4"])
