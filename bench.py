@@ -331,7 +331,7 @@ def cpu_baseline(cfg, T):
         for proj, codes, scales, scales2 in packs:
             per = codes[0].nbytes + scales[0].nbytes
             byts += len(active) * per
-        if time.perf_counter() - t_start > 10.0 or reps >= 20:
+        if time.perf_counter() - t_start > 12.0 or reps >= 400:
             break
     threads = cores
     if threadpool_info is not None:

@@ -971,7 +971,7 @@ static hipError_t gemv1w_dispatch(const GemmArgs &a, int C, int L_log2, int max_
     case 2: return gemv1w_go<FMT, 2, 4>(a, L_log2, max_slots, s);
     case 3: return gemv1w_go<FMT, 3, 2>(a, L_log2, max_slots, s);
     case 4:
-      if constexpr (FMT == GNF4_NF4_DQ) return gemv1w_go<FMT, 4, 1>(a, L_log2, max_slots, s);
+      if constexpr (FMT != GNF4_MXFP4) return gemv1w_go<FMT, 4, 1>(a, L_log2, max_slots, s);
       else return gemv1w_go<FMT, 4, 2>(a, L_log2, max_slots, s);
     default: return hipErrorInvalidValue;
   }
