@@ -13,6 +13,8 @@ precision, written for a reader checking it against the pages by eye:
 * ``routing``  expert histogram, exclusive prefix sum, stable permutation.
 * ``grouped_gemm``  per-expert fp64 matmul on the gathered rows.
 * ``combine``  weighted sum of the top-k rows back per token.
+* ``layer``    the router's top-k choice with softmax weights, SwiGLU between
+               the projections, and exact float64 -> bfloat16 rounding.
 
 Sources. The pages describe a kernel that computes mixture-of-experts matmuls
 directly on 4-bit packed expert weights, one launch for all active experts,
@@ -26,4 +28,4 @@ Parity status per function is listed in each module header. Every function
 here is pinned by at least one test that does not re-run its own formula.
 """
 
-from . import nf4, mxfp4, routing, grouped_gemm, combine  # noqa: F401
+from . import nf4, mxfp4, routing, grouped_gemm, combine, layer  # noqa: F401
