@@ -18,6 +18,8 @@ Reported (one JSON line on stdout):
              launch / its mean duration from HIP events on the launch stream
   prefill    TFLOP/s of the prefill step and the roofline of its gate_up
              MFMA kernel (algorithmic flops 2*rows*N*K per launch)
+  ffn_layer  the whole FFN layer step (router top-k from logits, gate_up,
+             SwiGLU, down on the SwiGLU output, combine) at the same T's
   cpu_baseline  the float64 CPU oracle (dequant + matmul + combine) timed on
              this host on one decode step of the same workload
 Inputs are resident in device memory before timing starts.
@@ -133,12 +135,21 @@ class Layer:
 
 
 class StepSlot:
-    """Inputs, outputs and the captured graph of one step."""
+    """Inputs, outputs and the captured graph of one step. ffn: the whole FFN
+    layer (router top-k from logits, gate_up, SwiGLU, down on its output,
+    combine) instead of route + both projections on standalone inputs."""
 
-    def __init__(self, torch, gnf4, cfg, layer, T, seed):
+    def __init__(self, torch, gnf4, cfg, layer, T, seed, ffn=False):
         import synth
         k = cfg.k
-        ids, tw = synth.routing_inputs(cfg, T, seed=seed)
+        self.ffn = ffn
+        if ffn:
+            logits = synth.router_logits(cfg, T, seed=seed).astype(np.float32)
+            self.logits = torch.from_numpy(logits).cuda()
+            ids = np.argsort(-logits.astype(np.float64), axis=1, kind="stable")[:, :k]
+            tw = np.zeros((T, k), dtype=np.float32)
+        else:
+            ids, tw = synth.routing_inputs(cfg, T, seed=seed)
         self.n_active = int(np.unique(ids).size)
         self.T = T
         self.ids = torch.from_numpy(ids).cuda()
@@ -147,8 +158,12 @@ class StepSlot:
         self.X = torch.from_numpy(synth.activations(cfg, T, first.K, synth.T_X, seed, T).view(np.int16)).cuda()
         self.layer = layer
         self.r = gnf4.route_buffers(T, k, cfg.E)
+        self.r["topk_ids"] = torch.empty((T, k), dtype=torch.int32, device="cuda")
+        self.r["topk_w"] = torch.empty((T, k), dtype=torch.float32, device="cuda")
         self.Y = [torch.empty((T * k, p.N), dtype=torch.float32, device="cuda") for p in cfg.projs]
-        if len(cfg.projs) > 1:
+        if ffn:
+            self.H = torch.empty((T * k, cfg.inter), dtype=torch.int16, device="cuda")
+        elif len(cfg.projs) > 1:
             down = cfg.projs[1]
             self.Xd = torch.from_numpy(synth.activations(cfg, T * k, down.K, synth.T_X_DOWN, seed, T)
                                        .view(np.int16)).cuda()
@@ -157,6 +172,13 @@ class StepSlot:
 
     def run(self, gnf4):
         cfg, T, k = self.layer.cfg, self.T, self.layer.cfg.k
+        if self.ffn:
+            r = gnf4.route_logits(self.logits, k, out=self.r)
+            gnf4.grouped_gemm(self.layer.projs[0], self.X, 1, r, T, k, self.Y[0])
+            gnf4.swiglu(self.Y[0], cfg.inter, self.H)
+            gnf4.grouped_gemm(self.layer.projs[1], self.H, 0, r, T, k, self.Y[1])
+            gnf4.combine(self.Y[1], r["inv"], r["topk_w"], T, k, self.out)
+            return
         r = gnf4.route(self.ids, cfg.E, out=self.r)
         gnf4.grouped_gemm(self.layer.projs[0], self.X, 1, r, T, k, self.Y[0])
         last = self.Y[0]
@@ -408,6 +430,29 @@ def main():
         del slots, layers, chain
         torch.cuda.empty_cache()
 
+    if len(cfg.projs) > 1 and args.only is None:
+        # the whole FFN layer (router top-k, gate_up, SwiGLU, down, combine)
+        ffn = {}
+        for T, tag in ((T_dec, "decode"), (T_pre, "prefill")):
+            if (tag == "decode") != (T * cfg.k <= 64):
+                continue
+            step_bytes = layer_bytes * min(1.0, T * cfg.k / cfg.E)
+            copies = int(min(32 if tag == "decode" else 8,
+                             max(2, np.ceil(3 * MALL_BYTES / max(step_bytes, 1)))))
+            layers = [base] + [base.clone(torch) for _ in range(copies - 1)]
+            nsl = max(copies, 16) if tag == "decode" else copies
+            slots = [StepSlot(torch, gnf4, cfg, layers[i % copies], T, seed=300 + i, ffn=True)
+                     for i in range(nsl)]
+            for sl in slots:
+                sl.capture(torch, gnf4)
+            chain = capture_chain(torch, gnf4, slots)
+            steps = args.steps if tag == "decode" else max(10, args.steps // 10)
+            dt, byts, fl = time_steps(torch, slots, chain, steps, max(2, args.warmup // 5))
+            ffn[tag] = (T, dt, byts, fl)
+            del slots, layers, chain
+            torch.cuda.empty_cache()
+        out["ffn"] = ffn
+
     if args.calib_copy:
         a = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
         b = torch.empty_like(a)
@@ -457,6 +502,19 @@ def main():
             result["unit"] = "TFLOP/s"
             result["ms_per_step"] = round(p["ms_per_step"], 5)
             result["roofline"] = result["prefill"]["roofline"]
+    if out.get("ffn"):
+        f = {}
+        if "decode" in out["ffn"]:
+            T, dt, byts, _ = out["ffn"]["decode"]
+            f["decode"] = {"T": T, "step_us": round(dt * 1e6, 3), "packed_GBps": round(byts / dt / 1e9, 2),
+                           "pct_hbm_peak": round(100 * byts / dt / 1e9 / HBM_PEAK_GBS, 2)}
+        if "prefill" in out["ffn"]:
+            T, dt, _, fl = out["ffn"]["prefill"]
+            f["prefill"] = {"T": T, "step_ms": round(dt * 1e3, 4), "tflops": round(fl / dt / 1e12, 2),
+                            "pct_mfma_peak": round(100 * fl / dt / 1e12 / BF16_PEAK_TFLOPS, 2)}
+        f["steps"] = ("route_logits (top-k + softmax + route), gate_up GEMM, SwiGLU (bf16 H), "
+                      "down GEMM on H, combine")
+        result["ffn_layer"] = f
     if not args.no_cpu and decode_ok:
         result["cpu_baseline"] = cpu_baseline(cfg, T_dec)
     print(json.dumps(result), flush=True)

@@ -120,6 +120,41 @@ gnf4_status gnf4_route(const int32_t *topk_ids, int32_t T, int32_t k, int32_t E,
                        "route launch");
 }
 
+gnf4_status gnf4_route_logits(const float *logits, int32_t T, int32_t k, int32_t E,
+                              int32_t *topk_ids, float *topk_w, int32_t *counts,
+                              int32_t *offsets, int32_t *perm, int32_t *inv, int32_t *active,
+                              int32_t *n_active, int32_t *bad_id_flag, gnf4_stream_t stream) {
+  if (E < 1 || E > GNF4_MAX_EXPERTS)
+    return fail(GNF4_ERR_INVALID_ARG, "E = %d outside [1, %d]", E, GNF4_MAX_EXPERTS);
+  if (k < 1 || k > 64 || k > E)
+    return fail(GNF4_ERR_INVALID_ARG, "k = %d outside [1, min(64, E = %d)]", k, E);
+  if (T < 0) return fail(GNF4_ERR_INVALID_ARG, "T = %d is negative", T);
+  if ((int64_t)T * k >= ((int64_t)1 << 31) - 1024)
+    return fail(GNF4_ERR_INVALID_ARG, "T*k too large");
+  if (!counts || !offsets || !active || !n_active || !bad_id_flag)
+    return fail(GNF4_ERR_INVALID_ARG, "an output pointer is NULL");
+  if (T > 0 && (!logits || !topk_ids || !topk_w || !perm || !inv))
+    return fail(GNF4_ERR_INVALID_ARG, "logits, topk_ids, topk_w, perm or inv is NULL");
+  hipError_t e = launch_topk(logits, T, E, k, topk_ids, topk_w, (hipStream_t)stream);
+  if (e != hipSuccess) return device_status(e, "top-k launch");
+  return device_status(launch_route(topk_ids, T, k, E, counts, offsets, perm, inv, active,
+                                    n_active, bad_id_flag, (hipStream_t)stream),
+                       "route launch");
+}
+
+gnf4_status gnf4_swiglu(const float *Y, int32_t rows, int32_t I, uint16_t *H,
+                        gnf4_stream_t stream) {
+  if (rows < 0) return fail(GNF4_ERR_INVALID_ARG, "rows = %d is negative", rows);
+  if (I < 4 || I % 4 || I > GNF4_MAX_N / 2)
+    return fail(GNF4_ERR_INVALID_ARG, "I = %d must be a positive multiple of 4 up to %d", I,
+                GNF4_MAX_N / 2);
+  if (rows == 0) return ok();
+  if (!Y || !H) return fail(GNF4_ERR_INVALID_ARG, "Y or H is NULL");
+  if (!aligned16(Y) || ((uintptr_t)H & 7u))
+    return fail(GNF4_ERR_INVALID_ARG, "Y must be 16-byte and H 8-byte aligned");
+  return device_status(launch_swiglu(Y, rows, I, H, (hipStream_t)stream), "swiglu launch");
+}
+
 gnf4_status gnf4_grouped_gemm(const gnf4_weights *w, const uint16_t *X, int32_t gather,
                               const int32_t *offsets, const int32_t *perm, const int32_t *active,
                               const int32_t *n_active, int32_t T, int32_t k, float *Y,

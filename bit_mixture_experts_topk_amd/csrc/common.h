@@ -137,6 +137,9 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
 hipError_t launch_route(const int32_t *ids, int32_t T, int32_t k, int32_t E, int32_t *counts,
                         int32_t *offsets, int32_t *perm, int32_t *inv, int32_t *active,
                         int32_t *n_active, int32_t *bad, hipStream_t s);
+hipError_t launch_topk(const float *logits, int32_t T, int32_t E, int32_t k, int32_t *ids,
+                       float *w, hipStream_t s);
+hipError_t launch_swiglu(const float *Y, int32_t rows, int32_t I, uint16_t *H, hipStream_t s);
 hipError_t launch_gemv(const GemmArgs &a, hipStream_t s);
 hipError_t launch_mfma(const GemmArgs &a, hipStream_t s);
 hipError_t launch_combine(const float *Y, const int32_t *inv, const float *w, int32_t T,

@@ -24,8 +24,9 @@ FORMATS = {"nf4": NF4, "nf4_dq": NF4_DQ, "mxfp4": MXFP4}
 STATUS = {0: "OK", 1: "INVALID_ARG", 2: "UNSUPPORTED", 4: "DEVICE"}
 
 # Every entry point declared in include/gnf4.h.
-EXPORTS = ("gnf4_route", "gnf4_grouped_gemm", "gnf4_combine", "gnf4_dequant", "gnf4_quantize",
-           "gnf4_nf4_codebook", "gnf4_last_error", "gnf4_build_id")
+EXPORTS = ("gnf4_route", "gnf4_route_logits", "gnf4_grouped_gemm", "gnf4_swiglu", "gnf4_combine",
+           "gnf4_dequant", "gnf4_quantize", "gnf4_nf4_codebook", "gnf4_last_error",
+           "gnf4_build_id")
 
 
 class Gnf4Error(RuntimeError):
@@ -52,6 +53,8 @@ def lib():
         L = ctypes.CDLL(LIB_PATH)
         P, I, S = ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p
         L.gnf4_route.argtypes = [P, I, I, I, P, P, P, P, P, P, P, S]
+        L.gnf4_route_logits.argtypes = [P, I, I, I, P, P, P, P, P, P, P, P, P, S]
+        L.gnf4_swiglu.argtypes = [P, I, I, P, S]
         L.gnf4_grouped_gemm.argtypes = [ctypes.POINTER(CWeights), P, I, P, P, P, P, I, I, P, S]
         L.gnf4_combine.argtypes = [P, P, P, I, I, I, P, S]
         L.gnf4_dequant.argtypes = [ctypes.POINTER(CWeights), I, P, S]
@@ -181,6 +184,38 @@ def route(topk_ids, E, out=None):
     r["perm"] = r["perm"][:T * k]
     r["inv"] = r["inv"][:T * k]
     return r
+
+
+def route_logits(logits, k, out=None):
+    """Top-k of float32 router logits [T, E] (CUDA) with softmax weights, then
+    route; returns the route dict plus "topk_ids" [T, k] and "topk_w" [T, k]."""
+    _dev(logits, torch.float32, "logits")
+    T, E = logits.shape
+    r = dict(out) if out is not None else route_buffers(T, k, E, logits.device)
+    if "topk_ids" not in r:
+        r["topk_ids"] = torch.empty((max(T, 1), k), dtype=torch.int32, device=logits.device)
+        r["topk_w"] = torch.empty((max(T, 1), k), dtype=torch.float32, device=logits.device)
+    _check(lib().gnf4_route_logits(_ptr(logits), T, k, E, _ptr(r["topk_ids"]), _ptr(r["topk_w"]),
+                                   _ptr(r["counts"]), _ptr(r["offsets"]), _ptr(r["perm"]),
+                                   _ptr(r["inv"]), _ptr(r["active"]), _ptr(r["n_active"]),
+                                   _ptr(r["bad"]), _stream()), "gnf4_route_logits")
+    r["perm"] = r["perm"][:T * k]
+    r["inv"] = r["inv"][:T * k]
+    r["topk_ids"] = r["topk_ids"][:T]
+    r["topk_w"] = r["topk_w"][:T]
+    return r
+
+
+def swiglu(Y, I, H=None):
+    """H [rows, I] bf16 bits (int16) = bf16(silu(Y[:, :I]) * Y[:, I:2I])."""
+    _dev(Y, torch.float32, "Y")
+    rows = Y.shape[0]
+    if Y.shape[1] != 2 * I:
+        raise ValueError("Y must have 2*I columns")
+    if H is None:
+        H = torch.empty((max(rows, 1), I), dtype=torch.int16, device=Y.device)
+    _check(lib().gnf4_swiglu(_ptr(Y), rows, I, _ptr(H), _stream()), "gnf4_swiglu")
+    return H
 
 
 def grouped_gemm(w, X, gather, r, T, k, Y=None):

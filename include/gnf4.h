@@ -13,6 +13,12 @@
  *   gnf4_route          top-k expert ids -> per-expert row segments
  *   gnf4_grouped_gemm   Y[p] = A[p] . W[expert(p)]^T for every routed row p
  *   gnf4_combine        out[t] = sum_j w[t,j] * Y[inv[t*k+j]]
+ * and a whole FFN layer adds the steps either side of the GEMM:
+ *   gnf4_route_logits   router logits -> top-k ids and weights, then route
+ *   gnf4_grouped_gemm   gate_up projection (gathered token rows)
+ *   gnf4_swiglu         H = silu(gate) * up, bf16, in routed order
+ *   gnf4_grouped_gemm   down projection (rows of H, routed order)
+ *   gnf4_combine
  *
  * Conventions for every entry point:
  *  - All array pointers are DEVICE pointers owned by the caller; the library
@@ -126,6 +132,42 @@ gnf4_status gnf4_grouped_gemm(const gnf4_weights *w, const uint16_t *X, int32_t 
  * [T][k], out float32 [T][N] (16-byte aligned). N % 4 == 0. */
 gnf4_status gnf4_combine(const float *Y, const int32_t *inv, const float *topk_w,
                          int32_t T, int32_t k, int32_t N, float *out, gnf4_stream_t stream);
+
+/* gnf4_route_logits -- the router's choice, then gnf4_route.
+ *
+ * The pages put the fused kernel behind a real router (section cited at the
+ * top, demonstration paragraph) without describing it; the definition used
+ * is that of the public models the workloads are shaped after. For each
+ * token t of logits float32 [T][E] (row-major):
+ *   topk_ids[t][j], j < k   the k largest logits in descending order, ties
+ *                           to the lower expert id; NaN ranks below every
+ *                           number (chosen only when fewer than k numbers
+ *                           remain, in ascending id)           int32 [T][k]
+ *   topk_w[t][j]            float32 of the softmax of the k chosen logits,
+ *                           computed in float64 with the largest chosen
+ *                           logit subtracted and the exponentials summed in
+ *                           rank order                         float32 [T][k]
+ * then gnf4_route(topk_ids, T, k, E, ...) with the same outputs and
+ * meaning. Limits: 1 <= k <= 64, k <= E <= GNF4_MAX_EXPERTS, 0 <= T,
+ * T*k < 2^31. T = 0 behaves as gnf4_route with T = 0. */
+gnf4_status gnf4_route_logits(const float *logits, int32_t T, int32_t k, int32_t E,
+                              int32_t *topk_ids, float *topk_w, int32_t *counts,
+                              int32_t *offsets, int32_t *perm, int32_t *inv, int32_t *active,
+                              int32_t *n_active, int32_t *bad_id_flag, gnf4_stream_t stream);
+
+/* gnf4_swiglu -- the activation between the two projections.
+ *   H[p][i] = bf16(silu(Y[p][i]) * Y[p][I + i]),  silu(x) = x / (1 + exp(-x))
+ * for p < rows, i < I: Y float32 [rows][2I] is the gate_up output with the
+ * gate in columns [0, I) and up in [I, 2I); H (uint16 bf16 bits [rows][I])
+ * is the input of the down projection in the same routed order (gather = 0).
+ * The product is formed in float64 and rounded once to bf16 (nearest, ties
+ * to even; NaN gives 0x7FC0), so H does not depend on how the GPU orders
+ * float32 operations. Rows of Y past the routed total (dropped ids) hold
+ * unspecified values, and so do the matching rows of H.
+ * I % 4 == 0, Y 16-byte and H 8-byte aligned. Not described on the pages
+ * (same reading as gnf4_route_logits). */
+gnf4_status gnf4_swiglu(const float *Y, int32_t rows, int32_t I, uint16_t *H,
+                        gnf4_stream_t stream);
 
 /* gnf4_dequant -- decode expert e of w to float32 out [N][K] (test aid).
  * NF4: fp32(c[q] * absmax); NF4_DQ: fp32(c[q] * fp32(q8 * scale2));

@@ -103,6 +103,37 @@ def test_route_rejects(L):
     assert L.gnf4_route(p, 4, 2, 8, p, None, p, p, p, p, p, None) == INVALID
 
 
+def test_route_logits_rejects(L):
+    p = 0x1000
+    ok_args = [p, 4, 2, 8, p, p, p, p, p, p, p, p, p, None]
+
+    def call(**kw):
+        a = list(ok_args)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return L.gnf4_route_logits(*a)
+
+    assert call(a3=0) == INVALID and "E = 0" in gnf4.last_error()
+    assert call(a2=9) == INVALID and "k = 9" in gnf4.last_error()        # k > E
+    assert call(a2=0) == INVALID
+    assert call(a2=65, a3=128) == INVALID                                  # k > 64
+    assert call(a1=-1) == INVALID
+    assert call(a0=None) == INVALID                                        # logits
+    assert call(a5=None) == INVALID                                        # topk_w
+    assert call(a7=None) == INVALID                                        # offsets
+
+
+def test_swiglu_rejects(L):
+    p = 0x1000
+    assert L.gnf4_swiglu(p, 4, 6, p, None) == INVALID and "I = 6" in gnf4.last_error()
+    assert L.gnf4_swiglu(p, 4, 0, p, None) == INVALID
+    assert L.gnf4_swiglu(p, -1, 8, p, None) == INVALID
+    assert L.gnf4_swiglu(0x1004, 4, 8, p, None) == INVALID                # Y alignment
+    assert L.gnf4_swiglu(p, 4, 8, 0x1002, None) == INVALID                # H alignment
+    assert L.gnf4_swiglu(None, 4, 8, p, None) == INVALID
+    assert L.gnf4_swiglu(None, 0, 8, None, None) == 0                     # nothing to do
+
+
 def test_combine_rejects(L):
     p = 0x1000
     assert L.gnf4_combine(p, p, p, 2, 2, 6, p, None) == INVALID
