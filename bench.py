@@ -18,8 +18,9 @@ Reported (one JSON line on stdout):
              launch / its mean duration from HIP events on the launch stream
   prefill    TFLOP/s of the prefill step and the roofline of its gate_up
              MFMA kernel (algorithmic flops 2*rows*N*K per launch)
-  ffn_layer  the whole FFN layer step (router top-k from logits, gate_up,
-             SwiGLU, down on the SwiGLU output, combine) at the same T's
+  ffn_layer  the whole FFN layer step (router top-k from logits, gate_up with
+             the SwiGLU epilogue, down on its bf16 output, combine) at the
+             same T's
   cpu_baseline  the float64 CPU oracle (dequant + matmul + combine) timed on
              this host on one decode step of the same workload
 Inputs are resident in device memory before timing starts.
@@ -174,8 +175,7 @@ class StepSlot:
         cfg, T, k = self.layer.cfg, self.T, self.layer.cfg.k
         if self.ffn:
             r = gnf4.route_logits(self.logits, k, out=self.r)
-            gnf4.grouped_gemm(self.layer.projs[0], self.X, 1, r, T, k, self.Y[0])
-            gnf4.swiglu(self.Y[0], cfg.inter, self.H)
+            gnf4.grouped_gemm_swiglu(self.layer.projs[0], self.X, 1, r, T, k, self.H)
             gnf4.grouped_gemm(self.layer.projs[1], self.H, 0, r, T, k, self.Y[1])
             gnf4.combine(self.Y[1], r["inv"], r["topk_w"], T, k, self.out)
             return
@@ -512,8 +512,8 @@ def main():
             T, dt, _, fl = out["ffn"]["prefill"]
             f["prefill"] = {"T": T, "step_ms": round(dt * 1e3, 4), "tflops": round(fl / dt / 1e12, 2),
                             "pct_mfma_peak": round(100 * fl / dt / 1e12 / BF16_PEAK_TFLOPS, 2)}
-        f["steps"] = ("route_logits (top-k + softmax + route), gate_up GEMM, SwiGLU (bf16 H), "
-                      "down GEMM on H, combine")
+        f["steps"] = ("route_logits (top-k + softmax + route), gate_up GEMM with the SwiGLU "
+                      "epilogue (bf16 H), down GEMM on H, combine")
         result["ffn_layer"] = f
     if not args.no_cpu and decode_ok:
         result["cpu_baseline"] = cpu_baseline(cfg, T_dec)

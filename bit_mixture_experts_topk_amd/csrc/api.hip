@@ -155,10 +155,14 @@ gnf4_status gnf4_swiglu(const float *Y, int32_t rows, int32_t I, uint16_t *H,
   return device_status(launch_swiglu(Y, rows, I, H, (hipStream_t)stream), "swiglu launch");
 }
 
-gnf4_status gnf4_grouped_gemm(const gnf4_weights *w, const uint16_t *X, int32_t gather,
-                              const int32_t *offsets, const int32_t *perm, const int32_t *active,
-                              const int32_t *n_active, int32_t T, int32_t k, float *Y,
-                              gnf4_stream_t stream) {
+}  // extern "C"
+
+// Shared by both GEMM entry points: validation, then the path chosen from
+// T*k (exactly one of Y / H is non-NULL).
+static gnf4_status grouped_gemm_any(const gnf4_weights *w, const uint16_t *X, int32_t gather,
+                                    const int32_t *offsets, const int32_t *perm,
+                                    const int32_t *active, const int32_t *n_active, int32_t T,
+                                    int32_t k, float *Y, uint16_t *H, gnf4_stream_t stream) {
   gnf4_status st = check_weights(w);
   if (st != GNF4_OK) return st;
   if (gather != 0 && gather != 1) return fail(GNF4_ERR_INVALID_ARG, "gather must be 0 or 1");
@@ -166,11 +170,13 @@ gnf4_status gnf4_grouped_gemm(const gnf4_weights *w, const uint16_t *X, int32_t 
   if (T < 0) return fail(GNF4_ERR_INVALID_ARG, "T = %d is negative", T);
   if ((int64_t)T * k >= ((int64_t)1 << 31) - 1024)
     return fail(GNF4_ERR_INVALID_ARG, "T*k too large");
+  if (H && w->N % 2)
+    return fail(GNF4_ERR_INVALID_ARG, "the SwiGLU epilogue needs an even N (gate and up halves)");
   if (T == 0) return ok();
-  if (!X || !offsets || !perm || !active || !n_active || !Y)
+  if (!X || !offsets || !perm || !active || !n_active || !(Y || H))
     return fail(GNF4_ERR_INVALID_ARG, "a pointer argument is NULL");
-  if (!aligned16(X) || !aligned16(Y))
-    return fail(GNF4_ERR_INVALID_ARG, "X and Y must be 16-byte aligned");
+  if (!aligned16(X) || (Y && !aligned16(Y)) || (H && ((uintptr_t)H & 1u)))
+    return fail(GNF4_ERR_INVALID_ARG, "X and Y must be 16-byte aligned, H 2-byte aligned");
   GemmArgs a;
   a.w = to_kernel(w);
   a.X = X;
@@ -182,6 +188,7 @@ gnf4_status gnf4_grouped_gemm(const gnf4_weights *w, const uint16_t *X, int32_t 
   a.T = T;
   a.k = k;
   a.Y = Y;
+  a.H = H;
   const int64_t rows = (int64_t)T * k;
   hipError_t e;
   if (rows <= kGemvMaxRows && w->K <= kGemvMaxK)
@@ -193,6 +200,24 @@ gnf4_status gnf4_grouped_gemm(const gnf4_weights *w, const uint16_t *X, int32_t 
   else
     return fail(GNF4_ERR_UNSUPPORTED, "MXFP4 with K %% 64 != 0 needs K <= %d", kGemvMaxK);
   return device_status(e, "grouped GEMM launch");
+}
+
+extern "C" {
+
+gnf4_status gnf4_grouped_gemm(const gnf4_weights *w, const uint16_t *X, int32_t gather,
+                              const int32_t *offsets, const int32_t *perm, const int32_t *active,
+                              const int32_t *n_active, int32_t T, int32_t k, float *Y,
+                              gnf4_stream_t stream) {
+  if (!Y && T > 0) return fail(GNF4_ERR_INVALID_ARG, "a pointer argument is NULL");
+  return grouped_gemm_any(w, X, gather, offsets, perm, active, n_active, T, k, Y, nullptr, stream);
+}
+
+gnf4_status gnf4_grouped_gemm_swiglu(const gnf4_weights *w, const uint16_t *X, int32_t gather,
+                                     const int32_t *offsets, const int32_t *perm,
+                                     const int32_t *active, const int32_t *n_active, int32_t T,
+                                     int32_t k, uint16_t *H, gnf4_stream_t stream) {
+  if (!H && T > 0) return fail(GNF4_ERR_INVALID_ARG, "a pointer argument is NULL");
+  return grouped_gemm_any(w, X, gather, offsets, perm, active, n_active, T, k, nullptr, H, stream);
 }
 
 gnf4_status gnf4_combine(const float *Y, const int32_t *inv, const float *topk_w, int32_t T,

@@ -53,8 +53,70 @@ struct GemmArgs {
   const int32_t *active;
   const int32_t *n_active;
   int32_t T, k;
-  float *Y;
+  float *Y;          // float32 output [T*k][N] (plain GEMM)
+  uint16_t *H;       // bf16 output [T*k][N/2] (SwiGLU epilogue; then Y is unused)
 };
+
+// SwiGLU (the activation between a mixture-of-experts layer's projections;
+// not described on the pages, the form of the public models the workloads
+// follow): bf16 of silu(g) * u, silu(x) = x / (1 + exp(-x)), rounded once
+// from the float64 value. Shared by gnf4_swiglu and the GEMM's epilogue so
+// that both round alike.
+// float64 -> bfloat16 bits, nearest with ties to even, straight from the
+// float64 significand (no float32 step, which could round twice). A finite
+// x = m53 * 2^(e - 52) with the 53-bit significand m53; bf16 keeps the
+// significand n = m53 / 2^s rounded, s = 45 + (E - e), where E = max(e, -126)
+// is the bf16 exponent (-126 for its subnormals). NaN gives 0x7FC0.
+__device__ __forceinline__ uint16_t f64_to_bf16_rne(double x) {
+  const uint64_t b = __builtin_bit_cast(uint64_t, x);
+  const uint32_t sign = (uint32_t)(b >> 48) & 0x8000u;
+  const int ex = (int)((b >> 52) & 0x7ff);
+  const uint64_t man = b & ((1ull << 52) - 1);
+  if (ex == 0x7ff) return man ? (uint16_t)0x7FC0 : (uint16_t)(sign | 0x7F80);
+  if (ex == 0) return (uint16_t)sign;           // zero or below 2^-1022: rounds to zero
+  const int e = ex - 1023;
+  int E = e > -126 ? e : -126;
+  const int sh = 45 + (E - e);
+  const uint64_t m53 = (1ull << 52) | man;
+  uint32_t n;
+  if (sh >= 64) {
+    n = 0;                                      // below a quarter of the smallest subnormal
+  } else {
+    n = (uint32_t)(m53 >> sh);
+    const uint64_t rem = m53 & ((1ull << sh) - 1), half = 1ull << (sh - 1);
+    if (rem > half || (rem == half && (n & 1u))) ++n;
+  }
+  if (n == 256) {
+    n = 128;
+    ++E;
+  }
+  if (E > 127) return (uint16_t)(sign | 0x7F80);
+  if (n < 128) return (uint16_t)(sign | n);     // subnormal (E = -126)
+  return (uint16_t)(sign | ((uint32_t)(E + 127) << 7) | (n - 128));
+}
+
+// bf16 of silu(g) * u as the float64 product rounds it. The float32
+// estimate (g * u) * rcp(1 + expf(-g)) carries a few float32 ulps of
+// relative error (expf and v_rcp_f32 within 1-2 ulps each, three roundings
+// of half an ulp), so it rounds to the same bf16 as the exact value unless
+// it lies within that error of a rounding midpoint; those values, and the
+// ranges where the estimate loses its relative accuracy (exp(-g) overflowing,
+// a gate or result near the float32 subnormal or overflow range, non-finite
+// values), are redone in float64. With |g| >= 2^-100, g > -80 and the result
+// between 2^-99 and 2^100 every intermediate is a normal float32, and the
+// error stays below 11 ulps of h; the margin is 16.
+__device__ __forceinline__ uint16_t swiglu_bf16(float g, float u) {
+  const float h = (g * u) * __builtin_amdgcn_rcpf(1.0f + expf(-g));
+  const uint32_t hb = __builtin_bit_cast(uint32_t, h);
+  const uint32_t ex = (hb >> 23) & 0xffu;
+  const uint32_t gex = (__builtin_bit_cast(uint32_t, g) >> 23) & 0xffu;
+  const int32_t mid = (int32_t)(hb & 0xffffu) - 0x8000;
+  const bool easy = g > -80.0f && gex > 26u && ex > 27u && ex < 227u && (mid > 16 || mid < -16);
+  if (easy) return (uint16_t)((hb + 0x7fffu + ((hb >> 16) & 1u)) >> 16);
+  const double x = (double)g;
+  return f64_to_bf16_rne(x / (1.0 + exp(-x)) * (double)u);
+}
+
 
 // NF4 byte -> two bf16 codebook values as one dword (element 2i, the high
 // nibble, in the low half): the operand layout of v_dot2 and of the MFMA

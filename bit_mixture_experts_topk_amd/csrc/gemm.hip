@@ -78,6 +78,7 @@ struct GemvGeom {
   int L_log2, L, RW, li, seg, wave, KCH, rows_per_item;
   int ustride;   // wave slots between a wave's consecutive row slots (4: the
                  // workgroup's waves interleave; 1: a wave owns its rows)
+  int half;      // SwiGLU epilogue: N / 2, the first up row (0 otherwise)
 };
 
 // Issue the code and scale loads of the rows of item block n0 of expert e:
@@ -87,7 +88,11 @@ struct GemvGeom {
 // results are discarded where they are used. Addresses are a uniform base of
 // the item plus a 32-bit per-lane offset (one expert's packed matrix is
 // below 4 GiB).
-template <int FMT, int U, int C>
+//
+// SwiGLU epilogue (GLU): n0 is the first output column of the item, and the
+// first U/2 slots take gate rows n0 + ..., the others the matching up rows
+// half + n0 + ..., so that one lane holds each (gate, up) pair.
+template <int FMT, int U, int C, bool GLU = false>
 __device__ __forceinline__ void gemv_load_rows(const GemmArgs &a, const GemvGeom &g, int e, int n0,
                                                GemvRows<U, C> &R) {
   const int N = a.w.N, K = a.w.K;
@@ -96,7 +101,15 @@ __device__ __forceinline__ void gemv_load_rows(const GemmArgs &a, const GemvGeom
   const uint8_t *cb = a.w.codes + row0 * (K / 2);
   uint32_t r[U], ch[C];
 #pragma unroll
-  for (int u = 0; u < U; ++u) r[u] = (uint32_t)min((u * g.ustride + g.wave) * g.RW + g.seg, rmax);
+  for (int u = 0; u < U; ++u) {
+    if constexpr (GLU) {
+      constexpr int UH = U / 2;
+      const int rel = min(((u % UH) * g.ustride + g.wave) * g.RW + g.seg, g.half - 1 - n0);
+      r[u] = (uint32_t)((u / UH) * g.half + rel);
+    } else {
+      r[u] = (uint32_t)min((u * g.ustride + g.wave) * g.RW + g.seg, rmax);
+    }
+  }
 #pragma unroll
   for (int c = 0; c < C; ++c) ch[c] = (uint32_t)min(g.li + c * g.L, g.KCH - 1);
   // The small scale loads go first and the code rows after them in row
@@ -222,6 +235,31 @@ __device__ __forceinline__ void gemv_store(const GemmArgs &a, const GemvGeom &g,
   }
 }
 
+// SwiGLU epilogue: H[row][col] = bf16(silu(gate) * up) for the item's
+// output columns col = n0 + ..., gate in slots u < U/2, up in u + U/2.
+template <int MT, int U>
+__device__ __forceinline__ void gemv_store_glu(const GemmArgs &a, const GemvGeom &g,
+                                               const float (&v)[U][MT], int n0, int p0, int tg,
+                                               int m) {
+  constexpr int UH = U / 2;
+#pragma unroll
+  for (int u = 0; u < UH; ++u) {
+    const int col = n0 + (u * g.ustride + g.wave) * g.RW + g.seg;
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+      if (g.li == 0 && col < g.half && tg + t < m)
+        a.H[(int64_t)(p0 + tg + t) * g.half + col] = swiglu_bf16(v[u][t], v[u + UH][t]);
+  }
+}
+
+template <bool GLU, int MT, int U>
+__device__ __forceinline__ void gemv_store_any(const GemmArgs &a, const GemvGeom &g,
+                                               const float (&v)[U][MT], int n0, int p0, int tg,
+                                               int m) {
+  if constexpr (GLU) gemv_store_glu<MT, U>(a, g, v, n0, p0, tg, m);
+  else gemv_store<MT, U>(a, g, v, n0, p0, tg, m);
+}
+
 // Token slice of activation row `src` (one token), chunks li + c*L (past
 // K/32: a valid neighbour, discarded by the product mask).
 template <int C>
@@ -250,9 +288,10 @@ __device__ __forceinline__ void gemv_load_x_row(const GemmArgs &a, const GemvGeo
 // token slices and then the weight rows are issued back to back on the second
 // memory round trip; the products of each row start as soon as that row
 // has arrived while later rows are still streaming.
-template <int FMT, int MT, int C, int U>
+template <int FMT, int MT, int C, int U, bool GLU>
 __global__ __launch_bounds__(kThreads, 2) void gemv_kernel(GemmArgs a, int L_log2,
                                                            int items_per_expert) {
+  static_assert(!GLU || U % 2 == 0, "the SwiGLU epilogue pairs slot u with u + U/2");
   constexpr bool kLut = FMT != GNF4_MXFP4;
   constexpr int kPer = (GNF4_MAX_EXPERTS + kThreads) / kThreads;   // offsets per thread
   constexpr int kSrcPer = kGemvSrcCache / kThreads;
@@ -270,8 +309,9 @@ __global__ __launch_bounds__(kThreads, 2) void gemv_kernel(GemmArgs a, int L_log
   g.seg = lane >> L_log2;
   g.wave = tid >> 6;
   g.ustride = 4;
+  g.half = GLU ? a.w.N / 2 : 0;
   g.KCH = a.w.K >> 5;
-  g.rows_per_item = 4 * g.RW * U;
+  g.rows_per_item = 4 * g.RW * (GLU ? U / 2 : U);
   const int E = a.w.E, rows = a.T * a.k;
   const int slot = (int)(blockIdx.x / (unsigned)items_per_expert);
   const int ib = (int)(blockIdx.x - (unsigned)slot * (unsigned)items_per_expert);
@@ -312,16 +352,16 @@ __global__ __launch_bounds__(kThreads, 2) void gemv_kernel(GemmArgs a, int L_log
   GemvRows<U, C> R;
   gemv_load_x<MT, C>(a, g, s_src, src_cached, p0, 0, m, x);
   __builtin_amdgcn_sched_barrier(0);
-  gemv_load_rows<FMT, U, C>(a, g, e, n0, R);
+  gemv_load_rows<FMT, U, C, GLU>(a, g, e, n0, R);
   __builtin_amdgcn_sched_barrier(0);
   float v[U][MT];
   gemv_dot<FMT, MT, U, C>(g, lut, lane4, R, x, v);
-  gemv_store<MT, U>(a, g, v, n0, p0, 0, m);
+  gemv_store_any<GLU, MT, U>(a, g, v, n0, p0, 0, m);
   // more routed rows than one token group (an expert routed several times)
   for (int tg = MT; tg < m; tg += MT) {
     gemv_load_x<MT, C>(a, g, s_src, src_cached, p0, tg, m, x);
     gemv_dot<FMT, MT, U, C>(g, lut, lane4, R, x, v);
-    gemv_store<MT, U>(a, g, v, n0, p0, tg, m);
+    gemv_store_any<GLU, MT, U>(a, g, v, n0, p0, tg, m);
   }
 }
 
@@ -332,9 +372,10 @@ __global__ __launch_bounds__(kThreads, 2) void gemv_kernel(GemmArgs a, int L_log
 // whenever every lower active expert has one routed row, which the offsets
 // confirm at the end (otherwise the rows are streamed again with the right
 // slices). Offsets arrive while the products are computed.
-template <int FMT, int C, int U>
+template <int FMT, int C, int U, bool GLU>
 __global__ __launch_bounds__(kThreads, 2) void gemv1_kernel(GemmArgs a, int L_log2,
                                                             int items_per_expert) {
+  static_assert(!GLU || U % 2 == 0, "the SwiGLU epilogue pairs slot u with u + U/2");
   constexpr bool kLut = FMT != GNF4_MXFP4;
   __shared__ uint32_t lut[kLut ? kLutWords : 1];
 
@@ -348,8 +389,9 @@ __global__ __launch_bounds__(kThreads, 2) void gemv1_kernel(GemmArgs a, int L_lo
   g.seg = lane >> L_log2;
   g.wave = tid >> 6;
   g.ustride = 4;
+  g.half = GLU ? a.w.N / 2 : 0;
   g.KCH = a.w.K >> 5;
-  g.rows_per_item = 4 * g.RW * U;
+  g.rows_per_item = 4 * g.RW * (GLU ? U / 2 : U);
   const int slot = (int)(blockIdx.x / (unsigned)items_per_expert);
   const int ib = (int)(blockIdx.x - (unsigned)slot * (unsigned)items_per_expert);
 
@@ -361,7 +403,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemv1_kernel(GemmArgs a, int L_lo
   const int n0 = ib * g.rows_per_item;
   GemvRows<U, C> R;
   __builtin_amdgcn_sched_barrier(0);
-  gemv_load_rows<FMT, U, C>(a, g, e, n0, R);
+  gemv_load_rows<FMT, U, C, GLU>(a, g, e, n0, R);
   __builtin_amdgcn_sched_barrier(0);
   const int p0 = a.offsets[e];
   const int p1 = a.offsets[e + 1];
@@ -371,15 +413,15 @@ __global__ __launch_bounds__(kThreads, 2) void gemv1_kernel(GemmArgs a, int L_lo
   const int m = p1 - p0;
   if (a.gather) {
     // every routed row of this expert is token 0: same products
-    for (int t = 0; t < m; ++t) gemv_store<1, U>(a, g, v, n0, p0 + t, 0, 1);
+    for (int t = 0; t < m; ++t) gemv_store_any<GLU, 1, U>(a, g, v, n0, p0 + t, 0, 1);
   } else if (m == 1 && p0 == slot) {
-    gemv_store<1, U>(a, g, v, n0, p0, 0, 1);
+    gemv_store_any<GLU, 1, U>(a, g, v, n0, p0, 0, 1);
   } else {
     for (int t = 0; t < m; ++t) {               // rows streamed again (rare: repeated experts)
       gemv_load_x_row<C>(a, g, p0 + t, x);
-      gemv_load_rows<FMT, U, C>(a, g, e, n0, R);
+      gemv_load_rows<FMT, U, C, GLU>(a, g, e, n0, R);
       gemv_dot<FMT, 1, U, C>(g, lut, lane4, R, x, v);
-      gemv_store<1, U>(a, g, v, n0, p0 + t, 0, 1);
+      gemv_store_any<GLU, 1, U>(a, g, v, n0, p0 + t, 0, 1);
     }
   }
 }
@@ -394,10 +436,11 @@ __global__ __launch_bounds__(kThreads, 2) void gemv1_kernel(GemmArgs a, int L_lo
 // range, read once: one token has at most 64 slots.
 constexpr int kGemvWaveThreads = 1024;
 
-template <int FMT, int C, int U>
+template <int FMT, int C, int U, bool GLU>
 __global__ __launch_bounds__(kGemvWaveThreads, 1) void gemv1w_kernel(GemmArgs a, int L_log2,
                                                                      int items_per_expert,
                                                                      int max_slots) {
+  static_assert(!GLU || U % 2 == 0, "the SwiGLU epilogue pairs slot u with u + U/2");
   constexpr bool kLut = FMT != GNF4_MXFP4;
   constexpr int kWaves = kGemvWaveThreads / 64;
   __shared__ uint32_t lut[kLut ? kLutWords : 1];
@@ -412,8 +455,9 @@ __global__ __launch_bounds__(kGemvWaveThreads, 1) void gemv1w_kernel(GemmArgs a,
   g.seg = lane >> L_log2;
   g.wave = 0;
   g.ustride = 1;
+  g.half = GLU ? a.w.N / 2 : 0;
   g.KCH = a.w.K >> 5;
-  g.rows_per_item = g.RW * U;
+  g.rows_per_item = g.RW * (GLU ? U / 2 : U);
   const int ipe = items_per_expert;
 
   const int nact = *a.n_active;
@@ -432,11 +476,11 @@ __global__ __launch_bounds__(kGemvWaveThreads, 1) void gemv1w_kernel(GemmArgs a,
   for (int it = (tid >> 6) * (int)gridDim.x + (int)blockIdx.x; it < total; it += W) {
     const int slot = it / ipe;
     const int n0 = (it - slot * ipe) * g.rows_per_item;
-    gemv_load_rows<FMT, U, C>(a, g, __builtin_amdgcn_readlane(ej, slot), n0, R);
+    gemv_load_rows<FMT, U, C, GLU>(a, g, __builtin_amdgcn_readlane(ej, slot), n0, R);
     gemv_dot<FMT, 1, U, C>(g, lut, lane4, R, x, v);
     const int p0 = __builtin_amdgcn_readlane(pj0, slot);
     const int m = __builtin_amdgcn_readlane(pj1, slot) - p0;
-    for (int t = 0; t < m; ++t) gemv_store<1, U>(a, g, v, n0, p0 + t, 0, 1);
+    for (int t = 0; t < m; ++t) gemv_store_any<GLU, 1, U>(a, g, v, n0, p0 + t, 0, 1);
   }
 }
 
@@ -520,11 +564,16 @@ __device__ __forceinline__ void find_tile(const GemmArgs &a, int bid, int n_tile
 // last block fall on the next column or past the buffer (zero) and are not
 // used. Activation tensors of 4 GiB or more (BIGX) are read with 64-bit
 // addresses instead; their rows and blocks are clamped in range either way.
+//
+// SwiGLU epilogue (GLU): a workgroup covers 128 output columns of H = N / 2;
+// wave w's column tiles 0, 1 are gate columns c = 32w + 16t + (0..15) and
+// tiles 2, 3 the up columns N/2 + c of the same c, so one lane holds each
+// (gate, up) pair when storing bf16(silu(gate) * up).
 __device__ __forceinline__ int k16_seg(int p, int j) { return 4 * (p & 1) + 2 * (p >> 1) + j; }
 
 constexpr int kBufferDword3 = 0x00020000;   // raw buffer, 32-bit data format
 
-template <int FMT, int RT, bool BIGX>
+template <int FMT, int RT, bool BIGX, bool GLU>
 __global__ __launch_bounds__(kThreads, 2) void mfma16_kernel(GemmArgs a, int n_tiles_n,
                                                              uint32_t x_bytes) {
   // NF4 and NF4_DQ decode through the table and scale each block's partial;
@@ -551,7 +600,9 @@ __global__ __launch_bounds__(kThreads, 2) void mfma16_kernel(GemmArgs a, int n_t
   const int count = a.offsets[e + 1] - seg_start;
   const int row0 = seg_start + mt * BM;
   const int rows_valid = min(BM, count - mt * BM);
-  const int nb = nt * BN + wave * 64;           // this wave's first column
+  const int nb = GLU ? nt * (BN / 2) + wave * 32  // this wave's first (output) column
+                     : nt * BN + wave * 64;
+  const int half = a.w.N / 2;
   const int p = lane >> 4, c16 = lane & 15;
   const uint32_t lane4 = (uint32_t)lane << 2;
   const int nkb = K / 64;
@@ -599,7 +650,8 @@ __global__ __launch_bounds__(kThreads, 2) void mfma16_kernel(GemmArgs a, int n_t
   int64_t fblk[4];
 #pragma unroll
   for (int ct = 0; ct < 4; ++ct) {
-    const uint32_t col = (uint32_t)min(nb + ct * 16 + c16, N - 1);
+    const uint32_t col = GLU ? (uint32_t)((ct >> 1) * half + min(nb + (ct & 1) * 16 + c16, half - 1))
+                             : (uint32_t)min(nb + ct * 16 + c16, N - 1);
     coff[ct] = col * (uint32_t)(K / 2) + 16u * (uint32_t)p;
     soff[ct] = kDQ ? col * scale_row + 2u * (uint32_t)p
                : kWin ? col * scale_row + 8u * (uint32_t)p : col * scale_row + (uint32_t)(p & 1);
@@ -807,18 +859,34 @@ __global__ __launch_bounds__(kThreads, 2) void mfma16_kernel(GemmArgs a, int n_t
 #undef GNF4_LOAD_STAGE
 
   // ---- store: register r of a 16x16 tile holds row 4 p + r, column c16
+  if constexpr (GLU) {
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt)
+    for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-    for (int ct = 0; ct < 4; ++ct) {
-      const int col = nb + ct * 16 + c16;
-      if (col >= N) continue;
+      for (int ct = 0; ct < 2; ++ct) {
+        const int col = nb + ct * 16 + c16;
+        if (col >= half) continue;
 #pragma unroll
-      for (int r2 = 0; r2 < 4; ++r2) {
-        const int r = rt * 16 + 4 * p + r2;
-        if (r < rows_valid) a.Y[(int64_t)(row0 + r) * N + col] = acc[rt][ct][r2];
+        for (int r2 = 0; r2 < 4; ++r2) {
+          const int r = rt * 16 + 4 * p + r2;
+          if (r < rows_valid)
+            a.H[(int64_t)(row0 + r) * half + col] = swiglu_bf16(acc[rt][ct][r2], acc[rt][ct + 2][r2]);
+        }
       }
-    }
+  } else {
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) {
+        const int col = nb + ct * 16 + c16;
+        if (col >= N) continue;
+#pragma unroll
+        for (int r2 = 0; r2 < 4; ++r2) {
+          const int r = rt * 16 + 4 * p + r2;
+          if (r < rows_valid) a.Y[(int64_t)(row0 + r) * N + col] = acc[rt][ct][r2];
+        }
+      }
+  }
 }
 
 // ============================================================ host launch
@@ -831,8 +899,8 @@ struct GemvVariant {
 };
 static const GemvVariant kGemvVariants[] = {
     {1, 1, 3, {4, 8, 16}}, {1, 2, 2, {4, 8, 0}}, {1, 3, 2, {2, 4, 0}}, {1, 4, 1, {2, 0, 0}},
-    {2, 1, 2, {2, 4, 0}},  {2, 2, 1, {2, 0, 0}}, {2, 3, 1, {1, 0, 0}},
-    {4, 1, 1, {2, 0, 0}},  {4, 2, 1, {1, 0, 0}}, {8, 1, 1, {2, 0, 0}},
+    {2, 1, 2, {2, 4, 0}},  {2, 2, 1, {2, 0, 0}}, {2, 3, 2, {1, 2, 0}},
+    {4, 1, 1, {2, 0, 0}},  {4, 2, 2, {1, 2, 0}}, {8, 1, 1, {2, 0, 0}},
 };
 
 // NF4_DQ rebuilds each absmax from two loads and needs more registers: its
@@ -845,41 +913,44 @@ static const GemvVariant *gemv_variant(int MT, int C) {
   return nullptr;
 }
 
+// Output columns of a call: N, or N / 2 with the SwiGLU epilogue.
+static int out_cols(const GemmArgs &a) { return a.H ? a.w.N / 2 : a.w.N; }
+
 // One token, gathered input: the persistent kernel, one workgroup per CU (or
 // as many as are resident at once).
-template <int FMT, int C, int U>
+template <int FMT, int C, int U, bool GLU>
 static hipError_t gemv1w_go(const GemmArgs &a, int L_log2, int max_slots, hipStream_t s) {
   static int per_cu = 0;
   if (per_cu == 0) {
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gemv1w_kernel<FMT, C, U>,
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gemv1w_kernel<FMT, C, U, GLU>,
                                                      kGemvWaveThreads, 0) != hipSuccess || n < 1)
       n = 1;
     per_cu = n;
   }
-  const int rows_per_item = (64 >> L_log2) * U;
-  const int items = (a.w.N + rows_per_item - 1) / rows_per_item;
+  const int rows_per_item = (64 >> L_log2) * (GLU ? U / 2 : U);
+  const int items = (out_cols(a) + rows_per_item - 1) / rows_per_item;
   const int64_t waves = (int64_t)max_slots * items;
   const int64_t grid = std::min<int64_t>((int64_t)per_cu * device_cu_count(),
                                          (waves + kGemvWaveThreads / 64 - 1) / (kGemvWaveThreads / 64));
-  hipLaunchKernelGGL((gemv1w_kernel<FMT, C, U>), dim3((unsigned)grid),
+  hipLaunchKernelGGL((gemv1w_kernel<FMT, C, U, GLU>), dim3((unsigned)grid),
                      dim3(kGemvWaveThreads), 0, s, a, L_log2, items, max_slots);
   return hipGetLastError();
 }
 
-template <int FMT, int MT, int C, int U>
+template <int FMT, int MT, int C, int U, bool GLU>
 static hipError_t gemv_go(const GemmArgs &a, int L_log2, int max_slots, hipStream_t s) {
   const int L = 1 << L_log2;
-  const int rows_per_item = 4 * (64 / L) * U;
-  const int items = (a.w.N + rows_per_item - 1) / rows_per_item;
+  const int rows_per_item = 4 * (64 / L) * (GLU ? U / 2 : U);
+  const int items = (out_cols(a) + rows_per_item - 1) / rows_per_item;
   const int64_t grid = (int64_t)max_slots * items;
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
   if constexpr (MT == 1) {
     // one token in routed order (a gathered one takes gemv1w_kernel)
     if (a.T == 1) {
-      hipLaunchKernelGGL((gemv1_kernel<FMT, C, U>), dim3((unsigned)grid), dim3(kThreads), 0, s, a,
-                         L_log2, items);
+      hipLaunchKernelGGL((gemv1_kernel<FMT, C, U, GLU>), dim3((unsigned)grid), dim3(kThreads), 0,
+                         s, a, L_log2, items);
       return hipGetLastError();
     }
   }
@@ -888,15 +959,20 @@ static hipError_t gemv_go(const GemmArgs &a, int L_log2, int max_slots, hipStrea
   if constexpr (MT == 1 && C < 4) {
     return hipErrorInvalidValue;
   } else {
-    hipLaunchKernelGGL((gemv_kernel<FMT, MT, C, U>), dim3((unsigned)grid), dim3(kThreads), 0, s, a,
-                       L_log2, items);
+    hipLaunchKernelGGL((gemv_kernel<FMT, MT, C, U, GLU>), dim3((unsigned)grid), dim3(kThreads), 0,
+                       s, a, L_log2, items);
     return hipGetLastError();
   }
 }
 
-#define GNF4_GEMV_CASE(mt, c, u)                                                 \
-  if constexpr (FMT != GNF4_NF4_DQ || c * u <= 8)                                \
-    if (MT == mt && C == c && U == u) return gemv_go<FMT, mt, c, u>(a, L_log2, max_slots, s);
+// The SwiGLU epilogue pairs slot u with u + U/2, so it takes even U only.
+#define GNF4_GEMV_CASE(mt, c, u)                                                       \
+  if constexpr (FMT != GNF4_NF4_DQ || c * u <= 8)                                      \
+    if (MT == mt && C == c && U == u) {                                                \
+      if (!a.H) return gemv_go<FMT, mt, c, u, false>(a, L_log2, max_slots, s);         \
+      if constexpr (u % 2 == 0) return gemv_go<FMT, mt, c, u, true>(a, L_log2, max_slots, s); \
+      return hipErrorInvalidValue;                                                     \
+    }
 
 template <int FMT>
 static hipError_t gemv_dispatch(const GemmArgs &a, int MT, int C, int U, int L_log2, int max_slots,
@@ -905,7 +981,8 @@ static hipError_t gemv_dispatch(const GemmArgs &a, int MT, int C, int U, int L_l
   GNF4_GEMV_CASE(1, 2, 4) GNF4_GEMV_CASE(1, 2, 8) GNF4_GEMV_CASE(1, 3, 2) GNF4_GEMV_CASE(1, 3, 4)
   GNF4_GEMV_CASE(1, 4, 2)
   GNF4_GEMV_CASE(2, 1, 2) GNF4_GEMV_CASE(2, 1, 4) GNF4_GEMV_CASE(2, 2, 2) GNF4_GEMV_CASE(2, 3, 1)
-  GNF4_GEMV_CASE(4, 1, 2) GNF4_GEMV_CASE(4, 2, 1) GNF4_GEMV_CASE(8, 1, 2)
+  GNF4_GEMV_CASE(2, 3, 2)
+  GNF4_GEMV_CASE(4, 1, 2) GNF4_GEMV_CASE(4, 2, 1) GNF4_GEMV_CASE(4, 2, 2) GNF4_GEMV_CASE(8, 1, 2)
   return hipErrorInvalidValue;
 }
 #undef GNF4_GEMV_CASE
@@ -946,16 +1023,19 @@ bool gemv_shape(int K, int MT, int *L_log2, int *C) {
 int gemv_tokens(int T) { return T >= 5 ? 8 : (T >= 3 ? 4 : (T >= 2 ? 2 : 1)); }
 
 // Rows per wave slot: the smallest compiled U (that fits the format's
-// registers) whose grid fits the resident workgroups (two per CU), else the
-// largest that fits; 0 if none does.
-static int gemv_pick_u(const GemvVariant &v, int fmt, int N, int L_log2, int max_slots) {
+// registers, and is even for the SwiGLU epilogue) whose grid fits the
+// resident workgroups (two per CU), else the largest that fits; 0 if none
+// does. cols: output columns (N, or N / 2 with the epilogue).
+static int gemv_pick_u(const GemvVariant &v, int fmt, int cols, int L_log2, int max_slots,
+                       bool glu) {
   const int64_t target = 2LL * device_cu_count();
   int last = 0;
   for (int i = 0; i < v.nu; ++i) {
     if (!gemv_fits(fmt, v.C, v.U[i])) break;
+    if (glu && v.U[i] % 2) continue;
     last = v.U[i];
-    const int per = 4 * (64 >> L_log2) * v.U[i];
-    const int64_t items = (int64_t)max_slots * ((N + per - 1) / per);
+    const int per = 4 * (64 >> L_log2) * (glu ? v.U[i] / 2 : v.U[i]);
+    const int64_t items = (int64_t)max_slots * ((cols + per - 1) / per);
     if (items <= target) return v.U[i];
   }
   return last;
@@ -963,16 +1043,17 @@ static int gemv_pick_u(const GemvVariant &v, int fmt, int N, int L_log2, int max
 
 // Rows per wave slot of the one-token gathered kernel for C chunks per lane
 // (measured fastest on the workload shapes, and free of register spills).
-template <int FMT>
+// The SwiGLU epilogue needs an even U (slot u pairs with u + U/2).
+template <int FMT, bool GLU>
 static hipError_t gemv1w_dispatch(const GemmArgs &a, int C, int L_log2, int max_slots,
                                   hipStream_t s) {
   switch (C) {
-    case 1: return gemv1w_go<FMT, 1, 4>(a, L_log2, max_slots, s);
-    case 2: return gemv1w_go<FMT, 2, 4>(a, L_log2, max_slots, s);
-    case 3: return gemv1w_go<FMT, 3, 2>(a, L_log2, max_slots, s);
+    case 1: return gemv1w_go<FMT, 1, 4, GLU>(a, L_log2, max_slots, s);
+    case 2: return gemv1w_go<FMT, 2, 4, GLU>(a, L_log2, max_slots, s);
+    case 3: return gemv1w_go<FMT, 3, 2, GLU>(a, L_log2, max_slots, s);
     case 4:
-      if constexpr (FMT != GNF4_MXFP4) return gemv1w_go<FMT, 4, 1>(a, L_log2, max_slots, s);
-      else return gemv1w_go<FMT, 4, 2>(a, L_log2, max_slots, s);
+      if constexpr (FMT != GNF4_MXFP4 && !GLU) return gemv1w_go<FMT, 4, 1, GLU>(a, L_log2, max_slots, s);
+      else return gemv1w_go<FMT, 4, 2, GLU>(a, L_log2, max_slots, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -982,10 +1063,17 @@ hipError_t launch_gemv(const GemmArgs &a, hipStream_t s) {
     int L_log2 = 6, C = 1;
     if (!gemv_shape(a.w.K, 1, &L_log2, &C)) return hipErrorInvalidValue;
     const int max_slots = std::min<int>(a.w.E, a.k);
+    const bool glu = a.H != nullptr;
     switch (a.w.format) {
-      case GNF4_NF4: return gemv1w_dispatch<GNF4_NF4>(a, C, L_log2, max_slots, s);
-      case GNF4_NF4_DQ: return gemv1w_dispatch<GNF4_NF4_DQ>(a, C, L_log2, max_slots, s);
-      default: return gemv1w_dispatch<GNF4_MXFP4>(a, C, L_log2, max_slots, s);
+      case GNF4_NF4:
+        return glu ? gemv1w_dispatch<GNF4_NF4, true>(a, C, L_log2, max_slots, s)
+                   : gemv1w_dispatch<GNF4_NF4, false>(a, C, L_log2, max_slots, s);
+      case GNF4_NF4_DQ:
+        return glu ? gemv1w_dispatch<GNF4_NF4_DQ, true>(a, C, L_log2, max_slots, s)
+                   : gemv1w_dispatch<GNF4_NF4_DQ, false>(a, C, L_log2, max_slots, s);
+      default:
+        return glu ? gemv1w_dispatch<GNF4_MXFP4, true>(a, C, L_log2, max_slots, s)
+                   : gemv1w_dispatch<GNF4_MXFP4, false>(a, C, L_log2, max_slots, s);
     }
   }
   int MT = gemv_tokens(a.T);
@@ -997,7 +1085,7 @@ hipError_t launch_gemv(const GemmArgs &a, hipStream_t s) {
   const GemvVariant *v = gemv_variant(MT, C);
   if (!v) return hipErrorInvalidValue;
   const int max_slots = std::min<int>(a.w.E, a.T * a.k);
-  const int U = gemv_pick_u(*v, a.w.format, a.w.N, L_log2, max_slots);
+  const int U = gemv_pick_u(*v, a.w.format, out_cols(a), L_log2, max_slots, a.H != nullptr);
   if (U == 0) return hipErrorInvalidValue;
   switch (a.w.format) {
     case GNF4_NF4: return gemv_dispatch<GNF4_NF4>(a, MT, C, U, L_log2, max_slots, s);
@@ -1011,16 +1099,16 @@ static int64_t x_bytes(const GemmArgs &a) {
   return (a.gather ? (int64_t)a.T : (int64_t)a.T * a.k) * a.w.K * 2;
 }
 
-template <int FMT, int RT, bool BIGX>
+template <int FMT, int RT, bool BIGX, bool GLU>
 static hipError_t mfma16_go(const GemmArgs &a, hipStream_t s) {
-  constexpr int BM = 16 * RT, BN = 256;
+  constexpr int BM = 16 * RT, BN = GLU ? 128 : 256;    // output columns per tile
   const int rows = a.T * a.k;
-  const int n_tiles_n = (a.w.N + BN - 1) / BN;
+  const int n_tiles_n = (out_cols(a) + BN - 1) / BN;
   const int64_t m_tiles = (rows + BM - 1) / BM + std::min<int>(a.w.E, rows);
   int64_t grid = m_tiles * n_tiles_n;
   grid = (grid + 7) / 8 * 8;
   if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL((mfma16_kernel<FMT, RT, BIGX>), dim3((unsigned)grid), dim3(kThreads), 0, s,
+  hipLaunchKernelGGL((mfma16_kernel<FMT, RT, BIGX, GLU>), dim3((unsigned)grid), dim3(kThreads), 0, s,
                      a, n_tiles_n, BIGX ? 0u : (uint32_t)x_bytes(a));
   return hipGetLastError();
 }
@@ -1028,8 +1116,9 @@ static hipError_t mfma16_go(const GemmArgs &a, hipStream_t s) {
 template <int FMT>
 static hipError_t mfma_pick(const GemmArgs &a, hipStream_t s) {
   // 32-bit buffer offsets reach activation tensors below 4 GiB
-  if (x_bytes(a) < ((int64_t)1 << 32)) return mfma16_go<FMT, 4, false>(a, s);
-  return mfma16_go<FMT, 4, true>(a, s);
+  const bool big = x_bytes(a) >= ((int64_t)1 << 32);
+  if (a.H) return big ? mfma16_go<FMT, 4, true, true>(a, s) : mfma16_go<FMT, 4, false, true>(a, s);
+  return big ? mfma16_go<FMT, 4, true, false>(a, s) : mfma16_go<FMT, 4, false, false>(a, s);
 }
 
 hipError_t launch_mfma(const GemmArgs &a, hipStream_t s) {

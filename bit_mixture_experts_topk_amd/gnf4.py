@@ -24,7 +24,8 @@ FORMATS = {"nf4": NF4, "nf4_dq": NF4_DQ, "mxfp4": MXFP4}
 STATUS = {0: "OK", 1: "INVALID_ARG", 2: "UNSUPPORTED", 4: "DEVICE"}
 
 # Every entry point declared in include/gnf4.h.
-EXPORTS = ("gnf4_route", "gnf4_route_logits", "gnf4_grouped_gemm", "gnf4_swiglu", "gnf4_combine",
+EXPORTS = ("gnf4_route", "gnf4_route_logits", "gnf4_grouped_gemm", "gnf4_grouped_gemm_swiglu",
+           "gnf4_swiglu", "gnf4_combine",
            "gnf4_dequant", "gnf4_quantize", "gnf4_nf4_codebook", "gnf4_last_error",
            "gnf4_build_id")
 
@@ -56,6 +57,7 @@ def lib():
         L.gnf4_route_logits.argtypes = [P, I, I, I, P, P, P, P, P, P, P, P, P, S]
         L.gnf4_swiglu.argtypes = [P, I, I, P, S]
         L.gnf4_grouped_gemm.argtypes = [ctypes.POINTER(CWeights), P, I, P, P, P, P, I, I, P, S]
+        L.gnf4_grouped_gemm_swiglu.argtypes = [ctypes.POINTER(CWeights), P, I, P, P, P, P, I, I, P, S]
         L.gnf4_combine.argtypes = [P, P, P, I, I, I, P, S]
         L.gnf4_dequant.argtypes = [ctypes.POINTER(CWeights), I, P, S]
         L.gnf4_quantize.argtypes = [I, P, I, I, P, P, P, S]
@@ -229,6 +231,19 @@ def grouped_gemm(w, X, gather, r, T, k, Y=None):
                                    _ptr(r["perm"]), _ptr(r["active"]), _ptr(r["n_active"]),
                                    T, k, _ptr(Y), _stream()), "gnf4_grouped_gemm")
     return Y
+
+
+def grouped_gemm_swiglu(w, X, gather, r, T, k, H=None):
+    """H [T*k, N/2] bf16 bits (int16) = SwiGLU of the grouped GEMM, fused."""
+    if not (X.is_cuda and X.is_contiguous() and X.element_size() == 2):
+        raise ValueError("X must be a contiguous bf16 (or 16-bit bit pattern) CUDA tensor")
+    if H is None:
+        H = torch.empty((max(T * k, 1), w.N // 2), dtype=torch.int16, device=X.device)
+    cw = w.cstruct()
+    _check(lib().gnf4_grouped_gemm_swiglu(ctypes.byref(cw), _ptr(X), gather, _ptr(r["offsets"]),
+                                          _ptr(r["perm"]), _ptr(r["active"]), _ptr(r["n_active"]),
+                                          T, k, _ptr(H), _stream()), "gnf4_grouped_gemm_swiglu")
+    return H
 
 
 def combine(Y, inv, topk_w, T, k, out=None):

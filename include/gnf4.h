@@ -15,8 +15,9 @@
  *   gnf4_combine        out[t] = sum_j w[t,j] * Y[inv[t*k+j]]
  * and a whole FFN layer adds the steps either side of the GEMM:
  *   gnf4_route_logits   router logits -> top-k ids and weights, then route
- *   gnf4_grouped_gemm   gate_up projection (gathered token rows)
- *   gnf4_swiglu         H = silu(gate) * up, bf16, in routed order
+ *   gnf4_grouped_gemm_swiglu   gate_up projection (gathered token rows)
+ *                       with H = silu(gate) * up, bf16, as its epilogue
+ *                       (or gnf4_grouped_gemm, then gnf4_swiglu)
  *   gnf4_grouped_gemm   down projection (rows of H, routed order)
  *   gnf4_combine
  *
@@ -124,6 +125,22 @@ gnf4_status gnf4_grouped_gemm(const gnf4_weights *w, const uint16_t *X, int32_t 
                               const int32_t *offsets, const int32_t *perm,
                               const int32_t *active, const int32_t *n_active,
                               int32_t T, int32_t k, float *Y, gnf4_stream_t stream);
+
+/* gnf4_grouped_gemm_swiglu -- the first projection with the SwiGLU step as
+ * its epilogue: for every routed row p and i < N/2,
+ *   H[p][i] = bf16(silu(Y[p][i]) * Y[p][N/2 + i])
+ * where Y is what gnf4_grouped_gemm computes for the same arguments (same
+ * kernels, same float32 values) and the rounding is gnf4_swiglu's, so the
+ * result equals gnf4_grouped_gemm followed by gnf4_swiglu bit for bit,
+ * without writing or reading the float32 Y. The weight's rows [0, N/2) are
+ * the gate, [N/2, N) the up projection; N must be even. H uint16 bf16 bits
+ * [T*k][N/2] (2-byte aligned), the down projection's input in routed order.
+ * Other arguments, limits and errors as gnf4_grouped_gemm. Not described on
+ * the pages (reading of gnf4_swiglu). */
+gnf4_status gnf4_grouped_gemm_swiglu(const gnf4_weights *w, const uint16_t *X, int32_t gather,
+                                     const int32_t *offsets, const int32_t *perm,
+                                     const int32_t *active, const int32_t *n_active,
+                                     int32_t T, int32_t k, uint16_t *H, gnf4_stream_t stream);
 
 /* gnf4_combine -- weighted top-k combine back to tokens.
  *   out[t][n] = sum_{j=0..k-1} topk_w[t][j] * Y[inv[t*k+j]][n]

@@ -123,6 +123,18 @@ def test_route_logits_rejects(L):
     assert call(a7=None) == INVALID                                        # offsets
 
 
+def test_fused_gemm_rejects(L):
+    w = weights()
+    p = 0x1000
+    assert L.gnf4_grouped_gemm_swiglu(ctypes.byref(w), p, 1, p, p, p, p, 2, 2, None, None) == INVALID
+    assert L.gnf4_grouped_gemm_swiglu(ctypes.byref(w), p, 1, p, p, p, p, 2, 2, 0x1001, None) == INVALID
+    assert "2-byte aligned" in gnf4.last_error()
+    assert L.gnf4_grouped_gemm_swiglu(ctypes.byref(w), p, 2, p, p, p, p, 2, 2, p, None) == INVALID
+    odd = weights(N=9)
+    assert L.gnf4_grouped_gemm_swiglu(ctypes.byref(odd), p, 1, p, p, p, p, 2, 2, p, None) == INVALID
+    assert "even N" in gnf4.last_error()
+
+
 def test_swiglu_rejects(L):
     p = 0x1000
     assert L.gnf4_swiglu(p, 4, 6, p, None) == INVALID and "I = 6" in gnf4.last_error()

@@ -104,27 +104,63 @@ def ffn_oracle(fmt, packs, X, logits, k, d, I):
     return ocombine.combine(Y2, r["inv"], w, T, k), H
 
 
+@pytest.mark.parametrize("fused", [False, True])
 @pytest.mark.parametrize("fmt", ["nf4", "nf4_dq", "mxfp4"])
 @pytest.mark.parametrize("T", [1, 5, 300])                 # GEMV (T*k <= 64) and MFMA paths
-def test_ffn_layer_end_to_end(fmt, T):
+def test_ffn_layer_end_to_end(fmt, T, fused):
     gl = gnf4()
     E, d, I, k = 8, 256, 128, 2
     W1, W2, X, logits = layer_case(E, d, I, T, k, 2)
     packs = [oracle_pack(fmt, W1), oracle_pack(fmt, W2)]
-    say("ffn layer", fmt, "T", T, "E", E, "d", d, "I", I, "k", k)
+    say("ffn layer", fmt, "T", T, "E", E, "d", d, "I", I, "k", k, "fused", fused)
     pw1 = packed_to_device(gl, fmt, *packs[0], E, 2 * I, d)
     pw2 = packed_to_device(gl, fmt, *packs[1], E, d, I)
     r = gl.route_logits(torch.from_numpy(logits).cuda(), k)
-    Y1 = gl.grouped_gemm(pw1, bits_to_device(X), 1, r, T, k)
-    H = gl.swiglu(Y1, I)
+    if fused:
+        H = gl.grouped_gemm_swiglu(pw1, bits_to_device(X), 1, r, T, k)
+    else:
+        Y1 = gl.grouped_gemm(pw1, bits_to_device(X), 1, r, T, k)
+        H = gl.swiglu(Y1, I)
     Y2 = gl.grouped_gemm(pw2, H, 0, r, T, k)
     out = gl.combine(Y2, r["inv"], r["topk_w"], T, k)
     torch.cuda.synchronize()
     ref, H_ref = ffn_oracle(fmt, packs, X, logits, k, d, I)
-    max_rel, frob = assert_within_layer(out.cpu().numpy()[:T], ref, "ffn layer %s T=%d" % (fmt, T))
+    max_rel, frob = assert_within_layer(out.cpu().numpy()[:T], ref, "ffn layer %s T=%d fused=%d" % (fmt, T, fused))
     print("ffn layer %s T=%d: max|err|/rms %.2e, rel Frobenius %.2e" % (fmt, T, max_rel, frob))
     # H itself: the GPU rounds its own float32 gate_up output, so a value
     # near a bf16 rounding boundary may land one bf16 step away
     fg = (H.cpu().numpy().view(np.uint16)[:T * k].astype(np.uint32) << 16).view(np.float32)
     fr = (H_ref.astype(np.uint32) << 16).view(np.float32)
     assert np.max(np.abs(fg - fr)) <= 2.0 ** -6 * np.max(np.abs(fr))
+
+
+@pytest.mark.parametrize("fmt", ["nf4", "nf4_dq", "mxfp4"])
+@pytest.mark.parametrize("E,I,K,T,k,gather,distinct", [
+    (6, 100, 256, 1, 4, 1, True),       # one token, gathered: persistent GEMV; ragged I
+    (6, 100, 256, 1, 4, 0, True),       # one token, routed order
+    (6, 100, 256, 1, 6, 0, False),      # routed order with repeated experts
+    (5, 72, 2880, 3, 4, 1, True),       # a few tokens: multi-token GEMV, K = 2880
+    (8, 300, 512, 40, 2, 1, True),      # MFMA: ragged M and H-column tails
+    (4, 64, 1024, 200, 2, 0, True),     # MFMA, routed-order input
+])
+def test_fused_swiglu_equals_gemm_then_swiglu(fmt, E, I, K, T, k, gather, distinct):
+    """The epilogue computes the same float32 products as the plain GEMM and
+    rounds them as gnf4_swiglu does: bit-identical H, on every path."""
+    gl = gnf4()
+    if fmt == "mxfp4" and K % 64:
+        K = 2944                              # the MFMA path needs K % 64 == 0
+    case = synth.small_layer(E, 2 * I, K, T, k, seed=4, distinct=distinct, gather=gather)
+    codes, scales, scales2 = oracle_pack(fmt, case["W"])
+    pw = packed_to_device(gl, fmt, codes, scales, scales2, E, 2 * I, K)
+    say("fused swiglu", fmt, E, I, K, T, k, gather, distinct)
+    r = gl.route(torch.from_numpy(case["ids"]).cuda(), E)
+    Xd = bits_to_device(case["X"])
+    Y = gl.grouped_gemm(pw, Xd, gather, r, T, k)
+    H_ref = gl.swiglu(Y, I)
+    H = gl.grouped_gemm_swiglu(pw, Xd, gather, r, T, k)
+    torch.cuda.synchronize()
+    nv = int(r["offsets"][-1].item())
+    assert nv > 0
+    a = H.cpu().numpy()[:nv]
+    b = H_ref.cpu().numpy()[:nv]
+    assert np.array_equal(a, b), int((a != b).sum())
