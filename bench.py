@@ -18,6 +18,9 @@ Reported (one JSON line on stdout):
              launch / its mean duration from HIP events on the launch stream
   prefill    TFLOP/s of the prefill step and the roofline of its gate_up
              MFMA kernel (algorithmic flops 2*rows*N*K per launch)
+  dequant_path  the same step through the dequantize-then-matmul path the
+             pages compare against (bf16 decode of the routed experts to HBM,
+             then library GEMMs), and the fused path's speed-up over it
   ffn_layer  the whole FFN layer step (router top-k from logits, gate_up with
              the SwiGLU epilogue, down on its bf16 output, combine) at the
              same T's
@@ -50,6 +53,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="olmoe")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-dequant-path", action="store_true",
+                    help="skip the dequantize-then-matmul comparison leg")
     ap.add_argument("--only", choices=["decode", "prefill"], default=None)
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
@@ -204,6 +209,55 @@ class StepSlot:
 
     def flops(self):
         return sum(2.0 * self.T * self.layer.cfg.k * pw.N * pw.K for pw in self.layer.projs)
+
+
+class DequantSlot(StepSlot):
+    """The same step (route, both projections on the same inputs, combine)
+    through the dequantize-then-matmul path the pages compare against: the
+    routed experts of each projection are decoded to bf16 in HBM
+    (gnf4_dequant_experts_bf16), then multiplied with torch's library GEMMs
+    (hipBLASLt / rocBLAS): one batched product at T = 1, one 2-D product per
+    active expert otherwise (torch has no grouped GEMM)."""
+
+    def __init__(self, torch, gnf4, cfg, layer, T, seed, wbuf):
+        super().__init__(torch, gnf4, cfg, layer, T, seed)
+        k = cfg.k
+        ids = self.ids.cpu().numpy()
+        self.wbuf = wbuf                       # bf16 decode buffers, one per projection
+        self.counts = np.bincount(ids.reshape(-1), minlength=cfg.E)
+        self.segs = []                          # (slot, first routed row, rows)
+        off = 0
+        for e in range(cfg.E):
+            c = int(self.counts[e])
+            if c:
+                self.segs.append((len(self.segs), off, c))
+            off += c
+        self.max_slots = min(cfg.E, T * k)
+        perm = np.argsort(ids.reshape(-1), kind="stable")
+        self.src = torch.from_numpy((perm // k).astype(np.int64)).cuda()
+        self.Yb = [torch.empty((T * k, p.N), dtype=torch.bfloat16, device="cuda") for p in cfg.projs]
+
+    def run(self, gnf4):
+        import torch
+        cfg, T, k = self.layer.cfg, self.T, self.layer.cfg.k
+        r = gnf4.route(self.ids, cfg.E, out=self.r)
+        ins = [self.X, self.Xd if len(cfg.projs) > 1 else None]
+        for pi, pw in enumerate(self.layer.projs):
+            W = gnf4.dequant_experts_bf16(pw, r["active"], r["n_active"], self.max_slots,
+                                          self.wbuf[pi]).view(torch.bfloat16)
+            Xb = ins[pi].view(torch.bfloat16)
+            if T == 1:
+                # slot s holds routed row s (distinct ids); a gathered input is the token row
+                xs = Xb.expand(self.max_slots, -1) if pi == 0 else Xb
+                torch.bmm(W[:self.max_slots], xs.contiguous().unsqueeze(2),
+                          out=self.Yb[pi].view(self.max_slots, pw.N, 1))
+            else:
+                A = Xb.index_select(0, self.src) if pi == 0 else Xb
+                for slot, p0, c in self.segs:
+                    torch.mm(A[p0:p0 + c], W[slot].t(), out=self.Yb[pi][p0:p0 + c])
+        last = len(cfg.projs) - 1
+        self.Y[last].copy_(self.Yb[last])
+        gnf4.combine(self.Y[last], r["inv"], self.tw, T, k, self.out)
 
 
 def capture_chain(torch, gnf4, slots):
@@ -453,6 +507,31 @@ def main():
             torch.cuda.empty_cache()
         out["ffn"] = ffn
 
+    if args.only is None and not args.no_dequant_path:
+        # the dequantize-then-matmul comparison path, same steps and inputs
+        dq = {}
+        for T, tag in ((T_dec, "decode"), (T_pre, "prefill")):
+            if not ((tag == "decode" and decode_ok) or (tag == "prefill" and prefill_ok)):
+                continue
+            step_bytes = layer_bytes * min(1.0, T * cfg.k / cfg.E)
+            copies = int(min(32 if tag == "decode" else 4,
+                             max(2, np.ceil(3 * MALL_BYTES / max(step_bytes, 1)))))
+            layers = [base] + [base.clone(torch) for _ in range(copies - 1)]
+            ms = min(cfg.E, T * cfg.k)
+            wbuf = [torch.empty((ms, pw.N, pw.K), dtype=torch.int16, device="cuda") for pw in base.projs]
+            nsl = max(copies, 16) if tag == "decode" else copies
+            slots = [DequantSlot(torch, gnf4, cfg, layers[i % copies], T, 400 + i, wbuf)
+                     for i in range(nsl)]
+            for sl in slots:
+                sl.capture(torch, gnf4)
+            chain = capture_chain(torch, gnf4, slots)
+            steps = args.steps if tag == "decode" else max(10, args.steps // 10)
+            dt, byts, fl = time_steps(torch, slots, chain, steps, max(2, args.warmup // 5))
+            dq[tag] = (T, dt)
+            del slots, layers, chain, wbuf
+            torch.cuda.empty_cache()
+        out["dequant"] = dq
+
     if args.calib_copy:
         a = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
         b = torch.empty_like(a)
@@ -515,6 +594,16 @@ def main():
         f["steps"] = ("route_logits (top-k + softmax + route), gate_up GEMM with the SwiGLU "
                       "epilogue (bf16 H), down GEMM on H, combine")
         result["ffn_layer"] = f
+    if out.get("dequant"):
+        dqr = {}
+        for tag, (T, dt) in out["dequant"].items():
+            fused = out[tag]["ms_per_step"] * 1e-3 if tag in out else None
+            dqr[tag] = {"T": T, "step_us": round(dt * 1e6, 2),
+                        "fused_speedup": round(dt / fused, 3) if fused else None}
+        dqr["steps"] = ("route, bf16 dequant of the routed experts of each projection "
+                        "(gnf4_dequant_experts_bf16), torch.bmm (T = 1) or one torch.mm per "
+                        "active expert (library GEMMs), combine; same inputs as the fused step")
+        result["dequant_path"] = dqr
     if not args.no_cpu and decode_ok:
         result["cpu_baseline"] = cpu_baseline(cfg, T_dec)
     print(json.dumps(result), flush=True)

@@ -248,6 +248,23 @@ gnf4_status gnf4_dequant(const gnf4_weights *w, int32_t e, float *out, gnf4_stre
   return device_status(launch_dequant(k, e, out, (hipStream_t)stream), "dequant launch");
 }
 
+gnf4_status gnf4_dequant_experts_bf16(const gnf4_weights *w, const int32_t *experts,
+                                      const int32_t *count, int32_t max_experts, uint16_t *out,
+                                      gnf4_stream_t stream) {
+  gnf4_status st = check_weights(w);
+  if (st != GNF4_OK) return st;
+  if (max_experts < 0 || max_experts > w->E)
+    return fail(GNF4_ERR_INVALID_ARG, "max_experts = %d outside [0, E = %d]", max_experts, w->E);
+  if (max_experts == 0) return ok();
+  if (!experts || !count || !out) return fail(GNF4_ERR_INVALID_ARG, "a pointer argument is NULL");
+  if (!aligned16(out)) return fail(GNF4_ERR_INVALID_ARG, "out must be 16-byte aligned");
+  if ((int64_t)max_experts * w->N * (w->K / 8) > 0x7fffffffLL * 256)
+    return fail(GNF4_ERR_UNSUPPORTED, "too many weights for one call");
+  Weights k = to_kernel(w);
+  return device_status(launch_dequant_bf16(k, experts, count, max_experts, out, (hipStream_t)stream),
+                       "bf16 dequant launch");
+}
+
 gnf4_status gnf4_quantize(int32_t format, const float *W, int32_t rows, int32_t K, uint8_t *codes,
                           void *scales, float *scales2, gnf4_stream_t stream) {
   if (format < GNF4_NF4 || format > GNF4_MXFP4)

@@ -63,6 +63,72 @@ __global__ __launch_bounds__(kCodecThreads) void dequant_kernel(Weights w, int e
   }
 }
 
+// The decode of the dequantize-then-matmul comparison path: the experts
+// listed in experts[0 .. min(*count, max_experts)) decoded to bf16 (the
+// exact float32 value rounded to nearest even; NaN stays a quiet NaN) into
+// out[slot][N][K]. One thread per 4 packed bytes (8 values, one 16-byte
+// store), so a wave's loads and stores each cover one contiguous span. The
+// 16 code values sit in lanes 0..15 of a register and reach each lane
+// through ds_bpermute (no select chain, no bank conflicts). Every lane of a
+// wave takes part in the permutes; lanes without work skip loads and stores.
+__global__ __launch_bounds__(kCodecThreads) void dequant_bf16_kernel(
+    Weights w, const int32_t *__restrict__ experts, const int32_t *__restrict__ count,
+    int32_t max_experts, uint16_t *__restrict__ out) {
+  const int64_t per_expert = (int64_t)w.N * (w.K / 8);      // 8-value groups
+  const int64_t grp = (int64_t)blockIdx.x * kCodecThreads + threadIdx.x;
+  const int lane = threadIdx.x & 63;
+  const bool mx = w.format == GNF4_MXFP4;
+  const float table = mx ? e2m1_value((uint32_t)lane) : nf4_value((uint32_t)lane);
+  const int slot = (int)(grp / per_expert);
+  int e = -1;
+  if (slot < max_experts && slot < *count) e = experts[slot];
+  const bool live = e >= 0 && e < w.E;
+  if (!__any(live)) return;                     // whole wave idle
+  const int64_t rem = grp - (int64_t)slot * per_expert;
+  const int64_t n = rem / (w.K / 8), j = rem % (w.K / 8);    // 8-value group j of row n
+  const int64_t row = (int64_t)(live ? e : 0) * w.N + (live ? n : 0);
+  uint32_t q = 0;
+  float sc = 0.0f;
+  if (live) {
+    q = reinterpret_cast<const uint32_t *>(w.codes + row * (w.K / 2))[j];
+    if (mx) {
+      sc = e8m0_to_f32(reinterpret_cast<const uint8_t *>(w.scales)[row * (w.K / 32) + j / 4]);
+    } else {
+      const int64_t blk = row * (w.K / 64) + j / 8;
+      sc = w.format == GNF4_NF4
+               ? reinterpret_cast<const float *>(w.scales)[blk]
+               : (float)reinterpret_cast<const int8_t *>(w.scales)[blk] * w.scales2[blk >> 8];
+    }
+  }
+  const int tbits = __builtin_bit_cast(int, table);
+  uint32_t h[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t b = (q >> (8 * i)) & 0xffu;
+    // element 2i: NF4 high nibble, MXFP4 low nibble
+    const uint32_t q0 = mx ? (b & 15u) : (b >> 4), q1 = mx ? (b >> 4) : (b & 15u);
+    const float v0 = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute((int)(q0 << 2), tbits)) * sc;
+    const float v1 = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute((int)(q1 << 2), tbits)) * sc;
+    const uint32_t u0 = __builtin_bit_cast(uint32_t, v0), u1 = __builtin_bit_cast(uint32_t, v1);
+    const uint32_t r0 = (v0 != v0) ? 0x7fc0u : ((u0 + 0x7fffu + ((u0 >> 16) & 1u)) >> 16);
+    const uint32_t r1 = (v1 != v1) ? 0x7fc0u : ((u1 + 0x7fffu + ((u1 >> 16) & 1u)) >> 16);
+    h[i] = r0 | (r1 << 16);
+  }
+  if (!live) return;
+  *reinterpret_cast<uint4 *>(out + ((int64_t)slot * w.N + n) * w.K + j * 8) =
+      make_uint4(h[0], h[1], h[2], h[3]);
+}
+
+hipError_t launch_dequant_bf16(const Weights &w, const int32_t *experts, const int32_t *count,
+                               int32_t max_experts, uint16_t *out, hipStream_t s) {
+  const int64_t groups = (int64_t)max_experts * w.N * (w.K / 8);
+  const int64_t blocks = (groups + kCodecThreads - 1) / kCodecThreads;
+  if (blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL(dequant_bf16_kernel, dim3((unsigned)blocks), dim3(kCodecThreads), 0, s, w,
+                     experts, count, max_experts, out);
+  return hipGetLastError();
+}
+
 hipError_t launch_dequant(const Weights &w, int32_t e, float *out, hipStream_t s) {
   const int64_t chunks = (int64_t)w.N * (w.K / 32);
   const int64_t blocks = (chunks + kCodecThreads - 1) / kCodecThreads;

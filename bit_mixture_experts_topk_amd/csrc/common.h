@@ -207,6 +207,8 @@ hipError_t launch_mfma(const GemmArgs &a, hipStream_t s);
 hipError_t launch_combine(const float *Y, const int32_t *inv, const float *w, int32_t T,
                           int32_t k, int32_t N, float *out, hipStream_t s);
 hipError_t launch_dequant(const Weights &w, int32_t e, float *out, hipStream_t s);
+hipError_t launch_dequant_bf16(const Weights &w, const int32_t *experts, const int32_t *count,
+                               int32_t max_experts, uint16_t *out, hipStream_t s);
 hipError_t launch_quantize(int32_t fmt, const float *W, int32_t rows, int32_t K, uint8_t *codes,
                            void *scales, float *scales2, hipStream_t s);
 

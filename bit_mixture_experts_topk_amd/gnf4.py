@@ -26,7 +26,8 @@ STATUS = {0: "OK", 1: "INVALID_ARG", 2: "UNSUPPORTED", 4: "DEVICE"}
 # Every entry point declared in include/gnf4.h.
 EXPORTS = ("gnf4_route", "gnf4_route_logits", "gnf4_grouped_gemm", "gnf4_grouped_gemm_swiglu",
            "gnf4_swiglu", "gnf4_combine",
-           "gnf4_dequant", "gnf4_quantize", "gnf4_nf4_codebook", "gnf4_last_error",
+           "gnf4_dequant", "gnf4_dequant_experts_bf16", "gnf4_quantize", "gnf4_nf4_codebook",
+           "gnf4_last_error",
            "gnf4_build_id")
 
 
@@ -60,6 +61,7 @@ def lib():
         L.gnf4_grouped_gemm_swiglu.argtypes = [ctypes.POINTER(CWeights), P, I, P, P, P, P, I, I, P, S]
         L.gnf4_combine.argtypes = [P, P, P, I, I, I, P, S]
         L.gnf4_dequant.argtypes = [ctypes.POINTER(CWeights), I, P, S]
+        L.gnf4_dequant_experts_bf16.argtypes = [ctypes.POINTER(CWeights), P, P, I, P, S]
         L.gnf4_quantize.argtypes = [I, P, I, I, P, P, P, S]
         L.gnf4_nf4_codebook.argtypes = [ctypes.POINTER(ctypes.c_float)]
         L.gnf4_nf4_codebook.restype = None
@@ -254,6 +256,19 @@ def combine(Y, inv, topk_w, T, k, out=None):
         out = torch.empty((max(T, 1), N), dtype=torch.float32, device=Y.device)
     _check(lib().gnf4_combine(_ptr(Y), _ptr(inv), _ptr(topk_w), T, k, N, _ptr(out), _stream()),
            "gnf4_combine")
+    return out
+
+
+def dequant_experts_bf16(w, experts, count, max_experts, out=None):
+    """bf16 bits (int16) [max_experts, N, K] of the listed experts (device
+    int32 experts[], count[1]); slots past *count are left untouched."""
+    _dev(experts, torch.int32, "experts")
+    _dev(count, torch.int32, "count")
+    if out is None:
+        out = torch.zeros((max(max_experts, 1), w.N, w.K), dtype=torch.int16, device=w.codes.device)
+    cw = w.cstruct()
+    _check(lib().gnf4_dequant_experts_bf16(ctypes.byref(cw), _ptr(experts), _ptr(count), max_experts,
+                                           _ptr(out), _stream()), "gnf4_dequant_experts_bf16")
     return out
 
 

@@ -191,6 +191,21 @@ gnf4_status gnf4_swiglu(const float *Y, int32_t rows, int32_t I, uint16_t *H,
  * MXFP4: e2m1(q) * 2^(s-127), exact (s = 255 gives NaN). */
 gnf4_status gnf4_dequant(const gnf4_weights *w, int32_t e, float *out, gnf4_stream_t stream);
 
+/* gnf4_dequant_experts_bf16 -- the decode step of the dequantize-then-matmul
+ * path the pages measure the fused kernel against (section cited at the
+ * top: grouped decode faster than a dequant path; the comparison path is
+ * this library's reading of it). For slot s < min(*count, max_experts)
+ * with e = experts[s] in [0, E):
+ *   out[s][n][k] = bf16(W'[e][n][k])   (nearest even; NaN -> 0x7FC0)
+ * where W' is gnf4_dequant's float32 value. experts and count are device
+ * int32 (e.g. gnf4_route's active and n_active, so nothing is read back);
+ * slots at or past *count, or with an id outside [0, E), are left as they
+ * are. out uint16 bf16 bits [max_experts][N][K], 16-byte aligned.
+ * 0 <= max_experts <= E. */
+gnf4_status gnf4_dequant_experts_bf16(const gnf4_weights *w, const int32_t *experts,
+                                      const int32_t *count, int32_t max_experts,
+                                      uint16_t *out, gnf4_stream_t stream);
+
 /* gnf4_quantize -- pack float32 weights W [rows][K] (rows = E*N) into the
  * layout above: NF4 / NF4_DQ block 64 with nearest-code rounding (ties to
  * the lower code, decided in float64), NF4_DQ with linear int8 absmax and

@@ -135,6 +135,17 @@ def test_fused_gemm_rejects(L):
     assert "even N" in gnf4.last_error()
 
 
+def test_dequant_experts_bf16_rejects(L):
+    w = weights()
+    p = 0x1000
+    assert L.gnf4_dequant_experts_bf16(ctypes.byref(w), p, p, 5, p, None) == INVALID   # > E
+    assert "max_experts = 5" in gnf4.last_error()
+    assert L.gnf4_dequant_experts_bf16(ctypes.byref(w), p, p, -1, p, None) == INVALID
+    assert L.gnf4_dequant_experts_bf16(ctypes.byref(w), None, p, 2, p, None) == INVALID
+    assert L.gnf4_dequant_experts_bf16(ctypes.byref(w), p, p, 2, 0x1008, None) == INVALID
+    assert L.gnf4_dequant_experts_bf16(ctypes.byref(w), None, None, 0, None, None) == 0
+
+
 def test_swiglu_rejects(L):
     p = 0x1000
     assert L.gnf4_swiglu(p, 4, 6, p, None) == INVALID and "I = 6" in gnf4.last_error()

@@ -119,3 +119,36 @@ def test_route_edge_cases(E, T, k):
     r = g.route(torch.from_numpy(ids).cuda().reshape(T, k), E)
     ref = routing.route(ids, E)
     check_route(r, ref, T * k)
+
+
+def dequant_bf16_ref(fmt, codes, scales, scales2, e, N, K):
+    """The oracle's float32 dequant of expert e rounded to bf16 bits."""
+    from oracle import grouped_gemm as ogemm
+    from oracle import layer as olayer
+    W = ogemm.dequant_rows(fmt, codes, scales, scales2, e, np.arange(N), N, K)
+    return olayer.f64_to_bf16_bits(W.astype(np.float64))
+
+
+@pytest.mark.parametrize("fmt", ["nf4", "nf4_dq", "mxfp4"])
+def test_dequant_experts_bf16_matches_oracle(fmt):
+    g = gnf4()
+    E, N, K = 6, 40, 256
+    W = adversarial_weights(fmt, E=E, N=N, K=K)
+    codes, scales, scales2 = oracle_pack(fmt, W)
+    if fmt == "mxfp4":                               # the extreme e8m0 scales too
+        scales = scales.copy()
+        scales.reshape(-1)[:6] = np.array([0, 1, 127, 253, 254, 255], dtype=np.uint8)
+    pw = packed_to_device(g, fmt, codes, scales, scales2, E, N, K)
+    experts = torch.tensor([4, 1, 5, -1, 2, 0], dtype=torch.int32, device="cuda")
+    count = torch.tensor([5], dtype=torch.int32, device="cuda")
+    out = torch.full((6, N, K), 0x1234, dtype=torch.int16, device="cuda")
+    say("dequant bf16", fmt)
+    got = g.dequant_experts_bf16(pw, experts, count, 6, out).cpu().numpy().view(np.uint16)
+    for slot, e in enumerate([4, 1, 5]):
+        ref = dequant_bf16_ref(fmt, codes, scales, scales2, e, N, K)
+        nan = (ref & 0x7FFF) > 0x7F80
+        assert np.array_equal(nan, (got[slot] & 0x7FFF) > 0x7F80)
+        assert np.array_equal(got[slot][~nan], ref[~nan]), (fmt, slot)
+    assert np.all(got[3] == 0x1234)                  # id -1: left untouched
+    assert np.array_equal(got[4], dequant_bf16_ref(fmt, codes, scales, scales2, 2, N, K))
+    assert np.all(got[5] == 0x1234)                  # past the count
