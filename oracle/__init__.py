@@ -15,6 +15,8 @@ precision, written for a reader checking it against the pages by eye:
 * ``combine``  weighted sum of the top-k rows back per token.
 * ``layer``    the router's top-k choice with softmax weights, SwiGLU between
                the projections, and exact float64 -> bfloat16 rounding.
+* ``backward`` input gradient of the grouped GEMM through the frozen packed
+               weights, and its sum over a token's routed copies.
 
 Sources. The pages describe a kernel that computes mixture-of-experts matmuls
 directly on 4-bit packed expert weights, one launch for all active experts,
@@ -28,4 +30,4 @@ Parity status per function is listed in each module header. Every function
 here is pinned by at least one test that does not re-run its own formula.
 """
 
-from . import nf4, mxfp4, routing, grouped_gemm, combine, layer  # noqa: F401
+from . import nf4, mxfp4, routing, grouped_gemm, combine, layer, backward  # noqa: F401
