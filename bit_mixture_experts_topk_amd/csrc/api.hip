@@ -220,6 +220,29 @@ gnf4_status gnf4_grouped_gemm_swiglu(const gnf4_weights *w, const uint16_t *X, i
   return grouped_gemm_any(w, X, gather, offsets, perm, active, n_active, T, k, nullptr, H, stream);
 }
 
+gnf4_status gnf4_grouped_gemm_dx(const gnf4_weights *w, const uint16_t *dY,
+                                 const int32_t *offsets, int32_t T, int32_t k, float *dA,
+                                 gnf4_stream_t stream) {
+  gnf4_status st = check_weights(w);
+  if (st != GNF4_OK) return st;
+  if (k < 1 || k > 64) return fail(GNF4_ERR_INVALID_ARG, "k = %d outside [1, 64]", k);
+  if (T < 0) return fail(GNF4_ERR_INVALID_ARG, "T = %d is negative", T);
+  if ((int64_t)T * k >= ((int64_t)1 << 31) - 1024)
+    return fail(GNF4_ERR_INVALID_ARG, "T*k too large");
+  if (w->N % 8) return fail(GNF4_ERR_INVALID_ARG, "N = %d must be a multiple of 8", w->N);
+  if (T == 0) return ok();
+  if (!dY || !offsets || !dA) return fail(GNF4_ERR_INVALID_ARG, "a pointer argument is NULL");
+  if (!aligned16(dY) || !aligned16(dA))
+    return fail(GNF4_ERR_INVALID_ARG, "dY and dA must be 16-byte aligned");
+  DxArgs a;
+  a.w = to_kernel(w);
+  a.dY = dY;
+  a.offsets = offsets;
+  a.rows = T * k;
+  a.dA = dA;
+  return device_status(launch_gemm_dx(a, (hipStream_t)stream), "grouped GEMM dx launch");
+}
+
 gnf4_status gnf4_combine(const float *Y, const int32_t *inv, const float *topk_w, int32_t T,
                          int32_t k, int32_t N, float *out, gnf4_stream_t stream) {
   if (k < 1 || k > 64) return fail(GNF4_ERR_INVALID_ARG, "k = %d outside [1, 64]", k);

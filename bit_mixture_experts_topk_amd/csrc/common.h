@@ -57,6 +57,16 @@ struct GemmArgs {
   uint16_t *H;       // bf16 output [T*k][N/2] (SwiGLU epilogue; then Y is unused)
 };
 
+// Input gradient of the grouped GEMM: dA [rows][K] from dY [rows][N], both
+// in routed (permuted) order, segments given by offsets.
+struct DxArgs {
+  Weights w;
+  const uint16_t *dY;
+  const int32_t *offsets;
+  int32_t rows;
+  float *dA;
+};
+
 // SwiGLU (the activation between a mixture-of-experts layer's projections;
 // not described on the pages, the form of the public models the workloads
 // follow): bf16 of silu(g) * u, silu(x) = x / (1 + exp(-x)), rounded once
@@ -204,6 +214,7 @@ hipError_t launch_topk(const float *logits, int32_t T, int32_t E, int32_t k, int
 hipError_t launch_swiglu(const float *Y, int32_t rows, int32_t I, uint16_t *H, hipStream_t s);
 hipError_t launch_gemv(const GemmArgs &a, hipStream_t s);
 hipError_t launch_mfma(const GemmArgs &a, hipStream_t s);
+hipError_t launch_gemm_dx(const DxArgs &a, hipStream_t s);
 hipError_t launch_combine(const float *Y, const int32_t *inv, const float *w, int32_t T,
                           int32_t k, int32_t N, float *out, hipStream_t s);
 hipError_t launch_dequant(const Weights &w, int32_t e, float *out, hipStream_t s);

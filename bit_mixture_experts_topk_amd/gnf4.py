@@ -25,7 +25,7 @@ STATUS = {0: "OK", 1: "INVALID_ARG", 2: "UNSUPPORTED", 4: "DEVICE"}
 
 # Every entry point declared in include/gnf4.h.
 EXPORTS = ("gnf4_route", "gnf4_route_logits", "gnf4_grouped_gemm", "gnf4_grouped_gemm_swiglu",
-           "gnf4_swiglu", "gnf4_combine",
+           "gnf4_grouped_gemm_dx", "gnf4_swiglu", "gnf4_combine",
            "gnf4_dequant", "gnf4_dequant_experts_bf16", "gnf4_quantize", "gnf4_nf4_codebook",
            "gnf4_last_error",
            "gnf4_build_id")
@@ -59,6 +59,7 @@ def lib():
         L.gnf4_swiglu.argtypes = [P, I, I, P, S]
         L.gnf4_grouped_gemm.argtypes = [ctypes.POINTER(CWeights), P, I, P, P, P, P, I, I, P, S]
         L.gnf4_grouped_gemm_swiglu.argtypes = [ctypes.POINTER(CWeights), P, I, P, P, P, P, I, I, P, S]
+        L.gnf4_grouped_gemm_dx.argtypes = [ctypes.POINTER(CWeights), P, P, I, I, P, S]
         L.gnf4_combine.argtypes = [P, P, P, I, I, I, P, S]
         L.gnf4_dequant.argtypes = [ctypes.POINTER(CWeights), I, P, S]
         L.gnf4_dequant_experts_bf16.argtypes = [ctypes.POINTER(CWeights), P, P, I, P, S]
@@ -246,6 +247,29 @@ def grouped_gemm_swiglu(w, X, gather, r, T, k, H=None):
                                           _ptr(r["perm"]), _ptr(r["active"]), _ptr(r["n_active"]),
                                           T, k, _ptr(H), _stream()), "gnf4_grouped_gemm_swiglu")
     return H
+
+
+def grouped_gemm_dx(w, dY, r, T, k, dA=None):
+    """dA [T*k, K] float32 = dY [T*k, N] (bf16 bits, routed order) times the
+    dequantized weights of each row's expert: the input gradient of
+    grouped_gemm with frozen weights. Rows past the routed ones are left as
+    they are (uninitialised when dA is allocated here)."""
+    if not (dY.is_cuda and dY.is_contiguous() and dY.element_size() == 2):
+        raise ValueError("dY must be a contiguous bf16 (or 16-bit bit pattern) CUDA tensor")
+    if dA is None:
+        dA = torch.empty((max(T * k, 1), w.K), dtype=torch.float32, device=dY.device)
+    cw = w.cstruct()
+    _check(lib().gnf4_grouped_gemm_dx(ctypes.byref(cw), _ptr(dY), _ptr(r["offsets"]), T, k,
+                                      _ptr(dA), _stream()), "gnf4_grouped_gemm_dx")
+    return dA
+
+
+def token_grad(dA, r, T, k, out=None):
+    """dX [T, K] float32: the sum of each token's k routed copies of dA (the
+    gradient through the gather of a first projection), via gnf4_combine
+    with unit weights."""
+    ones = torch.ones((max(T, 1), k), dtype=torch.float32, device=dA.device)
+    return combine(dA, r["inv"], ones, T, k, out=out)
 
 
 def combine(Y, inv, topk_w, T, k, out=None):

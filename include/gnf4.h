@@ -20,6 +20,10 @@
  *                       (or gnf4_grouped_gemm, then gnf4_swiglu)
  *   gnf4_grouped_gemm   down projection (rows of H, routed order)
  *   gnf4_combine
+ * and the backward pass through the frozen experts is, per projection:
+ *   gnf4_grouped_gemm_dx   dA[p] = dY[p] . W'[e]    (one launch)
+ *   gnf4_combine           with unit weights: dX[t] = sum_j dA[inv[t*k+j]]
+ *                          for a projection whose rows were gathered
  *
  * Conventions for every entry point:
  *  - All array pointers are DEVICE pointers owned by the caller; the library
@@ -141,6 +145,30 @@ gnf4_status gnf4_grouped_gemm_swiglu(const gnf4_weights *w, const uint16_t *X, i
                                      const int32_t *offsets, const int32_t *perm,
                                      const int32_t *active, const int32_t *n_active,
                                      int32_t T, int32_t k, uint16_t *H, gnf4_stream_t stream);
+
+/* gnf4_grouped_gemm_dx -- input gradient of gnf4_grouped_gemm through the
+ * frozen packed weights, one launch for all active experts, the codes and
+ * scales read as stored (Jordan Anderson, jordananderson-pages.pages.dev,
+ * section "grouped-nf4-gemm & experts-4bit", fourth bullet: a differentiable
+ * kernel whose backward is one launch on the packed 4-bit weights). For
+ * expert e and every routed row p in [offsets[e], offsets[e+1]),
+ *   dA[p][j] = sum_{n<N} dY[p][n] * W'[e][n][j]         (j < K)
+ * with W' the dequantized weights (exactly as gnf4_dequant decodes them).
+ * dY uint16 bf16 bits [T*k][N] and dA float32 [T*k][K], both in the routed
+ * order of gnf4_route (rows of Y in the forward call), both 16-byte aligned;
+ * N % 8 == 0. The weights are read only (no weight gradient: the experts are
+ * frozen). Rows p >= offsets[E] (dropped assignments) are not written.
+ * Arithmetic: float32 accumulation of bf16 products; each dequantized NF4 /
+ * NF4_DQ weight w (float32) enters as bf16(w) plus bf16(w - bf16(w)), which
+ * leaves out less than 2^-16 of |w|; MXFP4 weights are exact in bf16.
+ * For the gathered first projection the gradient of token t's activation row
+ * is the sum over its k routed copies: gnf4_combine(dA, inv, ones, T, k, K).
+ * Errors: INVALID_ARG for bad weights (as gnf4_grouped_gemm), k outside
+ * [1, 64], T < 0, N % 8 != 0, NULL or misaligned pointers; T = 0 is a
+ * no-op. */
+gnf4_status gnf4_grouped_gemm_dx(const gnf4_weights *w, const uint16_t *dY,
+                                 const int32_t *offsets, int32_t T, int32_t k, float *dA,
+                                 gnf4_stream_t stream);
 
 /* gnf4_combine -- weighted top-k combine back to tokens.
  *   out[t][n] = sum_{j=0..k-1} topk_w[t][j] * Y[inv[t*k+j]][n]

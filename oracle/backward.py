@@ -36,6 +36,7 @@ of the forward gather).
 
 import numpy as np
 
+from . import mxfp4, nf4
 from .grouped_gemm import bf16_bits_to_f64, dequant_expert
 
 
@@ -69,3 +70,41 @@ def token_grad(dA, inv, T, k):
             if p >= 0:
                 dX[t] += dA[p]
     return dX
+
+
+def dequant_cols(fmt, codes, scales, scales2, e, c0, width, N, K):
+    """float32 [N, width]: columns [c0, c0 + width) of expert e's dequantized
+    weights, decoded from the matching slice of every row (c0 and width are
+    multiples of the format's block, 64 for NF4 / NF4_DQ and 32 for MXFP4),
+    with the same block scales as dequant_expert."""
+    if fmt == "mxfp4":
+        return mxfp4.dequantize(codes[e][:, c0 // 2:(c0 + width) // 2],
+                                scales[e][:, c0 // 32:(c0 + width) // 32], width)
+    b0, nb = c0 // nf4.BLOCK, width // nf4.BLOCK
+    if fmt == "nf4":
+        a = np.asarray(scales[e][:, b0:b0 + nb], dtype=np.float32)
+    else:
+        q8 = np.asarray(scales).reshape(-1)
+        s2 = np.asarray(scales2, dtype=np.float32)
+        blk = ((e * N + np.arange(N))[:, None] * (K // nf4.BLOCK) + b0 + np.arange(nb)[None, :]).reshape(-1)
+        a = (q8[blk].astype(np.float64) * s2[blk // nf4.DQ_GROUP].astype(np.float64)).astype(np.float32)
+        a = a.reshape(N, nb)
+    return nf4.dequantize(codes[e][:, c0 // 2:(c0 + width) // 2], a, width)
+
+
+def grouped_gemm_dx_entries(fmt, codes, scales, scales2, dY_bits, offsets, N, K, p, j):
+    """float64 dA[p[i], j[i]] for sampled (routed row, column) pairs, as
+    grouped_gemm_dx defines them, decoding only the 64-column (NF4) or
+    32-column (MXFP4) block of each sampled column, for every weight row."""
+    p = np.asarray(p, dtype=np.int64)
+    j = np.asarray(j, dtype=np.int64)
+    offsets = np.asarray(offsets).reshape(-1)
+    blk = 32 if fmt == "mxfp4" else nf4.BLOCK
+    expert = np.searchsorted(offsets, p, side="right") - 1
+    out = np.empty(p.size, dtype=np.float64)
+    for e, cb in sorted(set(zip(expert.tolist(), (j // blk).tolist()))):
+        sel = np.nonzero((expert == e) & (j // blk == cb))[0]
+        W = dequant_cols(fmt, codes, scales, scales2, e, cb * blk, blk, N, K).astype(np.float64)
+        dY = bf16_bits_to_f64(np.asarray(dY_bits)[p[sel]]).reshape(sel.size, N)
+        out[sel] = np.einsum("sn,sn->s", dY, W[:, j[sel] - cb * blk].T)
+    return out

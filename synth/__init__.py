@@ -26,7 +26,10 @@ routing; and down, W [E, d, I], whose input is a separate bf16 N(0,1) matrix
 [T*k, I] already in routed order.
 
 Distributions. X ~ N(0, 1) drawn in float32 and rounded to bfloat16 (round to
-nearest even). W ~ N(0, 0.02) (0.02 is the standard deviation) in float32.
+nearest even). Output gradients dY for the backward pass through the frozen
+experts are drawn the same way ([T*k, N], routed order; the pages give no
+gradient statistics, and the comparison bars are relative to the result's
+own scale). W ~ N(0, 0.02) (0.02 is the standard deviation) in float32.
 Router logits: N(0, 1) (tiny, qwen235, gptoss, mixtral), U(0, 1) (olmoe),
 N(0, 1) plus a Zipf(1.1) bias ln(p_e), p_e proportional to (e+1)^-1.1
 (qwen30, expert 0 hottest). Top-k by logit, ties to the lower expert id; the
@@ -52,6 +55,7 @@ T_X_DOWN = 5
 T_W_SINGLE = 6
 T_Y = 7
 T_PACKED = 8
+T_DY = 9
 
 
 @dataclass(frozen=True)
@@ -110,6 +114,11 @@ def f32_to_bf16_bits(x):
     u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
     r = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
     return r.astype(np.uint16)
+
+
+def grad_rows(cfg, rows, N, seed=0, extra=0):
+    """bf16 bits [rows, N] of N(0,1) output gradients in routed order."""
+    return activations(cfg, rows, N, T_DY, seed, extra)
 
 
 def activations(cfg, rows, K, tensor_id=T_X, seed=0, extra=0):

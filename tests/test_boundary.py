@@ -176,3 +176,23 @@ def test_dequant_and_quantize_reject(L):
     assert L.gnf4_quantize(5, 0x1000, 4, 64, 0x2000, 0x3000, None, None) == INVALID
     assert L.gnf4_quantize(0, 0x1000, 4, 64, 0x2008, 0x3000, None, None) == INVALID
     assert L.gnf4_quantize(0, None, 0, 64, None, None, None, None) == 0
+
+
+def test_gemm_dx_rejects(L):
+    w = weights()                      # N = 8
+    p = 0x1000
+    assert L.gnf4_grouped_gemm_dx(ctypes.byref(w), None, p, 2, 2, p, None) == INVALID
+    assert "NULL" in gnf4.last_error()
+    assert L.gnf4_grouped_gemm_dx(ctypes.byref(w), p, p, 2, 2, 0x1004, None) == INVALID
+    assert "16-byte" in gnf4.last_error()
+    assert L.gnf4_grouped_gemm_dx(ctypes.byref(w), 0x1008, p, 2, 2, p, None) == INVALID
+    assert L.gnf4_grouped_gemm_dx(ctypes.byref(w), p, p, 2, 0, p, None) == INVALID
+    assert "k = 0" in gnf4.last_error()
+    assert L.gnf4_grouped_gemm_dx(ctypes.byref(w), p, p, -1, 2, p, None) == INVALID
+    ragged = weights(N=60)
+    assert L.gnf4_grouped_gemm_dx(ctypes.byref(ragged), p, p, 2, 2, p, None) == INVALID
+    assert "multiple of 8" in gnf4.last_error()
+    assert L.gnf4_grouped_gemm_dx(None, p, p, 2, 2, p, None) == INVALID
+    bad = weights(fmt=2, K=48)
+    assert L.gnf4_grouped_gemm_dx(ctypes.byref(bad), p, p, 2, 2, p, None) == INVALID
+    assert L.gnf4_grouped_gemm_dx(ctypes.byref(w), None, None, 0, 2, None, None) == 0      # T = 0

@@ -180,3 +180,23 @@ def test_flipped_weight_byte_breaks_identity():
     lo, hi = int(r["offsets"][e]), int(r["offsets"][e + 1])
     broken = [abs(float(dA[p] @ Af[p]) - float(dYf[p] @ Y[p])) > 1e-9 for p in range(lo, hi)]
     assert hi > lo and all(broken)
+
+
+@pytest.mark.parametrize("fmt", ["nf4", "nf4_dq", "mxfp4"])
+def test_sampled_entries_and_column_blocks(fmt):
+    """The column-block decoder returns the same float32 weights as the whole
+    expert's decode, and the sampled entries equal the full gradient's."""
+    E, N, K, T, k = 4, 40, 256, 10, 3
+    codes, scales, scales2, r, _, dY = case(fmt, E, N, K, T, k, 13)
+    for e in range(E):
+        W = grouped_gemm.dequant_expert(fmt, codes, scales, scales2, e, N, K)
+        for c0 in (0, 64, 192):
+            assert np.array_equal(backward.dequant_cols(fmt, codes, scales, scales2, e, c0, 64, N, K),
+                                  W[:, c0:c0 + 64])
+    dA = backward.grouped_gemm_dx(fmt, codes, scales, scales2, dY, r["offsets"], N, K)
+    g = np.random.default_rng(2)
+    nv = int(r["offsets"][-1])
+    p = g.integers(0, nv, size=200)
+    j = g.integers(0, K, size=200)
+    got = backward.grouped_gemm_dx_entries(fmt, codes, scales, scales2, dY, r["offsets"], N, K, p, j)
+    assert np.allclose(got, dA[p, j], rtol=1e-12, atol=1e-14)

@@ -18,6 +18,16 @@ own error. The layer bar adds the three per-call bars:
 
 * max |got - ref| <= 3e-2 * rms(ref)
 * ||got - ref||_F / ||ref||_F <= 6e-3
+
+The input gradient through the frozen experts (gnf4_grouped_gemm_dx) feeds
+each dequantized float32 weight to the MFMA as bf16 hi + lo; the part left
+out is below 2^-16 of each weight (RNE twice: 2^-9 then 2^-9 of that), and
+the float32 accumulation adds about 2^-24 sqrt(N) relative. Its own bar,
+which a dropped lo term (a 2^-9 relative error per weight, about 1.6e-3
+relative Frobenius) fails:
+
+* max |got - ref| <= 1e-4 * rms(ref)
+* ||got - ref||_F / ||ref||_F <= 2e-5
 """
 
 import numpy as np
@@ -26,6 +36,8 @@ MAX_REL_RMS = 1e-2
 FROB_REL = 2e-3
 LAYER_MAX_REL_RMS = 3 * MAX_REL_RMS
 LAYER_FROB_REL = 3 * FROB_REL
+DX_MAX_REL_RMS = 1e-4
+DX_FROB_REL = 2e-5
 
 
 def errors(got, ref):
@@ -60,4 +72,12 @@ def assert_within_layer(got, ref, what=""):
     assert max_rel <= LAYER_MAX_REL_RMS and frob <= LAYER_FROB_REL, (
         "%s: max|err|/rms = %.3e (bar %.0e), rel Frobenius = %.3e (bar %.0e)"
         % (what, max_rel, LAYER_MAX_REL_RMS, frob, LAYER_FROB_REL))
+    return max_rel, frob
+
+
+def assert_within_dx(got, ref, what=""):
+    max_rel, frob = errors(got, ref)
+    assert max_rel <= DX_MAX_REL_RMS and frob <= DX_FROB_REL, (
+        "%s: max|err|/rms = %.3e (bar %.0e), rel Frobenius = %.3e (bar %.0e)"
+        % (what, max_rel, DX_MAX_REL_RMS, frob, DX_FROB_REL))
     return max_rel, frob
