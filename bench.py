@@ -55,13 +55,17 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-dequant-path", action="store_true",
                     help="skip the dequantize-then-matmul comparison leg")
-    ap.add_argument("--only", choices=["decode", "prefill"], default=None)
+    ap.add_argument("--only", choices=["decode", "prefill", "backward"], default=None,
+                    help="run only the forward decode leg, the forward prefill leg, or the "
+                         "backward legs")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
     ap.add_argument("--kernel-only", choices=["decode", "prefill"], default=None,
                     help="launch only the gate_up grouped GEMM of one step, --steps times "
                          "(for hardware-counter passes); prints no JSON")
     ap.add_argument("--proj", default=None, help="projection for --kernel-only (default gate_up)")
+    ap.add_argument("--dx", action="store_true",
+                    help="with --kernel-only: launch the input-gradient GEMM instead")
     return ap.parse_args()
 
 
@@ -86,16 +90,23 @@ def kernel_only(args):
     X = torch.from_numpy(synth.activations(cfg, rows, proj.K, synth.T_X, 0, T).view(np.int16)).cuda()
     r = gnf4.route(torch.from_numpy(ids).cuda(), cfg.E)
     Y = torch.empty((T * cfg.k, proj.N), dtype=torch.float32, device="cuda")
+    if args.dx:
+        dY = torch.from_numpy(synth.grad_rows(cfg, T * cfg.k, proj.N, 0, T).view(np.int16)).cuda()
+        dA = torch.empty((T * cfg.k, proj.K), dtype=torch.float32, device="cuda")
     torch.cuda.synchronize()
     for _ in range(args.steps):
-        gnf4.grouped_gemm(pw, X, proj.gather, r, T, cfg.k, Y)
+        if args.dx:
+            gnf4.grouped_gemm_dx(pw, dY, r, T, cfg.k, dA)
+        else:
+            gnf4.grouped_gemm(pw, X, proj.gather, r, T, cfg.k, Y)
     if args.calib_copy:
         a = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
         b = torch.empty_like(a)
         b.copy_(a)
     torch.cuda.synchronize()
-    print("kernel-only %s %s %s T=%d x%d done" % (cfg.name, proj.name, args.kernel_only, T,
-                                                  args.steps), file=sys.stderr, flush=True)
+    print("kernel-only %s %s %s%s T=%d x%d done" % (cfg.name, proj.name, args.kernel_only,
+                                                    " dx" if args.dx else "", T, args.steps),
+          file=sys.stderr, flush=True)
 
 
 def packed_bytes_per_expert(pw):
@@ -260,6 +271,74 @@ class DequantSlot(StepSlot):
         gnf4.combine(self.Y[last], r["inv"], self.tw, T, k, self.out)
 
 
+class BackwardSlot(StepSlot):
+    """One backward step through the frozen experts of the layer: route, then
+    for each projection in reverse order the input gradient dA = dY . W' on
+    the packed weights (gnf4_grouped_gemm_dx, one launch each), then the sum
+    of each token's routed copies for the gathered first projection. Each
+    projection's output gradient dY is a standalone bf16 N(0,1) matrix in
+    routed order (the SwiGLU and combine backward steps between them need
+    saved forward activations and are not part of the path)."""
+
+    def __init__(self, torch, gnf4, cfg, layer, T, seed):
+        import synth
+        super().__init__(torch, gnf4, cfg, layer, T, seed)
+        k = cfg.k
+        self.dY = [torch.from_numpy(synth.grad_rows(cfg, T * k, p.N, seed, T + 7 * pi).view(np.int16)).cuda()
+                   for pi, p in enumerate(cfg.projs)]
+        self.dA = [torch.empty((T * k, p.K), dtype=torch.float32, device="cuda") for p in cfg.projs]
+        self.ones = torch.ones((T, k), dtype=torch.float32, device="cuda")
+        self.dX = torch.empty((T, cfg.projs[0].K), dtype=torch.float32, device="cuda")
+
+    def run(self, gnf4):
+        cfg, T, k = self.layer.cfg, self.T, self.layer.cfg.k
+        r = gnf4.route(self.ids, cfg.E, out=self.r)
+        for pi in reversed(range(len(self.layer.projs))):
+            gnf4.grouped_gemm_dx(self.layer.projs[pi], self.dY[pi], r, T, k, self.dA[pi])
+        gnf4.combine(self.dA[0], r["inv"], self.ones, T, k, self.dX)
+
+
+class DequantBackwardSlot(BackwardSlot):
+    """The same backward step through the dequantize-then-matmul path: the
+    routed experts of each projection decoded to bf16 in HBM, then torch's
+    library GEMMs dA = dY . W (torch.bmm at T = 1, one torch.mm per active
+    expert otherwise), bf16 results widened to float32 for the token sum."""
+
+    def __init__(self, torch, gnf4, cfg, layer, T, seed, wbuf):
+        super().__init__(torch, gnf4, cfg, layer, T, seed)
+        k = cfg.k
+        ids = self.ids.cpu().numpy()
+        self.wbuf = wbuf
+        counts = np.bincount(ids.reshape(-1), minlength=cfg.E)
+        self.segs = []
+        off = 0
+        for e in range(cfg.E):
+            c = int(counts[e])
+            if c:
+                self.segs.append((len(self.segs), off, c))
+            off += c
+        self.max_slots = min(cfg.E, T * k)
+        self.dAb = [torch.empty((T * k, p.K), dtype=torch.bfloat16, device="cuda") for p in cfg.projs]
+
+    def run(self, gnf4):
+        import torch
+        cfg, T, k = self.layer.cfg, self.T, self.layer.cfg.k
+        r = gnf4.route(self.ids, cfg.E, out=self.r)
+        for pi in reversed(range(len(self.layer.projs))):
+            pw = self.layer.projs[pi]
+            W = gnf4.dequant_experts_bf16(pw, r["active"], r["n_active"], self.max_slots,
+                                          self.wbuf[pi]).view(torch.bfloat16)
+            dYb = self.dY[pi].view(torch.bfloat16)
+            if T == 1:
+                torch.bmm(dYb.view(self.max_slots, 1, pw.N), W[:self.max_slots],
+                          out=self.dAb[pi].view(self.max_slots, 1, pw.K))
+            else:
+                for slot, p0, c in self.segs:
+                    torch.mm(dYb[p0:p0 + c], W[slot], out=self.dAb[pi][p0:p0 + c])
+        self.dA[0].copy_(self.dAb[0])
+        gnf4.combine(self.dA[0], r["inv"], self.ones, T, k, self.dX)
+
+
 def capture_chain(torch, gnf4, slots):
     """One graph holding one step per slot, in slot order: a replay runs
     len(slots) consecutive steps with no host launch between them."""
@@ -290,12 +369,23 @@ def time_steps(torch, slots, chain, steps, warmup):
     return dt, per, fl
 
 
-def time_kernel(torch, gnf4, slots, steps, warmup):
-    """Mean duration of the gate_up GEMM launch: `steps` launches rotating
-    through the slots (route outputs computed beforehand) are captured in one
-    graph, and HIP events recorded on the replay stream bracket its replays;
-    the mean is elapsed time / launches, so host launch cost is excluded and
-    the gaps between back-to-back launches are included."""
+def gate_up_launch(gnf4, sl):
+    cfg = sl.layer.cfg
+    gnf4.grouped_gemm(sl.layer.projs[0], sl.X, 1, sl.r, sl.T, cfg.k, sl.Y[0])
+
+
+def gate_up_dx_launch(gnf4, sl):
+    cfg = sl.layer.cfg
+    gnf4.grouped_gemm_dx(sl.layer.projs[0], sl.dY[0], sl.r, sl.T, cfg.k, sl.dA[0])
+
+
+def time_kernel(torch, gnf4, slots, steps, warmup, launch=gate_up_launch):
+    """Mean duration of one launch of the gate_up GEMM (or of `launch`):
+    `steps` launches rotating through the slots (route outputs computed
+    beforehand) are captured in one graph, and HIP events recorded on the
+    replay stream bracket its replays; the mean is elapsed time / launches,
+    so host launch cost is excluded and the gaps between back-to-back
+    launches are included."""
     for sl in slots:
         gnf4.route(sl.ids, sl.layer.cfg.E, out=sl.r)
     torch.cuda.synchronize()
@@ -305,14 +395,12 @@ def time_kernel(torch, gnf4, slots, steps, warmup):
     stream.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(stream):
         for i in range(min(warmup, G)):
-            sl = slots[i % len(slots)]
-            gnf4.grouped_gemm(sl.layer.projs[0], sl.X, 1, sl.r, sl.T, cfg.k, sl.Y[0])
+            launch(gnf4, slots[i % len(slots)])
     torch.cuda.synchronize()
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph, stream=stream):
         for i in range(G):
-            sl = slots[i % len(slots)]
-            gnf4.grouped_gemm(sl.layer.projs[0], sl.X, 1, sl.r, sl.T, cfg.k, sl.Y[0])
+            launch(gnf4, slots[i % len(slots)])
     torch.cuda.synchronize()
     reps = max(2, -(-steps // G))
     with torch.cuda.stream(stream):
@@ -341,13 +429,17 @@ def gemm_kernel_name(cfg, T):
     return "mfma16_kernel"
 
 
-def profile_traffic(cfg_name, mode):
-    """HBM bytes per launch of the gate_up kernel from the committed rocprofv3
-    counter summary for this workload, if the GEMM source is unchanged since
-    the counters were taken (else None)."""
+def profile_traffic(cfg_name, mode, kernel=None):
+    """HBM bytes per launch of the gate_up kernel (the forward GEMM's, or the
+    named kernel's) from the committed rocprofv3 counter summary for this
+    workload, if the kernel's source is unchanged since the counters were
+    taken (else None)."""
     import glob
     import hashlib
-    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*-gate_up-%s-%s.txt" % (cfg_name, mode)))):
+    pattern = "%s-gate_up-%s-%s.txt" % (kernel or "*", cfg_name, mode)
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", pattern))):
+        if kernel is None and os.path.basename(path).startswith("mfma_dx_kernel"):
+            continue
         fields = {}
         for line in open(path):
             if ":" in line and not line.startswith(" "):
@@ -447,8 +539,8 @@ def main():
               "data": "synthetic"}
     T_dec = min(cfg.Ts)
     T_pre = max(cfg.Ts)
-    decode_ok = T_dec * cfg.k <= 64 and args.only != "prefill"
-    prefill_ok = T_pre * cfg.k > 64 and args.only != "decode"
+    decode_ok = T_dec * cfg.k <= 64 and args.only in (None, "decode")
+    prefill_ok = T_pre * cfg.k > 64 and args.only in (None, "prefill")
 
     out = {}
     if decode_ok:
@@ -532,6 +624,44 @@ def main():
             torch.cuda.empty_cache()
         out["dequant"] = dq
 
+    if args.only in (None, "backward"):
+        # backward through the frozen experts: input gradients of every projection
+        bw = {}
+        for T, tag in ((T_dec, "decode"), (T_pre, "prefill")):
+            if tag == "decode" and T * cfg.k > 64:
+                continue
+            step_bytes = layer_bytes * min(1.0, T * cfg.k / cfg.E)
+            copies = int(min(32 if tag == "decode" else 8,
+                             max(2, np.ceil(3 * MALL_BYTES / max(step_bytes, 1)))))
+            layers = [base] + [base.clone(torch) for _ in range(copies - 1)]
+            nsl = max(copies, 16) if tag == "decode" else copies
+            slots = [BackwardSlot(torch, gnf4, cfg, layers[i % copies], T, seed=500 + i)
+                     for i in range(nsl)]
+            for sl in slots:
+                sl.capture(torch, gnf4)
+            chain = capture_chain(torch, gnf4, slots)
+            steps = args.steps if tag == "decode" else max(10, args.steps // 10)
+            wu = max(2, args.warmup // 5)
+            dt, byts, fl = time_steps(torch, slots, chain, steps, wu)
+            kms, kbytes, kfl, _ = time_kernel(torch, gnf4, slots, steps, wu, gate_up_dx_launch)
+            entry = dict(T=T, dt=dt, byts=byts, fl=fl, kms=kms, kbytes=kbytes, kfl=kfl)
+            del slots, chain
+            if not args.no_dequant_path:
+                ms = min(cfg.E, T * cfg.k)
+                wbuf = [torch.empty((ms, pw.N, pw.K), dtype=torch.int16, device="cuda") for pw in base.projs]
+                nd = min(nsl, 16 if tag == "decode" else 4)
+                dslots = [DequantBackwardSlot(torch, gnf4, cfg, layers[i % copies], T, 600 + i, wbuf)
+                          for i in range(nd)]
+                for sl in dslots:
+                    sl.capture(torch, gnf4)
+                dchain = capture_chain(torch, gnf4, dslots)
+                entry["dq_dt"], _, _ = time_steps(torch, dslots, dchain, steps, wu)
+                del dslots, dchain, wbuf
+            bw[tag] = entry
+            del layers
+            torch.cuda.empty_cache()
+        out["backward"] = bw
+
     if args.calib_copy:
         a = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
         b = torch.empty_like(a)
@@ -604,6 +734,38 @@ def main():
                         "(gnf4_dequant_experts_bf16), torch.bmm (T = 1) or one torch.mm per "
                         "active expert (library GEMMs), combine; same inputs as the fused step")
         result["dequant_path"] = dqr
+    if out.get("backward"):
+        b = {}
+        for tag, en in out["backward"].items():
+            item = {"T": en["T"], "step_us": round(en["dt"] * 1e6, 2)}
+            kt = en["kfl"] / (en["kms"] * 1e-3) / 1e12
+            kg = en["kbytes"] / (en["kms"] * 1e-3) / 1e9
+            name = "mfma_dx_kernel (gate_up, T=%d)" % en["T"]
+            if tag == "decode":
+                item["packed_GBps"] = round(en["byts"] / en["dt"] / 1e9, 2)
+                tr, tsrc = profile_traffic(cfg.name, "decode", "mfma_dx_kernel")
+                item["roofline"] = {"bound": "hbm", "achieved": round(kg, 1), "peak": HBM_PEAK_GBS,
+                                    "unit": "GB/s", "frac": round(kg / HBM_PEAK_GBS, 4),
+                                    "traffic": tr, "traffic_unit": "HBM bytes/launch",
+                                    "traffic_source": tsrc, "kernel": name,
+                                    "kernel_us": round(en["kms"] * 1e3, 3),
+                                    "bytes_per_launch": int(en["kbytes"])}
+            else:
+                item["tflops"] = round(en["fl"] / en["dt"] / 1e12, 2)
+                tr, tsrc = profile_traffic(cfg.name, "prefill", "mfma_dx_kernel")
+                item["roofline"] = {"bound": "mfma", "achieved": round(kt, 2), "peak": BF16_PEAK_TFLOPS,
+                                    "unit": "TFLOP/s", "frac": round(kt / BF16_PEAK_TFLOPS, 4),
+                                    "traffic": tr, "traffic_unit": "HBM bytes/launch",
+                                    "traffic_source": tsrc, "kernel": name,
+                                    "kernel_us": round(en["kms"] * 1e3, 2)}
+            if "dq_dt" in en:
+                item["dequant_path_step_us"] = round(en["dq_dt"] * 1e6, 2)
+                item["fused_speedup"] = round(en["dq_dt"] / en["dt"], 3)
+            b[tag] = item
+        b["steps"] = ("route, gnf4_grouped_gemm_dx on down then gate_up (one launch each, packed "
+                      "weights), sum of each token's routed copies (gnf4_combine, unit weights); "
+                      "dequant_path: bf16 decode of the routed experts + torch.bmm / torch.mm")
+        result["backward"] = b
     if not args.no_cpu and decode_ok:
         result["cpu_baseline"] = cpu_baseline(cfg, T_dec)
     print(json.dumps(result), flush=True)

@@ -230,6 +230,8 @@ gnf4_status gnf4_grouped_gemm_dx(const gnf4_weights *w, const uint16_t *dY,
   if ((int64_t)T * k >= ((int64_t)1 << 31) - 1024)
     return fail(GNF4_ERR_INVALID_ARG, "T*k too large");
   if (w->N % 8) return fail(GNF4_ERR_INVALID_ARG, "N = %d must be a multiple of 8", w->N);
+  if ((int64_t)T * k * w->N * 2 >= ((int64_t)1 << 32))
+    return fail(GNF4_ERR_UNSUPPORTED, "dY must be below 4 GiB (T*k*N*2 bytes)");
   if (T == 0) return ok();
   if (!dY || !offsets || !dA) return fail(GNF4_ERR_INVALID_ARG, "a pointer argument is NULL");
   if (!aligned16(dY) || !aligned16(dA))

@@ -45,6 +45,7 @@
 // contiguous runs, so tiles that share weight columns and gradient rows run
 // on one XCD's L2 and no XCD is left idle by the host's upper bound.
 #include <algorithm>
+#include <type_traits>
 
 #include "common.h"
 
@@ -64,13 +65,18 @@ __device__ __forceinline__ uint32_t nf4_f32_bits(uint32_t q) {
 
 // Table entry b (an NF4 byte), copy j: the float32 pair (c[b >> 4], c[b & 15]),
 // the value of element 2i (high nibble) first, at byte offset b * 256 + j * 8.
-// Thread t writes float2 slots t + 256 i (i < 32): entry (t + 256 i) / 32.
+// Thread t writes float2 slots t + 256 i (i < 32), i.e. entry b = t / 32 + 8 i
+// copy t % 32: its high nibble is i / 2 (a constant of the unrolled loop) and
+// its low nibble t / 32 + 8 (i & 1), one of two values per thread.
 __device__ __forceinline__ void fill_dx_table(float *tab, int tid) {
-#pragma unroll 4
+  const uint32_t t5 = (uint32_t)tid >> 5;
+  const float lo0 = __builtin_bit_cast(float, nf4_f32_bits(t5));
+  const float lo1 = __builtin_bit_cast(float, nf4_f32_bits(t5 + 8u));
+#pragma unroll
   for (int i = 0; i < 256 * kDxPairCopies / kDxThreads; ++i) {
-    const uint32_t slot = (uint32_t)tid + kDxThreads * i, b = slot / kDxPairCopies;
-    tab[2 * slot] = __builtin_bit_cast(float, nf4_f32_bits(b >> 4));
-    tab[2 * slot + 1] = __builtin_bit_cast(float, nf4_f32_bits(b & 15u));
+    const uint32_t slot = (uint32_t)tid + kDxThreads * i;
+    *reinterpret_cast<float2 *>(tab + 2 * slot) =
+        make_float2(__builtin_bit_cast(float, kNF4Bits[i >> 1]), (i & 1) ? lo1 : lo0);
   }
 }
 
@@ -125,6 +131,20 @@ __device__ __forceinline__ int dx_total_tiles(const int32_t *offsets, int E, int
   return total * n_tiles_k;
 }
 
+// One halving step of a cross-lane reduction: the lane keeps half of its
+// first 2 CNT values (the upper half when lane & d), adds the partner's copy
+// of that half (lane ^ d) and leaves the sums in v[0 .. CNT).
+template <int CNT>
+__device__ __forceinline__ void halve(float *v, int d, int lane) {
+  const bool upper = (lane & d) != 0;
+#pragma unroll
+  for (int i = 0; i < CNT; ++i) {
+    const float send = upper ? v[i] : v[i + CNT];
+    const float keep = upper ? v[i + CNT] : v[i];
+    v[i] = keep + __shfl_xor(send, d, 64);
+  }
+}
+
 // Swizzled position of 16-byte chunk q (8 contraction values) of staged row r.
 __device__ __forceinline__ int dy_chunk(int r, int q) { return r * 4 + (q ^ ((r >> 2) & 3)); }
 
@@ -143,6 +163,8 @@ __device__ __forceinline__ void split_pair(float w0, float w1, uint32_t &hi, uin
   lo = pack_bf16_pair(w0 - h0, w1 - h1);
 }
 
+constexpr int kDxBufferDword3 = 0x00020000;   // raw buffer, 32-bit data format
+
 template <int FMT, int RT>
 __global__ __launch_bounds__(kDxThreads, 2) void mfma_dx_kernel(DxArgs a, int n_tiles_k) {
   constexpr bool kNF = FMT != GNF4_MXFP4;
@@ -153,7 +175,8 @@ __global__ __launch_bounds__(kDxThreads, 2) void mfma_dx_kernel(DxArgs a, int n_
   __shared__ float tab[kNF ? kDxPairWords : 1];
   __shared__ uint4 Ds[2][kChunks];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar offsets
   const int N = a.w.N, K = a.w.K, E = a.w.E;
 
   // logical tile id: contiguous runs of the real tile count per XCD
@@ -177,56 +200,96 @@ __global__ __launch_bounds__(kDxThreads, 2) void mfma_dx_kernel(DxArgs a, int n_
   const int colbase = kt * 256 + wave * 64;
   const int mycol = colbase + 4 * c;              // this lane's 4 output columns
   const bool col_ok = mycol < K;
-  const int ldcol = col_ok ? mycol : 0;           // clamped for loads
-  const int64_t half_k = K >> 1;
-  const uint8_t *codes_e = a.w.codes + (int64_t)e * N * half_k + (ldcol >> 1);
-  const int nkb = K >> 6, ngrp = K >> 5;
-  const int kb = ldcol >> 6, grp = ldcol >> 5;
-  const int64_t row_e = (int64_t)e * N;           // flat weight row of this expert's row 0
+  const uint32_t ldcol = col_ok ? (uint32_t)mycol : 0u;   // clamped for loads
+  const uint32_t half_k = (uint32_t)K >> 1, nkb = (uint32_t)K >> 6, ngrp = (uint32_t)K >> 5;
+  const uint32_t kb = ldcol >> 6, grp = ldcol >> 5;
+  // bytes per weight row of the scales: float32 absmax, int8 q8, e8m0 byte
+  const uint32_t scale_row = FMT == GNF4_NF4 ? nkb * 4u : kDQ ? nkb : ngrp;
+  const uint32_t scale_col = FMT == GNF4_NF4 ? kb * 4u : kDQ ? kb : grp;
+  const int64_t erow = (int64_t)e * N;            // flat weight row of this expert's row 0
 
-  // gradient rows: chunk loads of this thread for the step starting at n0
-  auto load_dy = [&](int n0, uint4 (&v)[kChunkLoads]) {
+  // buffer views: the expert's codes and scales, the tensor's second-level
+  // scales, the segment's gradient rows; every access below stays in range
+  const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)(a.w.codes + erow * half_k), (short)0, (int)((uint32_t)N * half_k), kDxBufferDword3);
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)(reinterpret_cast<const uint8_t *>(a.w.scales) + erow * scale_row), (short)0,
+      (int)((uint32_t)N * scale_row), kDxBufferDword3);
+  const __amdgpu_buffer_rsrc_t rs2 = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)a.w.scales2, (short)0,
+      kDQ ? (int)(uint32_t)((((int64_t)E * N * nkb + 255) >> 8) * 4) : 0, kDxBufferDword3);
+  const __amdgpu_buffer_rsrc_t rd = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)(a.dY + (int64_t)seg0 * N), (short)0, (int)((uint32_t)count * (uint32_t)N * 2u),
+      kDxBufferDword3);
+
+  // this lane's weight rows 8g + i of a step: code bytes at coff + row * half_k
+  const uint32_t coff = (uint32_t)(8 * g) * half_k + (ldcol >> 1);
+  const uint32_t soff = (uint32_t)(8 * g) * scale_row + scale_col;
+  // this thread's gradient chunks: row r (clamped to the segment), chunk q
+  uint32_t dyoff[kChunkLoads];
+  int dyq[kChunkLoads];
 #pragma unroll
-    for (int i = 0; i < kChunkLoads; ++i) {
-      const int ch = tid + kDxThreads * i;
-      v[i] = make_uint4(0, 0, 0, 0);
-      if (ch < kChunks) {
-        const int r = ch >> 2, q = ch & 3;
-        const int p = seg0 + min(row0 + r, count - 1);
-        const int n = n0 + 8 * q;
-        if (n < N) v[i] = *reinterpret_cast<const uint4 *>(a.dY + (int64_t)p * N + n);
-      }
-    }
-  };
-  auto store_dy = [&](int buf, const uint4 (&v)[kChunkLoads]) {
-#pragma unroll
-    for (int i = 0; i < kChunkLoads; ++i) {
-      const int ch = tid + kDxThreads * i;
-      if (ch < kChunks) Ds[buf][dy_chunk(ch >> 2, ch & 3)] = v[i];
-    }
-  };
-  // weight rows n0 + 8g + i (i < 8): two code bytes and the row's scale
-  uint32_t code[8];
-  float scl[8];
-  int8_t q8[8];
-  float s2[8];
-  uint32_t sb[8];
-  auto load_w = [&](int n0) {
+  for (int i = 0; i < kChunkLoads; ++i) {
+    const int ch = tid + kDxThreads * i;
+    const int r = ch >> 2;
+    dyq[i] = ch & 3;
+    dyoff[i] = (uint32_t)min(row0 + r, count - 1) * (uint32_t)N * 2u + (uint32_t)dyq[i] * 16u;
+  }
+
+  // Main loop: pairs of full 32-row steps, every load unconditional and in
+  // range (the prefetch step index is clamped with scalar arithmetic); the
+  // rest (an odd full step, a partial last step) runs after it without
+  // prefetch, each lane clamping its rows to N - 1 and zeroing rows past N.
+  const int nfull = N >> 5;
+  const int npair = nfull >> 1;
+  uint32_t cw[2][8], sv[2][8];
+  float s2v[2][8];
+  uint4 dreg[2][kChunkLoads];
+
+  // weights of step s into register set S; `clamp`: rows of a step that may
+  // reach past N are clamped per lane (else step s must be full)
+  auto issue_w = [&](auto SET, int s, bool clamp) {
+    constexpr int S = decltype(SET)::value;
+    const uint32_t n0 = (uint32_t)s * 32u;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const int n = n0 + 8 * g + i;
-      const int nn = n < N ? n : N - 1;
-      code[i] = *reinterpret_cast<const uint16_t *>(codes_e + (int64_t)nn * half_k);
-      const int64_t fr = row_e + nn;              // flat weight row
-      if constexpr (FMT == GNF4_NF4) {
-        scl[i] = static_cast<const float *>(a.w.scales)[fr * nkb + kb];
-      } else if constexpr (kDQ) {
-        const int64_t blk = fr * nkb + kb;
-        q8[i] = static_cast<const int8_t *>(a.w.scales)[blk];
-        s2[i] = a.w.scales2[blk >> 8];
-      } else {
-        sb[i] = static_cast<const uint8_t *>(a.w.scales)[fr * ngrp + grp];
+      uint32_t vc = coff, vs = soff, so_c = (n0 + i) * half_k, so_s = (n0 + i) * scale_row;
+      uint32_t row = n0 + 8 * g + i;
+      if (clamp) {
+        row = min(row, (uint32_t)N - 1u);
+        vc = row * half_k + (ldcol >> 1);
+        vs = row * scale_row + scale_col;
+        so_c = 0;
+        so_s = 0;
       }
+      cw[S][i] = __builtin_amdgcn_raw_buffer_load_b16(rc, vc, so_c, 0);
+      if constexpr (FMT == GNF4_NF4) {
+        sv[S][i] = __builtin_amdgcn_raw_buffer_load_b32(rs, vs, so_s, 0);
+      } else {
+        sv[S][i] = __builtin_amdgcn_raw_buffer_load_b8(rs, vs, so_s, 0);
+      }
+      if constexpr (kDQ) {
+        const int64_t blk = (erow + row) * nkb + kb;
+        s2v[S][i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                  rs2, (uint32_t)(blk >> 8) * 4u, 0, 0));
+      }
+    }
+  };
+  // gradient rows of full step s into register set S (threads without a
+  // chunk load a duplicate of a valid one and do not store it)
+  auto issue_dy = [&](auto SET, int s) {
+    constexpr int S = decltype(SET)::value;
+#pragma unroll
+    for (int i = 0; i < kChunkLoads; ++i)
+      dreg[S][i] = __builtin_bit_cast(
+          uint4, __builtin_amdgcn_raw_buffer_load_b128(rd, dyoff[i], (uint32_t)s * 64u, 0));
+  };
+  auto store_dy = [&](auto SET, int buf) {
+    constexpr int S = decltype(SET)::value;
+#pragma unroll
+    for (int i = 0; i < kChunkLoads; ++i) {
+      const int ch = tid + kDxThreads * i;
+      if (ch < kChunks) Ds[buf][dy_chunk(ch >> 2, dyq[i])] = dreg[S][i];
     }
   };
 
@@ -236,85 +299,120 @@ __global__ __launch_bounds__(kDxThreads, 2) void mfma_dx_kernel(DxArgs a, int n_
 #pragma unroll
     for (int t = 0; t < 4; ++t) acc[r][t] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
 
-  const int nsteps = (N + 31) >> 5;
-  {
-    uint4 v[kChunkLoads];
-    load_dy(0, v);
-    store_dy(0, v);
-  }
-  load_w(0);
-  __syncthreads();
-
   const uint32_t lane8 = (uint32_t)(lane & 31) * 8u;
-  for (int s = 0; s < nsteps; ++s) {
-    const int n0 = s * 32;
-    // this step's weights from registers, then the next step's loads
-    uint32_t cw[8];
+  // B fragments of register set S for the step starting at n0, then the
+  // MFMAs against LDS buffer `buf`
+  auto compute = [&](auto SET, int n0, int buf) {
+    constexpr int S = decltype(SET)::value;
     float aw[8];
+    uint32_t cwv[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      cw[i] = code[i];
-      float av;
-      if constexpr (FMT == GNF4_NF4) av = scl[i];
-      else if constexpr (kDQ) av = (float)q8[i] * s2[i];
-      else av = e8m0_to_f32(sb[i]);
-      aw[i] = (n0 + 8 * g + i < N) ? av : 0.0f;   // rows past N contribute zero
+      cwv[i] = cw[S][i];
+      if constexpr (FMT == GNF4_NF4) aw[i] = __builtin_bit_cast(float, sv[S][i]);
+      else if constexpr (kDQ) aw[i] = (float)(int8_t)sv[S][i] * s2v[S][i];
+      else aw[i] = e8m0_to_f32(sv[S][i]);
     }
-    uint4 dyv[kChunkLoads];
-    const bool more = s + 1 < nsteps;
-    if (more) {
-      load_dy(n0 + 32, dyv);
-      load_w(n0 + 32);
+    if (n0 + 32 > N) {                            // rows past N contribute zero
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        if (n0 + 8 * g + i >= N) aw[i] = 0.0f;
     }
-
-    // B fragments: tile t, rows 8g .. 8g+7 of column 4c + t, as bf16 pairs
     uint32_t bhi[4][4], blo[4][4];
-    float w[8][4];
+    {
+      float w[8][4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      if constexpr (kNF) {
-        const float2 p0 = *reinterpret_cast<const float2 *>(
-            reinterpret_cast<const char *>(tab) + __builtin_amdgcn_perm(cw[i], lane8, 0x0c0c0400u));
-        const float2 p1 = *reinterpret_cast<const float2 *>(
-            reinterpret_cast<const char *>(tab) + __builtin_amdgcn_perm(cw[i], lane8, 0x0c0c0500u));
-        w[i][0] = p0.x * aw[i];
-        w[i][1] = p0.y * aw[i];
-        w[i][2] = p1.x * aw[i];
-        w[i][3] = p1.y * aw[i];
-      } else {
-        typedef float f32x2_t __attribute__((ext_vector_type(2)));
-        const f32x2_t v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw[i], aw[i], 0);
-        const f32x2_t v1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw[i], aw[i], 1);
-        w[i][0] = v0[0];
-        w[i][1] = v0[1];
-        w[i][2] = v1[0];
-        w[i][3] = v1[1];
-      }
-    }
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-#pragma unroll
-      for (int h = 0; h < 4; ++h) {
-        if constexpr (kNF) split_pair(w[2 * h][t], w[2 * h + 1][t], bhi[t][h], blo[t][h]);
-        else bhi[t][h] = pack_bf16_pair(w[2 * h][t], w[2 * h + 1][t]);
-      }
-
-    const int buf = s & 1;
-#pragma unroll
-    for (int r = 0; r < RT; ++r) {
-      const uint4 av = Ds[buf][dy_chunk(16 * r + c, g)];
-      const bf16x8_t af = __builtin_bit_cast(bf16x8_t, av);
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const bf16x8_t bh = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4 *>(bhi[t]));
-        acc[r][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bh, acc[r][t], 0, 0, 0);
+      for (int i = 0; i < 8; ++i) {
         if constexpr (kNF) {
-          const bf16x8_t bl = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4 *>(blo[t]));
-          acc[r][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bl, acc[r][t], 0, 0, 0);
+          const float2 p0 = *reinterpret_cast<const float2 *>(
+              reinterpret_cast<const char *>(tab) + __builtin_amdgcn_perm(cwv[i], lane8, 0x0c0c0400u));
+          const float2 p1 = *reinterpret_cast<const float2 *>(
+              reinterpret_cast<const char *>(tab) + __builtin_amdgcn_perm(cwv[i], lane8, 0x0c0c0500u));
+          w[i][0] = p0.x * aw[i];
+          w[i][1] = p0.y * aw[i];
+          w[i][2] = p1.x * aw[i];
+          w[i][3] = p1.y * aw[i];
+        } else {
+          typedef float f32x2_t __attribute__((ext_vector_type(2)));
+          const f32x2_t v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cwv[i], aw[i], 0);
+          const f32x2_t v1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cwv[i], aw[i], 1);
+          w[i][0] = v0[0];
+          w[i][1] = v0[1];
+          w[i][2] = v1[0];
+          w[i][3] = v1[1];
         }
       }
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          if constexpr (kNF) split_pair(w[2 * h][t], w[2 * h + 1][t], bhi[t][h], blo[t][h]);
+          else bhi[t][h] = pack_bf16_pair(w[2 * h][t], w[2 * h + 1][t]);
+        }
     }
-    if (more) store_dy(buf ^ 1, dyv);
+    return [&, bhi, blo, buf]() {
+#pragma unroll
+      for (int r = 0; r < RT; ++r) {
+        const bf16x8_t af = __builtin_bit_cast(bf16x8_t, Ds[buf][dy_chunk(16 * r + c, g)]);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const bf16x8_t bh = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4 *>(bhi[t]));
+          acc[r][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bh, acc[r][t], 0, 0, 0);
+          if constexpr (kNF) {
+            const bf16x8_t bl = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4 *>(blo[t]));
+            acc[r][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bl, acc[r][t], 0, 0, 0);
+          }
+        }
+      }
+    };
+  };
+
+  using Set0 = std::integral_constant<int, 0>;
+  using Set1 = std::integral_constant<int, 1>;
+  if (npair > 0) {
+    issue_dy(Set0{}, 0);
+    issue_w(Set0{}, 0, false);
+    issue_dy(Set1{}, 1);
+    issue_w(Set1{}, 1, false);
+    store_dy(Set0{}, 0);
+    __syncthreads();
+    const int last = 2 * npair - 1;               // last step of the main loop
+    for (int s = 0; s < 2 * npair; s += 2) {
+      // step s: set 0, LDS buffer 0; its registers are reloaded for s + 2
+      {
+        auto mma = compute(Set0{}, s * 32, 0);
+        issue_w(Set0{}, min(s + 2, last), false);
+        issue_dy(Set0{}, min(s + 2, last));
+        mma();
+        store_dy(Set1{}, 1);                      // step s + 1's rows
+        __syncthreads();
+      }
+      // step s + 1: set 1, LDS buffer 1; reloaded for s + 3
+      {
+        auto mma = compute(Set1{}, s * 32 + 32, 1);
+        issue_w(Set1{}, min(s + 3, last), false);
+        issue_dy(Set1{}, min(s + 3, last));
+        mma();
+        store_dy(Set0{}, 0);                      // step s + 2's rows (unused after the last)
+        __syncthreads();
+      }
+    }
+  }
+  // the rest: at most one full step and one partial step
+  for (int s = 2 * npair; s < (N + 31) >> 5; ++s) {
+    const int n0 = s * 32;
+    issue_w(Set0{}, s, true);
+#pragma unroll
+    for (int i = 0; i < kChunkLoads; ++i) {
+      const int ch = tid + kDxThreads * i;
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (ch < kChunks && n0 + 8 * dyq[i] < N)
+        v = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rd, dyoff[i], (uint32_t)n0 * 2u, 0));
+      if (ch < kChunks) Ds[0][dy_chunk(ch >> 2, dyq[i])] = v;
+    }
+    __syncthreads();
+    auto mma = compute(Set0{}, n0, 0);
+    mma();
     __syncthreads();
   }
 
@@ -330,6 +428,225 @@ __global__ __launch_bounds__(kDxThreads, 2) void mfma_dx_kernel(DxArgs a, int n_
         *reinterpret_cast<float4 *>(a.dA + (int64_t)(seg0 + lr) * K + mycol) = o;
       }
     }
+}
+
+// ================================================ few rows per expert
+
+// gemv_dx_kernel: one workgroup per item (expert e, up to MT routed rows of
+// its segment, 32 output columns). Wave w takes the 64-row groups
+// R = w, w + 4, w + 8, ... of the weight rows, lane l row 64 R + l: it reads
+// the 16 code bytes of the item's columns in that row (one 128-bit load),
+// the row's scale and dY[p][n] of its MT rows p, and accumulates s * c[q] in
+// float32 with s = dY[p][n] * absmax (exact codebook values, no bf16
+// rounding of the weights). Each wave reduces its 32 MT partial sums over
+// its 64 lanes by halving exchanges (xor 32, 16, 8, 4, 2, then 1), after
+// which lanes 2j, 2j + 1 hold column j; the four waves' sums meet in LDS.
+//
+// Rows advance in batches of U per lane (4, or 2 for four rows per item),
+// two batches in flight: every load of the main loop is unconditional and in
+// range; the remaining groups (including a partial last one) run after it
+// with each lane's row clamped to N - 1 and its contribution zeroed.
+constexpr int kGemvDxMaxRows = 64;   // routed rows (T*k) up to which the GEMV path is used
+
+template <int FMT, int MT>
+__global__ __launch_bounds__(kDxThreads, 2) void gemv_dx_kernel(DxArgs a, int n_items) {
+  constexpr bool kNF = FMT != GNF4_MXFP4;
+  constexpr bool kDQ = FMT == GNF4_NF4_DQ;
+  constexpr int U = MT >= 4 ? 2 : 4;              // rows per lane per batch
+  __shared__ float tab[kNF ? kDxPairWords : 1];
+  __shared__ float red[4][MT][32];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar offsets
+  const int N = a.w.N, K = a.w.K, E = a.w.E;
+  // items: expert by expert, row block, then 32-column chunk (fastest), so
+  // the 8 chunks that share a 128-byte code line are neighbours; they are
+  // dealt to the XCDs in contiguous runs of the real item count
+  const int nchunk = K >> 5;
+  const int total = dx_total_tiles<MT>(a.offsets, E, nchunk, lane);
+  const int per = (total + 7) >> 3;
+  const int bid = blockIdx.x, jb = bid >> 3;
+  const int logical = (bid & 7) * per + jb;
+  if (jb >= per || logical >= total) return;      // whole workgroup
+  int e, start, mtiles;
+  dx_find_tile<MT>(a.offsets, E, nchunk, logical, lane, e, start, mtiles);
+  if (e < 0) return;
+  const int local = logical - start;
+  const int rb = local / nchunk, kc = local - rb * nchunk;
+  const int seg0 = a.offsets[e];
+  const int count = a.offsets[e + 1] - seg0;
+  const int prow0 = rb * MT;                      // first row of the item within the segment
+
+  const uint32_t half_k = (uint32_t)K >> 1, nkb = (uint32_t)K >> 6, ngrp = (uint32_t)K >> 5;
+  const uint32_t col0 = (uint32_t)kc * 32u;
+  const uint32_t kb = col0 >> 6;
+  const uint32_t scale_row = FMT == GNF4_NF4 ? nkb * 4u : kDQ ? nkb : ngrp;
+  const uint32_t scale_col = FMT == GNF4_NF4 ? kb * 4u : kDQ ? kb : (uint32_t)kc;
+  const int64_t erow = (int64_t)e * N;
+  const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)(a.w.codes + erow * half_k), (short)0, (int)((uint32_t)N * half_k), kDxBufferDword3);
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)(reinterpret_cast<const uint8_t *>(a.w.scales) + erow * scale_row), (short)0,
+      (int)((uint32_t)N * scale_row), kDxBufferDword3);
+  const __amdgpu_buffer_rsrc_t rs2 = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)a.w.scales2, (short)0,
+      kDQ ? (int)(uint32_t)((((int64_t)E * N * nkb + 255) >> 8) * 4) : 0, kDxBufferDword3);
+  const __amdgpu_buffer_rsrc_t rd = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)(a.dY + (int64_t)seg0 * N), (short)0, (int)((uint32_t)count * (uint32_t)N * 2u),
+      kDxBufferDword3);
+  uint32_t dyrow[MT];                             // byte offset of row p, element 0
+#pragma unroll
+  for (int m = 0; m < MT; ++m) dyrow[m] = (uint32_t)min(prow0 + m, count - 1) * (uint32_t)N * 2u;
+
+  // this wave's 64-row groups: R = wave + 4 i; the first `nfull` are whole
+  const int groups = (N + 63) >> 6;
+  const int nfull_w = ((N >> 6) - wave + 3) >> 2 > 0 ? ((N >> 6) - wave + 3) >> 2 : 0;
+  const int nall_w = (groups - wave + 3) >> 2 > 0 ? (groups - wave + 3) >> 2 : 0;
+  const int nb = nfull_w / U;                     // full batches of this wave
+
+  uint4 cq[2][U];
+  uint32_t sq[2][U], yq[2][U][MT];
+  float tq[2][U];
+  // iterations i0 .. i0 + U - 1 of this wave into register set S; `clamp`
+  // for iterations that may pass N (rows clamped per lane)
+  auto issue = [&](auto SET, int i0, bool clamp) {
+    constexpr int S = decltype(SET)::value;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint32_t g0 = (uint32_t)(64 * (wave + 4 * (i0 + u)));    // first row of the group
+      uint32_t row = g0 + (uint32_t)lane;
+      if (clamp) row = min(row, (uint32_t)N - 1u);
+      const uint32_t vc = (clamp ? row : (uint32_t)lane) * half_k + col0 / 2u;
+      const uint32_t vs = (clamp ? row : (uint32_t)lane) * scale_row + scale_col;
+      const uint32_t sc = clamp ? 0u : g0 * half_k, ss = clamp ? 0u : g0 * scale_row;
+      cq[S][u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rc, vc, sc, 0));
+      if constexpr (FMT == GNF4_NF4) sq[S][u] = __builtin_amdgcn_raw_buffer_load_b32(rs, vs, ss, 0);
+      else sq[S][u] = __builtin_amdgcn_raw_buffer_load_b8(rs, vs, ss, 0);
+      if constexpr (kDQ) {
+        const int64_t blk = (erow + row) * nkb + kb;
+        tq[S][u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                 rs2, (uint32_t)(blk >> 8) * 4u, 0, 0));
+      }
+#pragma unroll
+      for (int m = 0; m < MT; ++m)
+        yq[S][u][m] = __builtin_amdgcn_raw_buffer_load_b16(
+            rd, dyrow[m] + (clamp ? row : (uint32_t)lane) * 2u, clamp ? 0u : g0 * 2u, 0);
+    }
+  };
+
+  float acc[MT][32];
+#pragma unroll
+  for (int m = 0; m < MT; ++m)
+#pragma unroll
+    for (int j = 0; j < 32; ++j) acc[m][j] = 0.0f;
+  const uint32_t lane8 = (uint32_t)(lane & 31) * 8u;
+
+  auto consume = [&](auto SET, int i0, bool clamp) {
+    constexpr int S = decltype(SET)::value;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float sc;
+      if constexpr (FMT == GNF4_NF4) sc = __builtin_bit_cast(float, sq[S][u]);
+      else if constexpr (kDQ) sc = (float)(int8_t)sq[S][u] * tq[S][u];
+      else sc = e8m0_to_f32(sq[S][u]);
+      const int row = 64 * (wave + 4 * (i0 + u)) + lane;
+      const bool live = !clamp || (i0 + u < nall_w && row < N);
+      float sv[MT];
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        const float y = __builtin_bit_cast(float, yq[S][u][m] << 16);
+        if constexpr (kNF) sv[m] = live ? y * sc : 0.0f;
+        else sv[m] = live ? y : 0.0f;
+      }
+      const uint32_t wd[4] = {cq[S][u].x, cq[S][u].y, cq[S][u].z, cq[S][u].w};
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          float v0, v1;
+          if constexpr (kNF) {
+            const float2 pr = *reinterpret_cast<const float2 *>(
+                reinterpret_cast<const char *>(tab) +
+                __builtin_amdgcn_perm(wd[d], lane8, 0x0c0c0000u | ((4u + (uint32_t)b) << 8)));
+            v0 = pr.x;
+            v1 = pr.y;
+          } else {
+            typedef float f32x2_t __attribute__((ext_vector_type(2)));
+            f32x2_t pv;
+            if (b == 0) pv = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wd[d], sc, 0);
+            else if (b == 1) pv = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wd[d], sc, 1);
+            else if (b == 2) pv = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wd[d], sc, 2);
+            else pv = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wd[d], sc, 3);
+            v0 = pv[0];
+            v1 = pv[1];
+          }
+          const int j = 8 * d + 2 * b;           // columns j, j + 1 of the chunk
+#pragma unroll
+          for (int m = 0; m < MT; ++m) {
+            acc[m][j] = __builtin_fmaf(sv[m], v0, acc[m][j]);
+            acc[m][j + 1] = __builtin_fmaf(sv[m], v1, acc[m][j + 1]);
+          }
+        }
+      }
+    }
+  };
+
+  using Set0 = std::integral_constant<int, 0>;
+  using Set1 = std::integral_constant<int, 1>;
+  if (nb > 0) issue(Set0{}, 0, false);            // in flight while the table fills
+  if constexpr (kNF) fill_dx_table(tab, tid);
+  __syncthreads();
+  for (int b = 0; b < nb; b += 2) {
+    issue(Set1{}, U * min(b + 1, nb - 1), false);
+    consume(Set0{}, U * b, false);
+    if (b + 1 < nb) {
+      issue(Set0{}, U * min(b + 2, nb - 1), false);
+      consume(Set1{}, U * (b + 1), false);
+    }
+  }
+  for (int i0 = nb * U; i0 < nall_w; i0 += U) {
+    issue(Set0{}, i0, true);
+    consume(Set0{}, i0, true);
+  }
+
+  // reduce over the wave's 64 lanes: at mask d the lane keeps the half of its
+  // values selected by (lane & d) and adds the partner's copy of that half;
+  // values are ordered v = j * MT + m, so the halvings leave lanes 2j, 2j + 1
+  // with column j = (lane >> 1) & 31 of every row
+  float v[32 * MT];
+#pragma unroll
+  for (int j = 0; j < 32; ++j)
+#pragma unroll
+    for (int m = 0; m < MT; ++m) v[j * MT + m] = acc[m][j];
+  halve<16 * MT>(v, 32, lane);
+  halve<8 * MT>(v, 16, lane);
+  halve<4 * MT>(v, 8, lane);
+  halve<2 * MT>(v, 4, lane);
+  halve<MT>(v, 2, lane);
+#pragma unroll
+  for (int m = 0; m < MT; ++m) v[m] += __shfl_xor(v[m], 1, 64);
+  const int jc = (lane >> 1) & 31;
+  if ((lane & 1) == 0) {
+#pragma unroll
+    for (int m = 0; m < MT; ++m) red[wave][m][jc] = v[m];
+  }
+  __syncthreads();
+  // threads 0 .. 32 MT - 1: row m = tid / 32, column tid % 32, waves in order
+  if (tid < 32 * MT) {
+    const int m = tid >> 5, j = tid & 31;
+    const float sum = ((red[0][m][j] + red[1][m][j]) + red[2][m][j]) + red[3][m][j];
+    if (prow0 + m < count) a.dA[(int64_t)(seg0 + prow0 + m) * K + col0 + j] = sum;
+  }
+}
+
+template <int FMT, int MT>
+static hipError_t gemv_dx_go(const DxArgs &a, hipStream_t s) {
+  const int rows = a.rows;
+  const int nchunk = a.w.K / 32;
+  const int64_t items = ((int64_t)(rows + MT - 1) / MT + std::min<int>(a.w.E, rows)) * nchunk;
+  const int64_t grid = (items + 7) / 8 * 8;
+  hipLaunchKernelGGL((gemv_dx_kernel<FMT, MT>), dim3((unsigned)grid), dim3(kDxThreads), 0, s, a,
+                     (int)items);
+  return hipGetLastError();
 }
 
 template <int FMT, int RT>
@@ -352,10 +669,14 @@ template <int FMT>
 static hipError_t dx_pick(const DxArgs &a, hipStream_t s) {
   const int64_t experts = std::min<int64_t>(a.w.E, a.rows);
   const int64_t mean = experts > 0 ? (a.rows + experts - 1) / experts : 0;
+  if (a.rows <= kGemvDxMaxRows) {
+    if (mean <= 1) return gemv_dx_go<FMT, 1>(a, s);
+    if (mean <= 2) return gemv_dx_go<FMT, 2>(a, s);
+    if (mean <= 4) return gemv_dx_go<FMT, 4>(a, s);
+  }
   if (mean <= 16) return dx_go<FMT, 1>(a, s);
   if (mean <= 32) return dx_go<FMT, 2>(a, s);
-  if (mean <= 64) return dx_go<FMT, 4>(a, s);
-  return dx_go<FMT, 8>(a, s);
+  return dx_go<FMT, 4>(a, s);
 }
 
 hipError_t launch_gemm_dx(const DxArgs &a, hipStream_t s) {

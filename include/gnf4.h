@@ -164,7 +164,8 @@ gnf4_status gnf4_grouped_gemm_swiglu(const gnf4_weights *w, const uint16_t *X, i
  * For the gathered first projection the gradient of token t's activation row
  * is the sum over its k routed copies: gnf4_combine(dA, inv, ones, T, k, K).
  * Errors: INVALID_ARG for bad weights (as gnf4_grouped_gemm), k outside
- * [1, 64], T < 0, N % 8 != 0, NULL or misaligned pointers; T = 0 is a
+ * [1, 64], T < 0, N % 8 != 0, NULL or misaligned pointers; UNSUPPORTED when
+ * dY reaches 4 GiB (T*k*N*2 bytes, 32-bit buffer offsets); T = 0 is a
  * no-op. */
 gnf4_status gnf4_grouped_gemm_dx(const gnf4_weights *w, const uint16_t *dY,
                                  const int32_t *offsets, int32_t T, int32_t k, float *dA,

@@ -195,4 +195,7 @@ def test_gemm_dx_rejects(L):
     assert L.gnf4_grouped_gemm_dx(None, p, p, 2, 2, p, None) == INVALID
     bad = weights(fmt=2, K=48)
     assert L.gnf4_grouped_gemm_dx(ctypes.byref(bad), p, p, 2, 2, p, None) == INVALID
+    big = weights(N=65536, K=64)
+    assert L.gnf4_grouped_gemm_dx(ctypes.byref(big), p, p, 16384, 2, p, None) == 2        # 4 GiB dY
+    assert "4 GiB" in gnf4.last_error()
     assert L.gnf4_grouped_gemm_dx(ctypes.byref(w), None, None, 0, 2, None, None) == 0      # T = 0

@@ -49,10 +49,15 @@ CASES = [
     (8, 200, 320, 40, 2, True),        # N % 32 = 8 (short last step), K tail of 64 columns
     (8, 96, 256, 100, 2, False),       # ~25 rows per expert: 32-row tiles, duplicates
     (4, 128, 512, 100, 2, True),       # ~50 rows per expert: 64-row tiles
-    (6, 512, 1024, 300, 3, False),     # ~150 rows per expert: 128-row tiles, two per expert
+    (6, 512, 1024, 300, 3, False),     # ~150 rows per expert: 64-row tiles, three per expert
     (3, 96, 2880, 50, 2, True),        # K = 2880: eleven full K tiles and a 64-column tail
     (16, 72, 512, 20, 4, False),       # many experts, some empty
     (5, 1032, 128, 700, 1, True),      # K = 128 (half a tile), N = 32 * 32 + 8
+    # few routed rows (T*k <= 64): one wave per (expert, rows, 32 columns)
+    (64, 136, 2880, 8, 8, True),       # one row per item, K = 2880, N = 2 * 64 + 8
+    (32, 200, 320, 16, 4, False),      # two rows per item, duplicates span row blocks
+    (16, 96, 512, 12, 4, False),       # four rows per item
+    (3, 1032, 128, 2, 2, True),        # N = 1032: four full batches and a tail
 ]
 
 
