@@ -165,11 +165,13 @@ __device__ __forceinline__ void split_pair(float w0, float w1, uint32_t &hi, uin
 
 constexpr int kDxBufferDword3 = 0x00020000;   // raw buffer, 32-bit data format
 
-template <int FMT, int RT>
+template <int FMT, int RT, int CT>
 __global__ __launch_bounds__(kDxThreads, 2) void mfma_dx_kernel(DxArgs a, int n_tiles_k) {
   constexpr bool kNF = FMT != GNF4_MXFP4;
   constexpr bool kDQ = FMT == GNF4_NF4_DQ;
   constexpr int BM = 16 * RT;
+  static_assert(CT == 2 || CT == 4, "2 or 4 column tiles per wave");
+  constexpr int BN = 64 * CT;                     // columns per workgroup (16 CT per wave)
   constexpr int kChunks = BM * 4;                 // 16-byte dY chunks per step
   constexpr int kChunkLoads = (kChunks + kDxThreads - 1) / kDxThreads;
   __shared__ float tab[kNF ? kDxPairWords : 1];
@@ -197,8 +199,8 @@ __global__ __launch_bounds__(kDxThreads, 2) void mfma_dx_kernel(DxArgs a, int n_
   if constexpr (kNF) fill_dx_table(tab, tid);
 
   const int c = lane & 15, g = lane >> 4;
-  const int colbase = kt * 256 + wave * 64;
-  const int mycol = colbase + 4 * c;              // this lane's 4 output columns
+  const int colbase = kt * BN + wave * 16 * CT;
+  const int mycol = colbase + CT * c;             // this lane's CT output columns
   const bool col_ok = mycol < K;
   const uint32_t ldcol = col_ok ? (uint32_t)mycol : 0u;   // clamped for loads
   const uint32_t half_k = (uint32_t)K >> 1, nkb = (uint32_t)K >> 6, ngrp = (uint32_t)K >> 5;
@@ -262,7 +264,8 @@ __global__ __launch_bounds__(kDxThreads, 2) void mfma_dx_kernel(DxArgs a, int n_
         so_c = 0;
         so_s = 0;
       }
-      cw[S][i] = __builtin_amdgcn_raw_buffer_load_b16(rc, vc, so_c, 0);
+      if constexpr (CT == 4) cw[S][i] = __builtin_amdgcn_raw_buffer_load_b16(rc, vc, so_c, 0);
+      else cw[S][i] = __builtin_amdgcn_raw_buffer_load_b8(rc, vc, so_c, 0);
       if constexpr (FMT == GNF4_NF4) {
         sv[S][i] = __builtin_amdgcn_raw_buffer_load_b32(rs, vs, so_s, 0);
       } else {
@@ -293,11 +296,11 @@ __global__ __launch_bounds__(kDxThreads, 2) void mfma_dx_kernel(DxArgs a, int n_
     }
   };
 
-  f32x4_t acc[RT][4];
+  f32x4_t acc[RT][CT];
 #pragma unroll
   for (int r = 0; r < RT; ++r)
 #pragma unroll
-    for (int t = 0; t < 4; ++t) acc[r][t] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < CT; ++t) acc[r][t] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
 
   const uint32_t lane8 = (uint32_t)(lane & 31) * 8u;
   // B fragments of register set S for the step starting at n0, then the
@@ -318,50 +321,62 @@ __global__ __launch_bounds__(kDxThreads, 2) void mfma_dx_kernel(DxArgs a, int n_
       for (int i = 0; i < 8; ++i)
         if (n0 + 8 * g + i >= N) aw[i] = 0.0f;
     }
-    uint32_t bhi[4][4], blo[4][4];
+    uint32_t bhi[CT][4], blo[CT][4];
     {
-      float w[8][4];
+      float w[8][CT];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         if constexpr (kNF) {
           const float2 p0 = *reinterpret_cast<const float2 *>(
               reinterpret_cast<const char *>(tab) + __builtin_amdgcn_perm(cwv[i], lane8, 0x0c0c0400u));
-          const float2 p1 = *reinterpret_cast<const float2 *>(
-              reinterpret_cast<const char *>(tab) + __builtin_amdgcn_perm(cwv[i], lane8, 0x0c0c0500u));
           w[i][0] = p0.x * aw[i];
           w[i][1] = p0.y * aw[i];
-          w[i][2] = p1.x * aw[i];
-          w[i][3] = p1.y * aw[i];
+          if constexpr (CT == 4) {
+            const float2 p1 = *reinterpret_cast<const float2 *>(
+                reinterpret_cast<const char *>(tab) + __builtin_amdgcn_perm(cwv[i], lane8, 0x0c0c0500u));
+            w[i][2] = p1.x * aw[i];
+            w[i][3] = p1.y * aw[i];
+          }
         } else {
           typedef float f32x2_t __attribute__((ext_vector_type(2)));
           const f32x2_t v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cwv[i], aw[i], 0);
-          const f32x2_t v1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cwv[i], aw[i], 1);
           w[i][0] = v0[0];
           w[i][1] = v0[1];
-          w[i][2] = v1[0];
-          w[i][3] = v1[1];
+          if constexpr (CT == 4) {
+            const f32x2_t v1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cwv[i], aw[i], 1);
+            w[i][2] = v1[0];
+            w[i][3] = v1[1];
+          }
         }
       }
 #pragma unroll
-      for (int t = 0; t < 4; ++t)
+      for (int t = 0; t < CT; ++t)
 #pragma unroll
         for (int h = 0; h < 4; ++h) {
           if constexpr (kNF) split_pair(w[2 * h][t], w[2 * h + 1][t], bhi[t][h], blo[t][h]);
           else bhi[t][h] = pack_bf16_pair(w[2 * h][t], w[2 * h + 1][t]);
         }
     }
+    // all hi products, then all lo products: 4 RT independent MFMAs separate
+    // the two that update one accumulator
     return [&, bhi, blo, buf]() {
+      bf16x8_t af[RT];
 #pragma unroll
-      for (int r = 0; r < RT; ++r) {
-        const bf16x8_t af = __builtin_bit_cast(bf16x8_t, Ds[buf][dy_chunk(16 * r + c, g)]);
+      for (int r = 0; r < RT; ++r) af[r] = __builtin_bit_cast(bf16x8_t, Ds[buf][dy_chunk(16 * r + c, g)]);
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const bf16x8_t bh = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4 *>(bhi[t]));
-          acc[r][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bh, acc[r][t], 0, 0, 0);
-          if constexpr (kNF) {
-            const bf16x8_t bl = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4 *>(blo[t]));
-            acc[r][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bl, acc[r][t], 0, 0, 0);
-          }
+      for (int t = 0; t < CT; ++t) {
+        const bf16x8_t bh = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4 *>(bhi[t]));
+#pragma unroll
+        for (int r = 0; r < RT; ++r)
+          acc[r][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[r], bh, acc[r][t], 0, 0, 0);
+      }
+      if constexpr (kNF) {
+#pragma unroll
+        for (int t = 0; t < CT; ++t) {
+          const bf16x8_t bl = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4 *>(blo[t]));
+#pragma unroll
+          for (int r = 0; r < RT; ++r)
+            acc[r][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[r], bl, acc[r][t], 0, 0, 0);
         }
       }
     };
@@ -424,8 +439,11 @@ __global__ __launch_bounds__(kDxThreads, 2) void mfma_dx_kernel(DxArgs a, int n_
     for (int i = 0; i < 4; ++i) {
       const int lr = row0 + 16 * r + 4 * g + i;
       if (lr < count) {
-        const float4 o = make_float4(acc[r][0][i], acc[r][1][i], acc[r][2][i], acc[r][3][i]);
-        *reinterpret_cast<float4 *>(a.dA + (int64_t)(seg0 + lr) * K + mycol) = o;
+        float *dst = a.dA + (int64_t)(seg0 + lr) * K + mycol;
+        if constexpr (CT == 4)
+          *reinterpret_cast<float4 *>(dst) = make_float4(acc[r][0][i], acc[r][1][i], acc[r][2][i], acc[r][3][i]);
+        else
+          *reinterpret_cast<float2 *>(dst) = make_float2(acc[r][0][i], acc[r][1][i]);
       }
     }
 }
@@ -649,16 +667,16 @@ static hipError_t gemv_dx_go(const DxArgs &a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int FMT, int RT>
+template <int FMT, int RT, int CT>
 static hipError_t dx_go(const DxArgs &a, hipStream_t s) {
   constexpr int BM = 16 * RT;
   const int rows = a.rows;
-  const int n_tiles_k = (a.w.K + 255) / 256;
+  const int n_tiles_k = (a.w.K + 64 * CT - 1) / (64 * CT);
   const int64_t m_tiles = (rows + BM - 1) / BM + std::min<int>(a.w.E, rows);
   const int64_t bound = m_tiles * n_tiles_k;
   const int64_t grid = (bound + 7) / 8 * 8;
   if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL((mfma_dx_kernel<FMT, RT>), dim3((unsigned)grid), dim3(kDxThreads), 0, s, a,
+  hipLaunchKernelGGL((mfma_dx_kernel<FMT, RT, CT>), dim3((unsigned)grid), dim3(kDxThreads), 0, s, a,
                      n_tiles_k);
   return hipGetLastError();
 }
@@ -674,9 +692,10 @@ static hipError_t dx_pick(const DxArgs &a, hipStream_t s) {
     if (mean <= 2) return gemv_dx_go<FMT, 2>(a, s);
     if (mean <= 4) return gemv_dx_go<FMT, 4>(a, s);
   }
-  if (mean <= 16) return dx_go<FMT, 1>(a, s);
-  if (mean <= 32) return dx_go<FMT, 2>(a, s);
-  return dx_go<FMT, 4>(a, s);
+  if (mean <= 16) return dx_go<FMT, 1, 4>(a, s);
+  if (mean <= 32) return dx_go<FMT, 2, 4>(a, s);
+  if (mean <= 96) return dx_go<FMT, 4, 4>(a, s);
+  return dx_go<FMT, 8, 2>(a, s);
 }
 
 hipError_t launch_gemm_dx(const DxArgs &a, hipStream_t s) {

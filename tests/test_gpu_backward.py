@@ -53,6 +53,7 @@ CASES = [
     (3, 96, 2880, 50, 2, True),        # K = 2880: eleven full K tiles and a 64-column tail
     (16, 72, 512, 20, 4, False),       # many experts, some empty
     (5, 1032, 128, 700, 1, True),      # K = 128 (half a tile), N = 32 * 32 + 8
+    (4, 136, 640, 500, 1, True),       # ~125 rows per expert: 128-row tiles, 32 columns per wave
     # few routed rows (T*k <= 64): one wave per (expert, rows, 32 columns)
     (64, 136, 2880, 8, 8, True),       # one row per item, K = 2880, N = 2 * 64 + 8
     (32, 200, 320, 16, 4, False),      # two rows per item, duplicates span row blocks
@@ -70,11 +71,13 @@ def test_dx_matches_oracle(fmt, E, N, K, T, k, distinct):
     assert_within_dx(got[:nv], ref[:nv], "dx %s E=%d N=%d K=%d T=%d k=%d" % (fmt, E, N, K, T, k))
 
 
-def test_dx_mxfp4_half_block_tail():
-    """MXFP4 with K % 64 == 32: the last wave of the last K tile has only
-    lanes 0..7 (columns 0..31) in range."""
-    _, _, r_ref, got, ref = run_dx("mxfp4", 3, 64, 2912, 10, 2, 5)
-    assert_within_dx(got, ref, "dx mxfp4 K=2912")
+@pytest.mark.parametrize("T", [10, 400])
+def test_dx_mxfp4_half_block_tail(T):
+    """MXFP4 with K % 64 == 32: with 64-row tiles the last wave of the last K
+    tile has only lanes 0..7 (columns 0..31) in range; with 128-row tiles
+    (32 columns per wave) the last wave of the last tile is out of range."""
+    _, _, r_ref, got, ref = run_dx("mxfp4", 3, 64, 2912, T, 1 if T > 64 else 2, 5)
+    assert_within_dx(got, ref, "dx mxfp4 K=2912 T=%d" % T)
 
 
 @pytest.mark.parametrize("fmt", ["nf4", "mxfp4"])
