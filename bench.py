@@ -421,6 +421,15 @@ def time_kernel(torch, gnf4, slots, steps, warmup, launch=gate_up_launch):
     return float(np.median(ms)), float(byts), float(fl), G
 
 
+def dx_kernel_name(cfg, T):
+    """The HIP kernel gnf4_grouped_gemm_dx runs for this workload (the library
+    picks it from T*k and the mean rows per active expert)."""
+    rows = T * cfg.k
+    experts = min(cfg.E, rows)
+    mean = -(-rows // experts) if experts else 0
+    return "gemv_dx_kernel" if rows <= 64 and mean <= 4 else "mfma_dx_kernel"
+
+
 def gemm_kernel_name(cfg, T):
     """The HIP kernel gnf4_grouped_gemm runs for this workload's gate_up call
     (the library picks it from T*k and the format)."""
@@ -438,7 +447,7 @@ def profile_traffic(cfg_name, mode, kernel=None):
     import hashlib
     pattern = "%s-gate_up-%s-%s.txt" % (kernel or "*", cfg_name, mode)
     for path in sorted(glob.glob(os.path.join(ROOT, "profiles", pattern))):
-        if kernel is None and os.path.basename(path).startswith("mfma_dx_kernel"):
+        if kernel is None and "_dx_kernel" in os.path.basename(path):
             continue
         fields = {}
         for line in open(path):
@@ -740,10 +749,11 @@ def main():
             item = {"T": en["T"], "step_us": round(en["dt"] * 1e6, 2)}
             kt = en["kfl"] / (en["kms"] * 1e-3) / 1e12
             kg = en["kbytes"] / (en["kms"] * 1e-3) / 1e9
-            name = "mfma_dx_kernel (gate_up, T=%d)" % en["T"]
+            kname = dx_kernel_name(cfg, en["T"])
+            name = "%s (gate_up, T=%d)" % (kname, en["T"])
             if tag == "decode":
                 item["packed_GBps"] = round(en["byts"] / en["dt"] / 1e9, 2)
-                tr, tsrc = profile_traffic(cfg.name, "decode", "mfma_dx_kernel")
+                tr, tsrc = profile_traffic(cfg.name, "decode", kname)
                 item["roofline"] = {"bound": "hbm", "achieved": round(kg, 1), "peak": HBM_PEAK_GBS,
                                     "unit": "GB/s", "frac": round(kg / HBM_PEAK_GBS, 4),
                                     "traffic": tr, "traffic_unit": "HBM bytes/launch",
@@ -752,7 +762,7 @@ def main():
                                     "bytes_per_launch": int(en["kbytes"])}
             else:
                 item["tflops"] = round(en["fl"] / en["dt"] / 1e12, 2)
-                tr, tsrc = profile_traffic(cfg.name, "prefill", "mfma_dx_kernel")
+                tr, tsrc = profile_traffic(cfg.name, "prefill", kname)
                 item["roofline"] = {"bound": "mfma", "achieved": round(kt, 2), "peak": BF16_PEAK_TFLOPS,
                                     "unit": "TFLOP/s", "frac": round(kt / BF16_PEAK_TFLOPS, 4),
                                     "traffic": tr, "traffic_unit": "HBM bytes/launch",
