@@ -159,10 +159,18 @@ gnf4_status gnf4_swiglu(const float *Y, int32_t rows, int32_t I, uint16_t *H,
 
 // Shared by both GEMM entry points: validation, then the path chosen from
 // T*k (exactly one of Y / H is non-NULL).
+// Routing to run before the GEMM (gnf4_route_grouped_gemm): the ids and the
+// routing outputs; fused into the one-token GEMV when that path runs.
+struct FusedRoute {
+  const int32_t *ids;
+  int32_t *counts, *offsets, *perm, *inv, *active, *n_active, *bad;
+};
+
 static gnf4_status grouped_gemm_any(const gnf4_weights *w, const uint16_t *X, int32_t gather,
                                     const int32_t *offsets, const int32_t *perm,
                                     const int32_t *active, const int32_t *n_active, int32_t T,
-                                    int32_t k, float *Y, uint16_t *H, gnf4_stream_t stream) {
+                                    int32_t k, float *Y, uint16_t *H, gnf4_stream_t stream,
+                                    const FusedRoute *fr = nullptr) {
   gnf4_status st = check_weights(w);
   if (st != GNF4_OK) return st;
   if (gather != 0 && gather != 1) return fail(GNF4_ERR_INVALID_ARG, "gather must be 0 or 1");
@@ -177,7 +185,7 @@ static gnf4_status grouped_gemm_any(const gnf4_weights *w, const uint16_t *X, in
     return fail(GNF4_ERR_INVALID_ARG, "a pointer argument is NULL");
   if (!aligned16(X) || (Y && !aligned16(Y)) || (H && ((uintptr_t)H & 1u)))
     return fail(GNF4_ERR_INVALID_ARG, "X and Y must be 16-byte aligned, H 2-byte aligned");
-  GemmArgs a;
+  GemmArgs a{};
   a.w = to_kernel(w);
   a.X = X;
   a.gather = gather;
@@ -191,6 +199,22 @@ static gnf4_status grouped_gemm_any(const gnf4_weights *w, const uint16_t *X, in
   a.H = H;
   const int64_t rows = (int64_t)T * k;
   hipError_t e;
+  if (fr) {
+    if (T == 1 && gather == 1 && rows <= kGemvMaxRows && w->K <= kGemvMaxK) {
+      a.ids = fr->ids;                            // one launch: routing inside the GEMV
+      a.r_counts = fr->counts;
+      a.r_offsets = fr->offsets;
+      a.r_perm = fr->perm;
+      a.r_inv = fr->inv;
+      a.r_active = fr->active;
+      a.r_n_active = fr->n_active;
+      a.r_bad = fr->bad;
+      return device_status(launch_gemv(a, (hipStream_t)stream), "fused route + grouped GEMM launch");
+    }
+    e = launch_route(fr->ids, T, k, w->E, fr->counts, fr->offsets, fr->perm, fr->inv, fr->active,
+                     fr->n_active, fr->bad, (hipStream_t)stream);
+    if (e != hipSuccess) return device_status(e, "route launch");
+  }
   if (rows <= kGemvMaxRows && w->K <= kGemvMaxK)
     e = launch_gemv(a, (hipStream_t)stream);
   else if (w->K % 64 == 0)
@@ -210,6 +234,30 @@ gnf4_status gnf4_grouped_gemm(const gnf4_weights *w, const uint16_t *X, int32_t 
                               gnf4_stream_t stream) {
   if (!Y && T > 0) return fail(GNF4_ERR_INVALID_ARG, "a pointer argument is NULL");
   return grouped_gemm_any(w, X, gather, offsets, perm, active, n_active, T, k, Y, nullptr, stream);
+}
+
+gnf4_status gnf4_route_grouped_gemm(const int32_t *topk_ids, int32_t T, int32_t k,
+                                    int32_t *counts, int32_t *offsets, int32_t *perm, int32_t *inv,
+                                    int32_t *active, int32_t *n_active, int32_t *bad_id_flag,
+                                    const gnf4_weights *w, const uint16_t *X, float *Y, uint16_t *H,
+                                    gnf4_stream_t stream) {
+  gnf4_status st = check_weights(w);
+  if (st != GNF4_OK) return st;
+  if (k < 1 || k > 64) return fail(GNF4_ERR_INVALID_ARG, "k = %d outside [1, 64]", k);
+  if (T < 0) return fail(GNF4_ERR_INVALID_ARG, "T = %d is negative", T);
+  if ((int64_t)T * k >= ((int64_t)1 << 31) - 1024)
+    return fail(GNF4_ERR_INVALID_ARG, "T*k too large");
+  if (!counts || !offsets || !active || !n_active || !bad_id_flag)
+    return fail(GNF4_ERR_INVALID_ARG, "an output pointer is NULL");
+  if (T > 0 && (!topk_ids || !perm || !inv))
+    return fail(GNF4_ERR_INVALID_ARG, "topk_ids, perm or inv is NULL");
+  if (T > 0 && (Y == nullptr) == (H == nullptr))
+    return fail(GNF4_ERR_INVALID_ARG, "exactly one of Y and H must be given");
+  if (T == 0)                                     // routing of nothing: counts, offsets, flags
+    return gnf4_route(topk_ids, T, k, w->E, counts, offsets, perm, inv, active, n_active,
+                      bad_id_flag, stream);
+  const FusedRoute fr = {topk_ids, counts, offsets, perm, inv, active, n_active, bad_id_flag};
+  return grouped_gemm_any(w, X, 1, offsets, perm, active, n_active, T, k, Y, H, stream, &fr);
 }
 
 gnf4_status gnf4_grouped_gemm_swiglu(const gnf4_weights *w, const uint16_t *X, int32_t gather,

@@ -55,6 +55,11 @@ struct GemmArgs {
   int32_t T, k;
   float *Y;          // float32 output [T*k][N] (plain GEMM)
   uint16_t *H;       // bf16 output [T*k][N/2] (SwiGLU epilogue; then Y is unused)
+  // Routing fused into the one-token GEMV: the token's k ids and where the
+  // routing outputs go (as gnf4_route writes them); ids == NULL when the
+  // routing was done beforehand (offsets / active / n_active are read).
+  const int32_t *ids;
+  int32_t *r_counts, *r_offsets, *r_perm, *r_inv, *r_active, *r_n_active, *r_bad;
 };
 
 // Input gradient of the grouped GEMM: dA [rows][K] from dY [rows][N], both

@@ -436,7 +436,81 @@ __global__ __launch_bounds__(kThreads, 2) void gemv1_kernel(GemmArgs a, int L_lo
 // range, read once: one token has at most 64 slots.
 constexpr int kGemvWaveThreads = 1024;
 
-template <int FMT, int C, int U, bool GLU>
+// Routing of one token's k <= 64 assignments, from the ids alone, computed
+// by wave 0 of every workgroup of the fused one-token GEMV; the same result
+// as gnf4_route. Lane j holds id e_j. With one ballot per id bit, most
+// significant first, each lane finds the valid lanes with the same id (eq)
+// and with a smaller id (lt); its stable position is |lt| + |eq below j|,
+// the first lane of each id leads its slot, and slot s (experts ascending)
+// is led by the lane with |lt & leaders| = s. Slot s's expert, first routed
+// row and row count go to LDS for every wave; workgroup 0 also writes the
+// routing outputs (counts, offsets, active, perm, inv, n_active, bad).
+struct OneTokenRoute {
+  int exp[64], seg[64], cnt[64];
+  int nact, total;
+};
+
+__device__ __forceinline__ void route_one_token(const GemmArgs &a, OneTokenRoute &sr, int tid) {
+  const int lane = tid & 63, k = a.k, E = a.w.E;
+  if (tid < 64) {
+    const int e = lane < k ? a.ids[lane] : -1;
+    const bool valid = lane < k && (unsigned)e < (unsigned)E;
+    const uint64_t vmask = __ballot(valid);
+    uint64_t eq = vmask, lt = 0;
+    for (int b = 31 - __builtin_clz((unsigned)max(E - 1, 1)); b >= 0; --b) {
+      const bool bit = (e >> b) & 1;
+      const uint64_t B = __ballot(valid && bit);
+      if (bit) {
+        lt |= eq & ~B;
+        eq &= B;
+      } else {
+        eq &= ~B;
+      }
+    }
+    const uint64_t lower = lane ? (~0ull >> (64 - lane)) : 0ull;
+    const bool leader = valid && (eq & lower) == 0;
+    const uint64_t lmask = __ballot(leader);
+    const int pos = __popcll(lt) + __popcll(eq & lower);
+    const int nact = __popcll(lmask), total = __popcll(vmask);
+    if (leader) {
+      const int slot = __popcll(lt & lmask);
+      sr.exp[slot] = e;
+      sr.seg[slot] = pos;
+      sr.cnt[slot] = __popcll(eq);
+    }
+    if (lane == 0) {
+      sr.nact = nact;
+      sr.total = total;
+    }
+    if (blockIdx.x == 0 && lane < k) {
+      a.r_inv[lane] = valid ? pos : -1;
+      if (valid) a.r_perm[pos] = lane;
+      if (lane >= total) a.r_perm[lane] = -1;
+      if (lane == 0) {
+        a.r_n_active[0] = nact;
+        a.r_bad[0] = total != k ? 1 : 0;
+      }
+    }
+  }
+  __syncthreads();
+  if (blockIdx.x == 0) {
+    const int nact = sr.nact;
+    for (int e = tid; e < E; e += kGemvWaveThreads) {
+      int off = 0, c = 0;
+      for (int s = 0; s < nact; ++s) {
+        const int es = sr.exp[s];
+        if (es < e) off += sr.cnt[s];
+        if (es == e) c = sr.cnt[s];
+      }
+      a.r_counts[e] = c;
+      a.r_offsets[e] = off;
+      if (e == E - 1) a.r_offsets[E] = off + c;
+      a.r_active[e] = e < nact ? sr.exp[e] : -1;
+    }
+  }
+}
+
+template <int FMT, int C, int U, bool GLU, bool ROUTE>
 __global__ __launch_bounds__(kGemvWaveThreads, 1) void gemv1w_kernel(GemmArgs a, int L_log2,
                                                                      int items_per_expert,
                                                                      int max_slots) {
@@ -444,6 +518,7 @@ __global__ __launch_bounds__(kGemvWaveThreads, 1) void gemv1w_kernel(GemmArgs a,
   constexpr bool kLut = FMT != GNF4_MXFP4;
   constexpr int kWaves = kGemvWaveThreads / 64;
   __shared__ uint32_t lut[kLut ? kLutWords : 1];
+  __shared__ OneTokenRoute sr;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const uint32_t lane4 = (uint32_t)lane << 2;
@@ -460,14 +535,25 @@ __global__ __launch_bounds__(kGemvWaveThreads, 1) void gemv1w_kernel(GemmArgs a,
   g.rows_per_item = g.RW * (GLU ? U / 2 : U);
   const int ipe = items_per_expert;
 
-  const int nact = *a.n_active;
-  const int ej = a.active[min(lane, max_slots - 1)];   // slot lane's expert (lanes past: unused)
+  int nact, ej, pj0, pj1;                        // slot lane's expert and routed rows
   uint32_t x[1][C][16];
   gemv_load_x_row<C>(a, g, 0, x);
   if constexpr (kLut) fill_nf4_lut<kGemvWaveThreads>(lut, tid);
-  const int ejc = max(ej, 0);
-  const int pj0 = a.offsets[ejc], pj1 = a.offsets[ejc + 1];
-  __syncthreads();                              // decode table written
+  if constexpr (ROUTE) {
+    route_one_token(a, sr, tid);                  // ends with a barrier: table written too
+    nact = sr.nact;
+    const int sl = min(lane, 63);
+    ej = lane < nact ? sr.exp[sl] : -1;
+    pj0 = lane < nact ? sr.seg[sl] : 0;
+    pj1 = lane < nact ? sr.seg[sl] + sr.cnt[sl] : 0;
+  } else {
+    nact = *a.n_active;
+    ej = a.active[min(lane, max_slots - 1)];     // lanes past the active slots: unused
+    const int ejc = max(ej, 0);
+    pj0 = a.offsets[ejc];
+    pj1 = a.offsets[ejc + 1];
+    __syncthreads();                              // decode table written
+  }
 
   const int total = nact * ipe;
   const int W = (int)gridDim.x * kWaves;
@@ -918,12 +1004,12 @@ static int out_cols(const GemmArgs &a) { return a.H ? a.w.N / 2 : a.w.N; }
 
 // One token, gathered input: the persistent kernel, one workgroup per CU (or
 // as many as are resident at once).
-template <int FMT, int C, int U, bool GLU>
+template <int FMT, int C, int U, bool GLU, bool ROUTE>
 static hipError_t gemv1w_go(const GemmArgs &a, int L_log2, int max_slots, hipStream_t s) {
   static int per_cu = 0;
   if (per_cu == 0) {
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gemv1w_kernel<FMT, C, U, GLU>,
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gemv1w_kernel<FMT, C, U, GLU, ROUTE>,
                                                      kGemvWaveThreads, 0) != hipSuccess || n < 1)
       n = 1;
     per_cu = n;
@@ -933,7 +1019,7 @@ static hipError_t gemv1w_go(const GemmArgs &a, int L_log2, int max_slots, hipStr
   const int64_t waves = (int64_t)max_slots * items;
   const int64_t grid = std::min<int64_t>((int64_t)per_cu * device_cu_count(),
                                          (waves + kGemvWaveThreads / 64 - 1) / (kGemvWaveThreads / 64));
-  hipLaunchKernelGGL((gemv1w_kernel<FMT, C, U, GLU>), dim3((unsigned)grid),
+  hipLaunchKernelGGL((gemv1w_kernel<FMT, C, U, GLU, ROUTE>), dim3((unsigned)grid),
                      dim3(kGemvWaveThreads), 0, s, a, L_log2, items, max_slots);
   return hipGetLastError();
 }
@@ -1044,18 +1130,27 @@ static int gemv_pick_u(const GemvVariant &v, int fmt, int cols, int L_log2, int 
 // Rows per wave slot of the one-token gathered kernel for C chunks per lane
 // (measured fastest on the workload shapes, and free of register spills).
 // The SwiGLU epilogue needs an even U (slot u pairs with u + U/2).
-template <int FMT, bool GLU>
+template <int FMT, bool GLU, bool ROUTE>
 static hipError_t gemv1w_dispatch(const GemmArgs &a, int C, int L_log2, int max_slots,
                                   hipStream_t s) {
   switch (C) {
-    case 1: return gemv1w_go<FMT, 1, 4, GLU>(a, L_log2, max_slots, s);
-    case 2: return gemv1w_go<FMT, 2, 4, GLU>(a, L_log2, max_slots, s);
-    case 3: return gemv1w_go<FMT, 3, 2, GLU>(a, L_log2, max_slots, s);
+    case 1: return gemv1w_go<FMT, 1, 4, GLU, ROUTE>(a, L_log2, max_slots, s);
+    case 2: return gemv1w_go<FMT, 2, 4, GLU, ROUTE>(a, L_log2, max_slots, s);
+    case 3: return gemv1w_go<FMT, 3, 2, GLU, ROUTE>(a, L_log2, max_slots, s);
     case 4:
-      if constexpr (FMT != GNF4_MXFP4 && !GLU) return gemv1w_go<FMT, 4, 1, GLU>(a, L_log2, max_slots, s);
-      else return gemv1w_go<FMT, 4, 2, GLU>(a, L_log2, max_slots, s);
+      if constexpr (FMT != GNF4_MXFP4 && !GLU) return gemv1w_go<FMT, 4, 1, GLU, ROUTE>(a, L_log2, max_slots, s);
+      else return gemv1w_go<FMT, 4, 2, GLU, ROUTE>(a, L_log2, max_slots, s);
     default: return hipErrorInvalidValue;
   }
+}
+
+template <int FMT>
+static hipError_t gemv1w_any(const GemmArgs &a, int C, int L_log2, int max_slots, hipStream_t s) {
+  const bool glu = a.H != nullptr, route = a.ids != nullptr;
+  if (glu) return route ? gemv1w_dispatch<FMT, true, true>(a, C, L_log2, max_slots, s)
+                        : gemv1w_dispatch<FMT, true, false>(a, C, L_log2, max_slots, s);
+  return route ? gemv1w_dispatch<FMT, false, true>(a, C, L_log2, max_slots, s)
+               : gemv1w_dispatch<FMT, false, false>(a, C, L_log2, max_slots, s);
 }
 
 hipError_t launch_gemv(const GemmArgs &a, hipStream_t s) {
@@ -1063,17 +1158,13 @@ hipError_t launch_gemv(const GemmArgs &a, hipStream_t s) {
     int L_log2 = 6, C = 1;
     if (!gemv_shape(a.w.K, 1, &L_log2, &C)) return hipErrorInvalidValue;
     const int max_slots = std::min<int>(a.w.E, a.k);
-    const bool glu = a.H != nullptr;
     switch (a.w.format) {
       case GNF4_NF4:
-        return glu ? gemv1w_dispatch<GNF4_NF4, true>(a, C, L_log2, max_slots, s)
-                   : gemv1w_dispatch<GNF4_NF4, false>(a, C, L_log2, max_slots, s);
+        return gemv1w_any<GNF4_NF4>(a, C, L_log2, max_slots, s);
       case GNF4_NF4_DQ:
-        return glu ? gemv1w_dispatch<GNF4_NF4_DQ, true>(a, C, L_log2, max_slots, s)
-                   : gemv1w_dispatch<GNF4_NF4_DQ, false>(a, C, L_log2, max_slots, s);
+        return gemv1w_any<GNF4_NF4_DQ>(a, C, L_log2, max_slots, s);
       default:
-        return glu ? gemv1w_dispatch<GNF4_MXFP4, true>(a, C, L_log2, max_slots, s)
-                   : gemv1w_dispatch<GNF4_MXFP4, false>(a, C, L_log2, max_slots, s);
+        return gemv1w_any<GNF4_MXFP4>(a, C, L_log2, max_slots, s);
     }
   }
   int MT = gemv_tokens(a.T);

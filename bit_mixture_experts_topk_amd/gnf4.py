@@ -24,7 +24,8 @@ FORMATS = {"nf4": NF4, "nf4_dq": NF4_DQ, "mxfp4": MXFP4}
 STATUS = {0: "OK", 1: "INVALID_ARG", 2: "UNSUPPORTED", 4: "DEVICE"}
 
 # Every entry point declared in include/gnf4.h.
-EXPORTS = ("gnf4_route", "gnf4_route_logits", "gnf4_grouped_gemm", "gnf4_grouped_gemm_swiglu",
+EXPORTS = ("gnf4_route", "gnf4_route_logits", "gnf4_route_grouped_gemm", "gnf4_grouped_gemm",
+           "gnf4_grouped_gemm_swiglu",
            "gnf4_grouped_gemm_dx", "gnf4_swiglu", "gnf4_combine",
            "gnf4_dequant", "gnf4_dequant_experts_bf16", "gnf4_quantize", "gnf4_nf4_codebook",
            "gnf4_last_error",
@@ -59,6 +60,8 @@ def lib():
         L.gnf4_swiglu.argtypes = [P, I, I, P, S]
         L.gnf4_grouped_gemm.argtypes = [ctypes.POINTER(CWeights), P, I, P, P, P, P, I, I, P, S]
         L.gnf4_grouped_gemm_swiglu.argtypes = [ctypes.POINTER(CWeights), P, I, P, P, P, P, I, I, P, S]
+        L.gnf4_route_grouped_gemm.argtypes = [P, I, I, P, P, P, P, P, P, P,
+                                              ctypes.POINTER(CWeights), P, P, P, S]
         L.gnf4_grouped_gemm_dx.argtypes = [ctypes.POINTER(CWeights), P, P, I, I, P, S]
         L.gnf4_combine.argtypes = [P, P, P, I, I, I, P, S]
         L.gnf4_dequant.argtypes = [ctypes.POINTER(CWeights), I, P, S]
@@ -189,6 +192,34 @@ def route(topk_ids, E, out=None):
     r["perm"] = r["perm"][:T * k]
     r["inv"] = r["inv"][:T * k]
     return r
+
+
+def route_grouped_gemm(topk_ids, w, X, out=None, Y=None, H=None, swiglu=False):
+    """route() then grouped_gemm(gather=1) (or grouped_gemm_swiglu when
+    swiglu), one launch for a single token; returns (route dict, Y or H)."""
+    _dev(topk_ids, torch.int32, "topk_ids")
+    if not (X.is_cuda and X.is_contiguous() and X.element_size() == 2):
+        raise ValueError("X must be a contiguous bf16 (or 16-bit bit pattern) CUDA tensor")
+    T, k = topk_ids.shape
+    r = dict(out) if out is not None else route_buffers(T, k, w.E, topk_ids.device)
+    if swiglu:
+        if H is None:
+            H = torch.empty((max(T * k, 1), w.N // 2), dtype=torch.int16, device=X.device)
+        res = H
+    else:
+        if Y is None:
+            Y = torch.empty((max(T * k, 1), w.N), dtype=torch.float32, device=X.device)
+        res = Y
+    cw = w.cstruct()
+    _check(lib().gnf4_route_grouped_gemm(_ptr(topk_ids), T, k, _ptr(r["counts"]), _ptr(r["offsets"]),
+                                         _ptr(r["perm"]), _ptr(r["inv"]), _ptr(r["active"]),
+                                         _ptr(r["n_active"]), _ptr(r["bad"]), ctypes.byref(cw),
+                                         _ptr(X), None if swiglu else _ptr(Y),
+                                         _ptr(H) if swiglu else None, _stream()),
+           "gnf4_route_grouped_gemm")
+    r["perm"] = r["perm"][:T * k]
+    r["inv"] = r["inv"][:T * k]
+    return r, res
 
 
 def route_logits(logits, k, out=None):

@@ -13,7 +13,8 @@
  *   gnf4_route          top-k expert ids -> per-expert row segments
  *   gnf4_grouped_gemm   Y[p] = A[p] . W[expert(p)]^T for every routed row p
  *   gnf4_combine        out[t] = sum_j w[t,j] * Y[inv[t*k+j]]
- * and a whole FFN layer adds the steps either side of the GEMM:
+ * (gnf4_route_grouped_gemm runs the first two as one call, one launch for a
+ * single token) and a whole FFN layer adds the steps either side of the GEMM:
  *   gnf4_route_logits   router logits -> top-k ids and weights, then route
  *   gnf4_grouped_gemm_swiglu   gate_up projection (gathered token rows)
  *                       with H = silu(gate) * up, bf16, as its epilogue
@@ -129,6 +130,28 @@ gnf4_status gnf4_grouped_gemm(const gnf4_weights *w, const uint16_t *X, int32_t 
                               const int32_t *offsets, const int32_t *perm,
                               const int32_t *active, const int32_t *n_active,
                               int32_t T, int32_t k, float *Y, gnf4_stream_t stream);
+
+/* gnf4_route_grouped_gemm -- gnf4_route followed by the first projection
+ * (rows gathered from the token activations, gather = 1), as one call:
+ *   gnf4_route(topk_ids, T, k, w->E, counts, ..., bad_id_flag)
+ *   gnf4_grouped_gemm(w, X, 1, offsets, perm, active, n_active, T, k, Y)
+ * or, with H given instead of Y, gnf4_grouped_gemm_swiglu. Every output
+ * (the routing arrays and Y or H) is bit-identical to those two calls. For
+ * a single token (T == 1, the decode step) it is one launch: each
+ * workgroup of the one-token GEMV derives the routing from the k ids and
+ * the first workgroup writes the routing outputs, which saves a launch and
+ * a dependent round trip per layer step (the pages put per-token time at
+ * bytes over bandwidth plus a fixed cost: Jordan Anderson,
+ * jordananderson-pages.pages.dev, section "grouped-nf4-gemm &
+ * experts-4bit", demonstration paragraph of the first bullet). Otherwise
+ * the two launches of the separate calls. Exactly one of Y, H is non-NULL
+ * (for T > 0). Arguments, limits and errors as the two calls. */
+gnf4_status gnf4_route_grouped_gemm(const int32_t *topk_ids, int32_t T, int32_t k,
+                                    int32_t *counts, int32_t *offsets, int32_t *perm,
+                                    int32_t *inv, int32_t *active, int32_t *n_active,
+                                    int32_t *bad_id_flag, const gnf4_weights *w,
+                                    const uint16_t *X, float *Y, uint16_t *H,
+                                    gnf4_stream_t stream);
 
 /* gnf4_grouped_gemm_swiglu -- the first projection with the SwiGLU step as
  * its epilogue: for every routed row p and i < N/2,

@@ -1,0 +1,67 @@
+"""The fused entry points of the decode step give what the separate calls
+give: gnf4_route_grouped_gemm equals gnf4_route followed by the first
+projection (routing arrays and Y or H bit for bit), on the one-launch path
+(T = 1) and on the two-launch path (T > 1)."""
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+
+from .gpu_util import bits_to_device, gnf4, oracle_pack, packed_to_device, say
+
+pytestmark = pytest.mark.gpu
+
+
+def same_route(r_a, r_b, n):
+    for key in ("counts", "offsets", "active", "n_active", "bad"):
+        a, b = r_a[key].cpu().numpy(), r_b[key].cpu().numpy()
+        assert np.array_equal(a, b), (key, a, b)
+    if n:
+        for key in ("perm", "inv"):
+            a, b = r_a[key].cpu().numpy()[:n], r_b[key].cpu().numpy()[:n]
+            assert np.array_equal(a, b), (key, a, b)
+
+
+@pytest.mark.parametrize("fmt", ["nf4", "nf4_dq", "mxfp4"])
+@pytest.mark.parametrize("swiglu", [False, True])
+@pytest.mark.parametrize("E,N,K,T,k,ids_kind", [
+    (8, 256, 256, 1, 2, "distinct"),
+    (64, 512, 2048, 1, 8, "distinct"),
+    (16, 128, 512, 1, 6, "duplicates"),
+    (16, 128, 512, 1, 6, "bad"),          # out-of-range ids: dropped, flag raised
+    (128, 96, 2880, 1, 4, "distinct"),    # K = 2880
+    (1024, 64, 256, 1, 64, "distinct"),   # E = 1024, k = 64
+    (3, 64, 256, 1, 1, "distinct"),       # k = 1
+    (8, 256, 256, 5, 2, "duplicates"),    # T > 1: two launches
+])
+def test_route_grouped_gemm_equals_separate_calls(fmt, swiglu, E, N, K, T, k, ids_kind):
+    g = gnf4()
+    if fmt == "mxfp4" and K % 32:
+        pytest.skip("MXFP4 needs K % 32 == 0")
+    case = synth.small_layer(E, N, K, T, k, seed=8, distinct=(ids_kind == "distinct"), gather=1)
+    ids = case["ids"].copy()
+    if ids_kind == "bad":
+        ids[0, 1] = E + 5
+        ids[0, 3] = -2
+    codes, scales, scales2 = oracle_pack(fmt, case["W"])
+    pw = packed_to_device(g, fmt, codes, scales, scales2, E, N, K)
+    X = bits_to_device(case["X"])
+    ids_d = torch.from_numpy(ids).cuda()
+    say("route_grouped_gemm", fmt, "swiglu", swiglu, E, N, K, T, k, ids_kind)
+    r_ref = g.route(ids_d, E)
+    if swiglu:
+        ref = g.grouped_gemm_swiglu(pw, X, 1, r_ref, T, k)
+    else:
+        ref = g.grouped_gemm(pw, X, 1, r_ref, T, k)
+    r, got = g.route_grouped_gemm(ids_d, pw, X, swiglu=swiglu)
+    torch.cuda.synchronize()
+    same_route(r, r_ref, T * k)
+    nv = int(r_ref["offsets"][-1].item())
+    a = got.cpu().numpy()[:nv]
+    b = ref.cpu().numpy()[:nv]
+    assert np.array_equal(a.view(np.uint32) if a.dtype == np.float32 else a,
+                          b.view(np.uint32) if b.dtype == np.float32 else b), "outputs differ"
+    if ids_kind == "bad":
+        assert int(r["bad"].item()) == 1 and nv == T * k - 2
