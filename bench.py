@@ -94,9 +94,12 @@ def kernel_only(args):
         dY = torch.from_numpy(synth.grad_rows(cfg, T * cfg.k, proj.N, 0, T).view(np.int16)).cuda()
         dA = torch.empty((T * cfg.k, proj.K), dtype=torch.float32, device="cuda")
     torch.cuda.synchronize()
+    ids_d = torch.from_numpy(ids).cuda()
     for _ in range(args.steps):
         if args.dx:
             gnf4.grouped_gemm_dx(pw, dY, r, T, cfg.k, dA)
+        elif T == 1 and proj.gather:              # as the decode step runs it: routing fused in
+            gnf4.route_grouped_gemm(ids_d, pw, X, out=r, Y=Y)
         else:
             gnf4.grouped_gemm(pw, X, proj.gather, r, T, cfg.k, Y)
     if args.calib_copy:
@@ -192,16 +195,17 @@ class StepSlot:
         if self.ffn:
             r = gnf4.route_logits(self.logits, k, out=self.r)
             gnf4.grouped_gemm_swiglu(self.layer.projs[0], self.X, 1, r, T, k, self.H)
-            gnf4.grouped_gemm(self.layer.projs[1], self.H, 0, r, T, k, self.Y[1])
-            gnf4.combine(self.Y[1], r["inv"], r["topk_w"], T, k, self.out)
+            gnf4.grouped_gemm_combine(self.layer.projs[1], self.H, r, r["topk_w"], T, k, self.out,
+                                      Y=self.Y[1])
             return
-        r = gnf4.route(self.ids, cfg.E, out=self.r)
-        gnf4.grouped_gemm(self.layer.projs[0], self.X, 1, r, T, k, self.Y[0])
-        last = self.Y[0]
+        # route + first projection, second projection + combine: one launch
+        # each for a single token (the separate calls otherwise)
+        r, _ = gnf4.route_grouped_gemm(self.ids, self.layer.projs[0], self.X, out=self.r, Y=self.Y[0])
         if len(self.layer.projs) > 1:
-            gnf4.grouped_gemm(self.layer.projs[1], self.Xd, 0, r, T, k, self.Y[1])
-            last = self.Y[1]
-        gnf4.combine(last, r["inv"], self.tw, T, k, self.out)
+            gnf4.grouped_gemm_combine(self.layer.projs[1], self.Xd, r, self.tw, T, k, self.out,
+                                      Y=self.Y[1])
+        else:
+            gnf4.combine(self.Y[0], r["inv"], self.tw, T, k, self.out)
 
     def capture(self, torch, gnf4):
         s = torch.cuda.Stream()
@@ -370,8 +374,12 @@ def time_steps(torch, slots, chain, steps, warmup):
 
 
 def gate_up_launch(gnf4, sl):
+    """The gate_up launch of the step: with the routing fused in at T = 1."""
     cfg = sl.layer.cfg
-    gnf4.grouped_gemm(sl.layer.projs[0], sl.X, 1, sl.r, sl.T, cfg.k, sl.Y[0])
+    if sl.T == 1:
+        gnf4.route_grouped_gemm(sl.ids, sl.layer.projs[0], sl.X, out=sl.r, Y=sl.Y[0])
+    else:
+        gnf4.grouped_gemm(sl.layer.projs[0], sl.X, 1, sl.r, sl.T, cfg.k, sl.Y[0])
 
 
 def gate_up_dx_launch(gnf4, sl):

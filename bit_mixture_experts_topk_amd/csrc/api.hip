@@ -293,6 +293,43 @@ gnf4_status gnf4_grouped_gemm_dx(const gnf4_weights *w, const uint16_t *dY,
   return device_status(launch_gemm_dx(a, (hipStream_t)stream), "grouped GEMM dx launch");
 }
 
+gnf4_status gnf4_grouped_gemm_combine(const gnf4_weights *w, const uint16_t *X,
+                                      const int32_t *offsets, const int32_t *perm,
+                                      const int32_t *inv, const int32_t *active,
+                                      const int32_t *n_active, const float *topk_w, int32_t T,
+                                      int32_t k, float *Y, float *out, gnf4_stream_t stream) {
+  gnf4_status st = check_weights(w);
+  if (st != GNF4_OK) return st;
+  if (k < 1 || k > 64) return fail(GNF4_ERR_INVALID_ARG, "k = %d outside [1, 64]", k);
+  if (T < 0) return fail(GNF4_ERR_INVALID_ARG, "T = %d is negative", T);
+  if ((int64_t)T * k >= ((int64_t)1 << 31) - 1024)
+    return fail(GNF4_ERR_INVALID_ARG, "T*k too large");
+  if (w->N % 4) return fail(GNF4_ERR_INVALID_ARG, "N = %d must be a multiple of 4", w->N);
+  if (T == 0) return ok();
+  if (!X || !offsets || !perm || !inv || !active || !n_active || !topk_w || !out)
+    return fail(GNF4_ERR_INVALID_ARG, "a pointer argument is NULL");
+  if (!aligned16(X) || !aligned16(out))
+    return fail(GNF4_ERR_INVALID_ARG, "X and out must be 16-byte aligned");
+  GemmArgs a{};
+  a.w = to_kernel(w);
+  a.X = X;
+  a.gather = 0;
+  a.offsets = offsets;
+  a.perm = perm;
+  a.active = active;
+  a.n_active = n_active;
+  a.T = T;
+  a.k = k;
+  if (gemv_combine_fits(a))
+    return device_status(launch_gemv_combine(a, topk_w, inv, out, (hipStream_t)stream),
+                         "grouped GEMM + combine launch");
+  if (!Y) return fail(GNF4_ERR_INVALID_ARG, "Y (scratch for T*k rows) is NULL and T > 1");
+  st = grouped_gemm_any(w, X, 0, offsets, perm, active, n_active, T, k, Y, nullptr, stream);
+  if (st != GNF4_OK) return st;
+  return device_status(launch_combine(Y, inv, topk_w, T, k, w->N, out, (hipStream_t)stream),
+                       "combine launch");
+}
+
 gnf4_status gnf4_combine(const float *Y, const int32_t *inv, const float *topk_w, int32_t T,
                          int32_t k, int32_t N, float *out, gnf4_stream_t stream) {
   if (k < 1 || k > 64) return fail(GNF4_ERR_INVALID_ARG, "k = %d outside [1, 64]", k);

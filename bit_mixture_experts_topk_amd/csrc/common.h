@@ -220,6 +220,11 @@ hipError_t launch_swiglu(const float *Y, int32_t rows, int32_t I, uint16_t *H, h
 hipError_t launch_gemv(const GemmArgs &a, hipStream_t s);
 hipError_t launch_mfma(const GemmArgs &a, hipStream_t s);
 hipError_t launch_gemm_dx(const DxArgs &a, hipStream_t s);
+// One token's second projection with the combine fused (T = 1, routed-order
+// rows); gemv_combine_fits says whether that kernel takes the call.
+bool gemv_combine_fits(const GemmArgs &a);
+hipError_t launch_gemv_combine(const GemmArgs &a, const float *topk_w, const int32_t *inv,
+                               float *out, hipStream_t s);
 hipError_t launch_combine(const float *Y, const int32_t *inv, const float *w, int32_t T,
                           int32_t k, int32_t N, float *out, hipStream_t s);
 hipError_t launch_dequant(const Weights &w, int32_t e, float *out, hipStream_t s);

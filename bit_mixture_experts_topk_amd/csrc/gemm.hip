@@ -443,8 +443,9 @@ constexpr int kGemvWaveThreads = 1024;
 // and with a smaller id (lt); its stable position is |lt| + |eq below j|,
 // the first lane of each id leads its slot, and slot s (experts ascending)
 // is led by the lane with |lt & leaders| = s. Slot s's expert, first routed
-// row and row count go to LDS for every wave; workgroup 0 also writes the
-// routing outputs (counts, offsets, active, perm, inv, n_active, bad).
+// row and row count go to LDS for every wave; workgroup 0 writes perm, inv,
+// n_active and bad, and the per-expert arrays (counts, offsets, active) are
+// written 64 experts per workgroup.
 struct OneTokenRoute {
   int exp[64], seg[64], cnt[64];
   int nact, total;
@@ -493,9 +494,10 @@ __device__ __forceinline__ void route_one_token(const GemmArgs &a, OneTokenRoute
     }
   }
   __syncthreads();
-  if (blockIdx.x == 0) {
+  // the per-expert arrays, 64 experts per workgroup in turn
+  if (tid < 64) {
     const int nact = sr.nact;
-    for (int e = tid; e < E; e += kGemvWaveThreads) {
+    for (int e = (int)blockIdx.x * 64 + tid; e < E; e += (int)gridDim.x * 64) {
       int off = 0, c = 0;
       for (int s = 0; s < nact; ++s) {
         const int es = sr.exp[s];
@@ -567,6 +569,99 @@ __global__ __launch_bounds__(kGemvWaveThreads, 1) void gemv1w_kernel(GemmArgs a,
     const int p0 = __builtin_amdgcn_readlane(pj0, slot);
     const int m = __builtin_amdgcn_readlane(pj1, slot) - p0;
     for (int t = 0; t < m; ++t) gemv_store_any<GLU, 1, U>(a, g, v, n0, p0 + t, 0, 1);
+  }
+}
+
+// One token's second projection with the combine as its epilogue (T = 1,
+// activation rows in routed order): out[n] = sum_j w[j] * Y[inv[j]][n] over
+// j ascending, dropped copies (inv = -1) skipped, where Y[p][n] is the
+// float32 product the one-token GEMV forms (same lane geometry, same
+// reduction) and the sum uses the combine's operations in its order; so out
+// equals gnf4_grouped_gemm followed by gnf4_combine bit for bit, without
+// writing or reading Y. One workgroup of 8 waves per block of RW * U output
+// rows: wave w forms the products of copies j = w, w + 8, ... (its expert's
+// rows and its activation row), the products meet in LDS, and one thread
+// per output row adds them up. Each copy's expert comes from a binary search
+// of the offsets, read with the copies' rows and weights in one round trip.
+constexpr int kGemvCombineThreads = 512;
+
+template <int FMT, int C, int U>
+__global__ __launch_bounds__(kGemvCombineThreads, 2) void gemv1c_kernel(GemmArgs a, int L_log2,
+                                                                        int blocks_per_wg,
+                                                                        const float *topk_w,
+                                                                        const int32_t *inv,
+                                                                        float *out) {
+  constexpr bool kLut = FMT != GNF4_MXFP4;
+  constexpr int kWaves = kGemvCombineThreads / 64;
+  constexpr int kMaxRows = 8 * U;                 // RW <= 8 rows per wave slot
+  __shared__ uint32_t lut[kLut ? kLutWords : 1];
+  __shared__ int s_off[GNF4_MAX_EXPERTS + 1];
+  __shared__ int s_p[64], s_e[64];
+  __shared__ float s_w[64];
+  __shared__ float s_y[64][kMaxRows];           // [copy or (block, copy)][row]
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const uint32_t lane4 = (uint32_t)lane << 2;
+  const int N = a.w.N, K = a.w.K, E = a.w.E, k = a.k;
+  GemvGeom g;
+  g.L_log2 = L_log2;
+  g.L = 1 << L_log2;
+  g.RW = 64 >> L_log2;
+  g.li = lane & (g.L - 1);
+  g.seg = lane >> L_log2;
+  g.wave = 0;
+  g.ustride = 1;
+  g.half = 0;
+  g.KCH = K >> 5;
+  g.rows_per_item = g.RW * U;
+  const int G = blocks_per_wg;                    // row blocks of this workgroup (G * k <= 64)
+  const int nb0 = (int)blockIdx.x * G;
+
+  for (int e = tid; e <= E; e += kGemvCombineThreads) s_off[e] = a.offsets[e];
+  if (tid < k) {
+    s_p[tid] = inv[tid];
+    s_w[tid] = topk_w[tid];
+  }
+  if constexpr (kLut) fill_nf4_lut<kGemvCombineThreads>(lut, tid);
+  __syncthreads();
+  if (tid < k) {                                  // expert of copy tid's routed row
+    const int p = s_p[tid];
+    int lo = 0, hi = E;                           // last e with offsets[e] <= p
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (s_off[mid] <= p) lo = mid;
+      else hi = mid;
+    }
+    s_e[tid] = lo;
+  }
+  __syncthreads();
+
+  // task q = (row block q / k, copy q % k)
+  for (int q = wave; q < G * k; q += kWaves) {
+    const int b = q / k, j = q - b * k;
+    const int p = s_p[j];
+    uint32_t x[1][C][16];
+    gemv_load_x_row<C>(a, g, max(p, 0), x);
+    GemvRows<U, C> R;
+    gemv_load_rows<FMT, U, C, false>(a, g, s_e[j], (nb0 + b) * g.rows_per_item, R);
+    float v[U][1];
+    gemv_dot<FMT, 1, U, C>(g, lut, lane4, R, x, v);
+    if (g.li == 0) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) s_y[q][u * g.RW + g.seg] = v[u][0];
+    }
+  }
+  __syncthreads();
+  if (tid < G * g.rows_per_item) {               // the combine's operations, j ascending
+    const int b = tid / g.rows_per_item, r = tid - b * g.rows_per_item;
+    const int n = (nb0 + b) * g.rows_per_item + r;
+    if (n < N) {
+      float acc = 0.f;
+      for (int j = 0; j < k; ++j)
+        if (s_p[j] >= 0) acc = __builtin_fmaf(s_w[j], s_y[b * k + j][r], acc);
+      out[n] = acc;
+    }
   }
 }
 
@@ -1151,6 +1246,67 @@ static hipError_t gemv1w_any(const GemmArgs &a, int C, int L_log2, int max_slots
                         : gemv1w_dispatch<FMT, true, false>(a, C, L_log2, max_slots, s);
   return route ? gemv1w_dispatch<FMT, false, true>(a, C, L_log2, max_slots, s)
                : gemv1w_dispatch<FMT, false, false>(a, C, L_log2, max_slots, s);
+}
+
+template <int FMT, int C, int U>
+static hipError_t gemv1c_go(const GemmArgs &a, int L_log2, const float *topk_w,
+                            const int32_t *inv, float *out, hipStream_t s) {
+  const int rows_per_item = (64 >> L_log2) * U;
+  const int items = (a.w.N + rows_per_item - 1) / rows_per_item;
+  const int G = a.k < 8 ? 8 / a.k : 1;            // row blocks per workgroup
+  const int wgs = (items + G - 1) / G;
+  hipLaunchKernelGGL((gemv1c_kernel<FMT, C, U>), dim3((unsigned)wgs), dim3(kGemvCombineThreads), 0,
+                     s, a, L_log2, G, topk_w, inv, out);
+  return hipGetLastError();
+}
+
+// Rows per wave slot: the smallest U (1, 2, 4) whose workgroup count is at
+// most two per CU (fewer, larger workgroups amortize the table fill and the
+// routing read; more keep every CU busy).
+template <int FMT, int C>
+static hipError_t gemv1c_pick(const GemmArgs &a, int L_log2, const float *topk_w,
+                              const int32_t *inv, float *out, hipStream_t s) {
+  const int G = a.k < 8 ? 8 / a.k : 1;
+  const int64_t target = 2LL * device_cu_count();
+  int U = 4;
+  for (int u = 1; u <= 4; u <<= 1) {
+    const int64_t rows = (int64_t)(64 >> L_log2) * u * G;
+    if ((a.w.N + rows - 1) / rows <= target) {
+      U = u;
+      break;
+    }
+  }
+  if (U == 1) return gemv1c_go<FMT, C, 1>(a, L_log2, topk_w, inv, out, s);
+  if (U == 2) return gemv1c_go<FMT, C, 2>(a, L_log2, topk_w, inv, out, s);
+  return gemv1c_go<FMT, C, 4>(a, L_log2, topk_w, inv, out, s);
+}
+
+template <int FMT>
+static hipError_t gemv1c_dispatch(const GemmArgs &a, int C, int L_log2, const float *topk_w,
+                                  const int32_t *inv, float *out, hipStream_t s) {
+  switch (C) {
+    case 1: return gemv1c_pick<FMT, 1>(a, L_log2, topk_w, inv, out, s);
+    case 2: return gemv1c_pick<FMT, 2>(a, L_log2, topk_w, inv, out, s);
+    case 3: return gemv1c_pick<FMT, 3>(a, L_log2, topk_w, inv, out, s);
+    case 4: return gemv1c_pick<FMT, 4>(a, L_log2, topk_w, inv, out, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+bool gemv_combine_fits(const GemmArgs &a) {
+  int L_log2 = 6, C = 1;
+  return a.T == 1 && !a.gather && a.k <= 64 && gemv_shape(a.w.K, 1, &L_log2, &C);
+}
+
+hipError_t launch_gemv_combine(const GemmArgs &a, const float *topk_w, const int32_t *inv,
+                               float *out, hipStream_t s) {
+  int L_log2 = 6, C = 1;
+  if (!gemv_combine_fits(a) || !gemv_shape(a.w.K, 1, &L_log2, &C)) return hipErrorInvalidValue;
+  switch (a.w.format) {
+    case GNF4_NF4: return gemv1c_dispatch<GNF4_NF4>(a, C, L_log2, topk_w, inv, out, s);
+    case GNF4_NF4_DQ: return gemv1c_dispatch<GNF4_NF4_DQ>(a, C, L_log2, topk_w, inv, out, s);
+    default: return gemv1c_dispatch<GNF4_MXFP4>(a, C, L_log2, topk_w, inv, out, s);
+  }
 }
 
 hipError_t launch_gemv(const GemmArgs &a, hipStream_t s) {

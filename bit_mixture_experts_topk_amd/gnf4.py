@@ -25,7 +25,7 @@ STATUS = {0: "OK", 1: "INVALID_ARG", 2: "UNSUPPORTED", 4: "DEVICE"}
 
 # Every entry point declared in include/gnf4.h.
 EXPORTS = ("gnf4_route", "gnf4_route_logits", "gnf4_route_grouped_gemm", "gnf4_grouped_gemm",
-           "gnf4_grouped_gemm_swiglu",
+           "gnf4_grouped_gemm_swiglu", "gnf4_grouped_gemm_combine",
            "gnf4_grouped_gemm_dx", "gnf4_swiglu", "gnf4_combine",
            "gnf4_dequant", "gnf4_dequant_experts_bf16", "gnf4_quantize", "gnf4_nf4_codebook",
            "gnf4_last_error",
@@ -62,6 +62,8 @@ def lib():
         L.gnf4_grouped_gemm_swiglu.argtypes = [ctypes.POINTER(CWeights), P, I, P, P, P, P, I, I, P, S]
         L.gnf4_route_grouped_gemm.argtypes = [P, I, I, P, P, P, P, P, P, P,
                                               ctypes.POINTER(CWeights), P, P, P, S]
+        L.gnf4_grouped_gemm_combine.argtypes = [ctypes.POINTER(CWeights), P, P, P, P, P, P, P, I, I,
+                                                P, P, S]
         L.gnf4_grouped_gemm_dx.argtypes = [ctypes.POINTER(CWeights), P, P, I, I, P, S]
         L.gnf4_combine.argtypes = [P, P, P, I, I, I, P, S]
         L.gnf4_dequant.argtypes = [ctypes.POINTER(CWeights), I, P, S]
@@ -278,6 +280,25 @@ def grouped_gemm_swiglu(w, X, gather, r, T, k, H=None):
                                           _ptr(r["perm"]), _ptr(r["active"]), _ptr(r["n_active"]),
                                           T, k, _ptr(H), _stream()), "gnf4_grouped_gemm_swiglu")
     return H
+
+
+def grouped_gemm_combine(w, X, r, topk_w, T, k, out=None, Y=None):
+    """grouped_gemm(gather=0) then combine: out [T, N] float32; one launch for
+    a single token. Y is the [T*k, N] intermediate of the two-launch path
+    (allocated here when needed)."""
+    if not (X.is_cuda and X.is_contiguous() and X.element_size() == 2):
+        raise ValueError("X must be a contiguous bf16 (or 16-bit bit pattern) CUDA tensor")
+    _dev(topk_w, torch.float32, "topk_w")
+    if out is None:
+        out = torch.empty((max(T, 1), w.N), dtype=torch.float32, device=X.device)
+    if Y is None and not (T == 1 and w.K <= 8192):
+        Y = torch.empty((max(T * k, 1), w.N), dtype=torch.float32, device=X.device)
+    cw = w.cstruct()
+    _check(lib().gnf4_grouped_gemm_combine(ctypes.byref(cw), _ptr(X), _ptr(r["offsets"]), _ptr(r["perm"]),
+                                           _ptr(r["inv"]), _ptr(r["active"]), _ptr(r["n_active"]),
+                                           _ptr(topk_w), T, k, _ptr(Y), _ptr(out), _stream()),
+           "gnf4_grouped_gemm_combine")
+    return out
 
 
 def grouped_gemm_dx(w, dY, r, T, k, dA=None):

@@ -20,7 +20,8 @@
  *                       with H = silu(gate) * up, bf16, as its epilogue
  *                       (or gnf4_grouped_gemm, then gnf4_swiglu)
  *   gnf4_grouped_gemm   down projection (rows of H, routed order)
- *   gnf4_combine
+ *   gnf4_combine        (gnf4_grouped_gemm_combine: the last two as one call,
+ *                       one launch for a single token)
  * and the backward pass through the frozen experts is, per projection:
  *   gnf4_grouped_gemm_dx   dA[p] = dY[p] . W'[e]    (one launch)
  *   gnf4_combine           with unit weights: dX[t] = sum_j dA[inv[t*k+j]]
@@ -193,6 +194,28 @@ gnf4_status gnf4_grouped_gemm_swiglu(const gnf4_weights *w, const uint16_t *X, i
 gnf4_status gnf4_grouped_gemm_dx(const gnf4_weights *w, const uint16_t *dY,
                                  const int32_t *offsets, int32_t T, int32_t k, float *dA,
                                  gnf4_stream_t stream);
+
+/* gnf4_grouped_gemm_combine -- the second projection (rows already in
+ * routed order, gather = 0) followed by the combine, as one call:
+ *   gnf4_grouped_gemm(w, X, 0, offsets, perm, active, n_active, T, k, Y)
+ *   gnf4_combine(Y, inv, topk_w, T, k, N, out)
+ * out is bit-identical to those two calls. For a single token (T == 1) with
+ * K <= 8192 it is one launch that never writes Y: each output row block
+ * forms the products of every routed copy (the same float32 values as the
+ * GEMM) and adds them with the combine's operations in its order
+ * (j ascending, dropped copies skipped), which saves a launch and the Y
+ * round trip per layer step (fixed per-token cost: Jordan Anderson,
+ * jordananderson-pages.pages.dev, section "grouped-nf4-gemm &
+ * experts-4bit", demonstration paragraph of the first bullet). Otherwise
+ * the two launches, with Y float32 [T*k][N] (16-byte aligned) as their
+ * intermediate; Y may be NULL when the one-launch path applies. out float32
+ * [T][N] (16-byte aligned); N % 4 == 0. Other arguments, limits and errors
+ * as the two calls. */
+gnf4_status gnf4_grouped_gemm_combine(const gnf4_weights *w, const uint16_t *X,
+                                      const int32_t *offsets, const int32_t *perm,
+                                      const int32_t *inv, const int32_t *active,
+                                      const int32_t *n_active, const float *topk_w, int32_t T,
+                                      int32_t k, float *Y, float *out, gnf4_stream_t stream);
 
 /* gnf4_combine -- weighted top-k combine back to tokens.
  *   out[t][n] = sum_{j=0..k-1} topk_w[t][j] * Y[inv[t*k+j]][n]

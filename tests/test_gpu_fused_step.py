@@ -65,3 +65,41 @@ def test_route_grouped_gemm_equals_separate_calls(fmt, swiglu, E, N, K, T, k, id
                           b.view(np.uint32) if b.dtype == np.float32 else b), "outputs differ"
     if ids_kind == "bad":
         assert int(r["bad"].item()) == 1 and nv == T * k - 2
+
+
+@pytest.mark.parametrize("fmt", ["nf4", "nf4_dq", "mxfp4"])
+@pytest.mark.parametrize("E,N,K,T,k,ids_kind", [
+    (8, 256, 256, 1, 2, "distinct"),
+    (64, 2048, 1024, 1, 8, "distinct"),   # the OLMoE-shaped down projection (two rows per slot)
+    (8, 8192, 512, 1, 8, "distinct"),     # 8192 output rows: four rows per wave slot
+    (6, 2880, 1024, 1, 4, "duplicates"),  # k = 4: two row blocks per workgroup, two rows per slot
+    (16, 200, 512, 1, 6, "duplicates"),   # copies of one expert with different inputs
+    (16, 128, 512, 1, 6, "bad"),          # dropped copies add nothing
+    (128, 96, 2880, 1, 4, "distinct"),    # K = 2880 (three chunks per lane)
+    (1024, 64, 256, 1, 64, "distinct"),   # k = 64
+    (6, 64, 6144, 1, 5, "distinct"),      # K = 6144: four chunks per lane
+    (3, 64, 256, 1, 1, "distinct"),       # k = 1
+    (8, 64, 8192, 1, 4, "distinct"),      # K = 8192: the largest K of the one-launch path
+    (8, 64, 8256, 1, 5, "distinct"),      # K past it: two launches (MFMA GEMM, then combine)
+    (8, 256, 256, 7, 2, "duplicates"),    # T > 1: two launches
+])
+def test_grouped_gemm_combine_equals_separate_calls(fmt, E, N, K, T, k, ids_kind):
+    g = gnf4()
+    case = synth.small_layer(E, N, K, T, k, seed=9, distinct=(ids_kind == "distinct"), gather=0)
+    ids = case["ids"].copy()
+    if ids_kind == "bad":
+        ids[0, 0] = E
+        ids[0, 4] = -1
+    codes, scales, scales2 = oracle_pack(fmt, case["W"])
+    pw = packed_to_device(g, fmt, codes, scales, scales2, E, N, K)
+    X = bits_to_device(case["X"])
+    tw = torch.from_numpy(case["tw"]).cuda()
+    say("grouped_gemm_combine", fmt, E, N, K, T, k, ids_kind)
+    r = g.route(torch.from_numpy(ids).cuda(), E)
+    Y = g.grouped_gemm(pw, X, 0, r, T, k)
+    ref = g.combine(Y, r["inv"], tw, T, k)
+    got = g.grouped_gemm_combine(pw, X, r, tw, T, k)
+    torch.cuda.synchronize()
+    a = got.cpu().numpy()[:T]
+    b = ref.cpu().numpy()[:T]
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), int((a != b).sum())
