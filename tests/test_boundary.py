@@ -199,3 +199,39 @@ def test_gemm_dx_rejects(L):
     assert L.gnf4_grouped_gemm_dx(ctypes.byref(big), p, p, 16384, 2, p, None) == 2        # 4 GiB dY
     assert "4 GiB" in gnf4.last_error()
     assert L.gnf4_grouped_gemm_dx(ctypes.byref(w), None, None, 0, 2, None, None) == 0      # T = 0
+
+
+def test_route_grouped_gemm_rejects(L):
+    w = weights()
+    p = 0x1000
+
+    def call(T=1, k=2, ids=p, Y=p, H=None, counts=p, wt=None):
+        return L.gnf4_route_grouped_gemm(ids, T, k, counts, p, p, p, p, p, p,
+                                         ctypes.byref(wt or w), p, Y, H, None)
+
+    assert call(k=0) == INVALID and "k = 0" in gnf4.last_error()
+    assert call(k=65) == INVALID
+    assert call(T=-1) == INVALID
+    assert call(Y=p, H=p) == INVALID and "exactly one" in gnf4.last_error()
+    assert call(Y=None, H=None) == INVALID
+    assert call(ids=None) == INVALID
+    assert call(counts=None) == INVALID
+    assert call(wt=weights(E=0)) == INVALID and "E = 0" in gnf4.last_error()
+
+
+def test_grouped_gemm_combine_rejects(L):
+    w = weights()                      # N = 8
+    p = 0x1000
+
+    def call(T=1, k=2, X=p, out=p, wt=None, tw=p):
+        return L.gnf4_grouped_gemm_combine(ctypes.byref(wt or w), X, p, p, p, p, p, tw, T, k,
+                                           None, out, None)
+
+    assert call(k=0) == INVALID
+    assert call(T=-1) == INVALID
+    assert call(wt=weights(N=6)) == INVALID and "multiple of 4" in gnf4.last_error()
+    assert call(out=None) == INVALID and "NULL" in gnf4.last_error()
+    assert call(tw=None) == INVALID
+    assert call(X=0x1004) == INVALID and "16-byte" in gnf4.last_error()
+    assert call(out=0x1008) == INVALID
+    assert call(T=0, X=None, out=None) == 0                # nothing to do
