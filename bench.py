@@ -193,8 +193,9 @@ class StepSlot:
     def run(self, gnf4):
         cfg, T, k = self.layer.cfg, self.T, self.layer.cfg.k
         if self.ffn:
-            r = gnf4.route_logits(self.logits, k, out=self.r)
-            gnf4.grouped_gemm_swiglu(self.layer.projs[0], self.X, 1, r, T, k, self.H)
+            # router top-k + routing + gate_up with SwiGLU, down + combine
+            r, _ = gnf4.route_logits_grouped_gemm(self.logits, k, self.layer.projs[0], self.X,
+                                                  out=self.r, H=self.H, swiglu=True)
             gnf4.grouped_gemm_combine(self.layer.projs[1], self.H, r, r["topk_w"], T, k, self.out,
                                       Y=self.Y[1])
             return
@@ -738,8 +739,9 @@ def main():
             T, dt, _, fl = out["ffn"]["prefill"]
             f["prefill"] = {"T": T, "step_ms": round(dt * 1e3, 4), "tflops": round(fl / dt / 1e12, 2),
                             "pct_mfma_peak": round(100 * fl / dt / 1e12 / BF16_PEAK_TFLOPS, 2)}
-        f["steps"] = ("route_logits (top-k + softmax + route), gate_up GEMM with the SwiGLU "
-                      "epilogue (bf16 H), down GEMM on H, combine")
+        f["steps"] = ("router top-k + softmax + route + gate_up GEMM with the SwiGLU epilogue "
+                      "(bf16 H) (gnf4_route_logits_grouped_gemm), down GEMM on H + combine "
+                      "(gnf4_grouped_gemm_combine): two launches at T = 1")
         result["ffn_layer"] = f
     if out.get("dequant"):
         dqr = {}

@@ -164,6 +164,9 @@ gnf4_status gnf4_swiglu(const float *Y, int32_t rows, int32_t I, uint16_t *H,
 struct FusedRoute {
   const int32_t *ids;
   int32_t *counts, *offsets, *perm, *inv, *active, *n_active, *bad;
+  const float *logits;        // instead of ids: the router's top-k first
+  int32_t *topk_ids;
+  float *topk_w;
 };
 
 static gnf4_status grouped_gemm_any(const gnf4_weights *w, const uint16_t *X, int32_t gather,
@@ -202,6 +205,9 @@ static gnf4_status grouped_gemm_any(const gnf4_weights *w, const uint16_t *X, in
   if (fr) {
     if (T == 1 && gather == 1 && rows <= kGemvMaxRows && w->K <= kGemvMaxK) {
       a.ids = fr->ids;                            // one launch: routing inside the GEMV
+      a.logits = fr->logits;
+      a.r_topk_ids = fr->topk_ids;
+      a.r_topk_w = fr->topk_w;
       a.r_counts = fr->counts;
       a.r_offsets = fr->offsets;
       a.r_perm = fr->perm;
@@ -211,8 +217,12 @@ static gnf4_status grouped_gemm_any(const gnf4_weights *w, const uint16_t *X, in
       a.r_bad = fr->bad;
       return device_status(launch_gemv(a, (hipStream_t)stream), "fused route + grouped GEMM launch");
     }
-    e = launch_route(fr->ids, T, k, w->E, fr->counts, fr->offsets, fr->perm, fr->inv, fr->active,
-                     fr->n_active, fr->bad, (hipStream_t)stream);
+    if (fr->logits) {
+      e = launch_topk(fr->logits, T, w->E, k, fr->topk_ids, fr->topk_w, (hipStream_t)stream);
+      if (e != hipSuccess) return device_status(e, "top-k launch");
+    }
+    e = launch_route(fr->logits ? fr->topk_ids : fr->ids, T, k, w->E, fr->counts, fr->offsets,
+                     fr->perm, fr->inv, fr->active, fr->n_active, fr->bad, (hipStream_t)stream);
     if (e != hipSuccess) return device_status(e, "route launch");
   }
   if (rows <= kGemvMaxRows && w->K <= kGemvMaxK)
@@ -256,7 +266,36 @@ gnf4_status gnf4_route_grouped_gemm(const int32_t *topk_ids, int32_t T, int32_t 
   if (T == 0)                                     // routing of nothing: counts, offsets, flags
     return gnf4_route(topk_ids, T, k, w->E, counts, offsets, perm, inv, active, n_active,
                       bad_id_flag, stream);
-  const FusedRoute fr = {topk_ids, counts, offsets, perm, inv, active, n_active, bad_id_flag};
+  const FusedRoute fr = {topk_ids, counts, offsets, perm, inv, active, n_active, bad_id_flag,
+                         nullptr, nullptr, nullptr};
+  return grouped_gemm_any(w, X, 1, offsets, perm, active, n_active, T, k, Y, H, stream, &fr);
+}
+
+gnf4_status gnf4_route_logits_grouped_gemm(const float *logits, int32_t T, int32_t k,
+                                           int32_t *topk_ids, float *topk_w, int32_t *counts,
+                                           int32_t *offsets, int32_t *perm, int32_t *inv,
+                                           int32_t *active, int32_t *n_active,
+                                           int32_t *bad_id_flag, const gnf4_weights *w,
+                                           const uint16_t *X, float *Y, uint16_t *H,
+                                           gnf4_stream_t stream) {
+  gnf4_status st = check_weights(w);
+  if (st != GNF4_OK) return st;
+  if (k < 1 || k > 64 || k > w->E)
+    return fail(GNF4_ERR_INVALID_ARG, "k = %d outside [1, min(64, E = %d)]", k, w->E);
+  if (T < 0) return fail(GNF4_ERR_INVALID_ARG, "T = %d is negative", T);
+  if ((int64_t)T * k >= ((int64_t)1 << 31) - 1024)
+    return fail(GNF4_ERR_INVALID_ARG, "T*k too large");
+  if (!counts || !offsets || !active || !n_active || !bad_id_flag)
+    return fail(GNF4_ERR_INVALID_ARG, "an output pointer is NULL");
+  if (T > 0 && (!logits || !topk_ids || !topk_w || !perm || !inv))
+    return fail(GNF4_ERR_INVALID_ARG, "logits, topk_ids, topk_w, perm or inv is NULL");
+  if (T > 0 && (Y == nullptr) == (H == nullptr))
+    return fail(GNF4_ERR_INVALID_ARG, "exactly one of Y and H must be given");
+  if (T == 0)
+    return gnf4_route_logits(logits, T, k, w->E, topk_ids, topk_w, counts, offsets, perm, inv,
+                             active, n_active, bad_id_flag, stream);
+  const FusedRoute fr = {nullptr, counts, offsets, perm, inv, active, n_active, bad_id_flag,
+                         logits, topk_ids, topk_w};
   return grouped_gemm_any(w, X, 1, offsets, perm, active, n_active, T, k, Y, H, stream, &fr);
 }
 

@@ -60,6 +60,11 @@ struct GemmArgs {
   // routing was done beforehand (offsets / active / n_active are read).
   const int32_t *ids;
   int32_t *r_counts, *r_offsets, *r_perm, *r_inv, *r_active, *r_n_active, *r_bad;
+  // ... or the router's logits [1][E] (then the top-k ids and softmax weights
+  // are formed first and written to r_topk_ids / r_topk_w)
+  const float *logits;
+  int32_t *r_topk_ids;
+  float *r_topk_w;
 };
 
 // Input gradient of the grouped GEMM: dA [rows][K] from dY [rows][N], both
@@ -132,6 +137,68 @@ __device__ __forceinline__ uint16_t swiglu_bf16(float g, float u) {
   return f64_to_bf16_rne(x / (1.0 + exp(-x)) * (double)u);
 }
 
+
+// ------------------------------------------------ router top-k of one token
+
+// Order key of (logit, expert): larger keys rank first. The high half maps
+// the float's bits to an unsigned integer that increases with the value
+// (NaN maps to 0, below -inf); the low half is ~e, so that on equal logits
+// the lower expert ranks first. Absent and already chosen entries use key 0,
+// below every real entry (whose low half is at least ~1023).
+__device__ __forceinline__ uint64_t topk_key(float x, int e) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const uint32_t ord = (x != x) ? 0u : ((u & 0x80000000u) ? ~u : (u | 0x80000000u));
+  return ((uint64_t)ord << 32) | (uint32_t)~(uint32_t)e;
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const uint32_t lo = __shfl_xor((uint32_t)v, d, 64);
+    const uint32_t hi = __shfl_xor((uint32_t)(v >> 32), d, 64);
+    const uint64_t o = ((uint64_t)hi << 32) | lo;
+    v = o > v ? o : v;
+  }
+  return v;
+}
+
+// The router's choice for one token's logits row[0 .. E) (E <= 64 NPL), by
+// one whole wave: lane l holds the logits of experts l + 64 j (j < NPL); k
+// rounds each take the largest remaining key. Lane j < k returns the j-th
+// choice and its softmax weight, formed in float64 (the largest chosen
+// logit subtracted, the exponentials summed in rank order by every lane
+// alike) and rounded to float32. The result does not depend on NPL.
+template <int NPL>
+__device__ __forceinline__ void topk_row(const float *row, int E, int k, int lane, int &id,
+                                         float &wt) {
+  uint64_t key[NPL];
+#pragma unroll
+  for (int j = 0; j < NPL; ++j) {
+    const int e = lane + 64 * j;
+    key[j] = e < E ? topk_key(row[e], e) : 0ull;
+  }
+  int mine = 0;                                 // lane r: the expert chosen in round r
+  for (int r = 0; r < k; ++r) {
+    uint64_t best = 0;
+#pragma unroll
+    for (int j = 0; j < NPL; ++j) best = key[j] > best ? key[j] : best;
+    best = wave_max_u64(best);
+    const int e = (int)~(uint32_t)best;
+    if ((e & 63) == lane) {
+#pragma unroll
+      for (int j = 0; j < NPL; ++j)
+        if (j == (e >> 6)) key[j] = 0;
+    }
+    if (lane == r) mine = e;
+  }
+  const double x = lane < k ? (double)row[mine] : 0.0;
+  const double m = __shfl(x, 0, 64);
+  const double ex = exp(x - m);
+  double s = 0.0;
+  for (int j = 0; j < k; ++j) s += __shfl(ex, j, 64);
+  id = mine;
+  wt = (float)(ex / s);
+}
 
 // NF4 byte -> two bf16 codebook values as one dword (element 2i, the high
 // nibble, in the low half): the operand layout of v_dot2 and of the MFMA

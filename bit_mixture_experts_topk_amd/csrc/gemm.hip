@@ -445,16 +445,28 @@ constexpr int kGemvWaveThreads = 1024;
 // is led by the lane with |lt & leaders| = s. Slot s's expert, first routed
 // row and row count go to LDS for every wave; workgroup 0 writes perm, inv,
 // n_active and bad, and the per-expert arrays (counts, offsets, active) are
-// written 64 experts per workgroup.
+// written 64 experts per workgroup once its GEMV items are done.
 struct OneTokenRoute {
   int exp[64], seg[64], cnt[64];
   int nact, total;
 };
 
+template <bool LOGITS>
 __device__ __forceinline__ void route_one_token(const GemmArgs &a, OneTokenRoute &sr, int tid) {
   const int lane = tid & 63, k = a.k, E = a.w.E;
   if (tid < 64) {
-    const int e = lane < k ? a.ids[lane] : -1;
+    int e;
+    if constexpr (LOGITS) {                       // the router's top-k first (as gnf4_route_logits)
+      float wt;
+      topk_row<GNF4_MAX_EXPERTS / 64>(a.logits, E, k, lane, e, wt);
+      if (blockIdx.x == 0 && lane < k) {
+        a.r_topk_ids[lane] = e;
+        a.r_topk_w[lane] = wt;
+      }
+      if (lane >= k) e = -1;
+    } else {
+      e = lane < k ? a.ids[lane] : -1;
+    }
     const bool valid = lane < k && (unsigned)e < (unsigned)E;
     const uint64_t vmask = __ballot(valid);
     uint64_t eq = vmask, lt = 0;
@@ -494,7 +506,14 @@ __device__ __forceinline__ void route_one_token(const GemmArgs &a, OneTokenRoute
     }
   }
   __syncthreads();
-  // the per-expert arrays, 64 experts per workgroup in turn
+}
+
+// The per-expert routing arrays (counts, offsets, active), 64 experts per
+// workgroup in turn; called after the GEMV items (nothing in the launch
+// reads them).
+__device__ __forceinline__ void route_one_token_arrays(const GemmArgs &a, const OneTokenRoute &sr,
+                                                       int tid) {
+  const int E = a.w.E;
   if (tid < 64) {
     const int nact = sr.nact;
     for (int e = (int)blockIdx.x * 64 + tid; e < E; e += (int)gridDim.x * 64) {
@@ -512,7 +531,9 @@ __device__ __forceinline__ void route_one_token(const GemmArgs &a, OneTokenRoute
   }
 }
 
-template <int FMT, int C, int U, bool GLU, bool ROUTE>
+// ROUTE: 0 = routing read from a previous launch, 1 = routing from the k ids,
+// 2 = the router's top-k from the logits, then the routing.
+template <int FMT, int C, int U, bool GLU, int ROUTE>
 __global__ __launch_bounds__(kGemvWaveThreads, 1) void gemv1w_kernel(GemmArgs a, int L_log2,
                                                                      int items_per_expert,
                                                                      int max_slots) {
@@ -542,7 +563,7 @@ __global__ __launch_bounds__(kGemvWaveThreads, 1) void gemv1w_kernel(GemmArgs a,
   gemv_load_x_row<C>(a, g, 0, x);
   if constexpr (kLut) fill_nf4_lut<kGemvWaveThreads>(lut, tid);
   if constexpr (ROUTE) {
-    route_one_token(a, sr, tid);                  // ends with a barrier: table written too
+    route_one_token<ROUTE == 2>(a, sr, tid);      // ends with a barrier: table written too
     nact = sr.nact;
     const int sl = min(lane, 63);
     ej = lane < nact ? sr.exp[sl] : -1;
@@ -570,6 +591,7 @@ __global__ __launch_bounds__(kGemvWaveThreads, 1) void gemv1w_kernel(GemmArgs a,
     const int m = __builtin_amdgcn_readlane(pj1, slot) - p0;
     for (int t = 0; t < m; ++t) gemv_store_any<GLU, 1, U>(a, g, v, n0, p0 + t, 0, 1);
   }
+  if constexpr (ROUTE) route_one_token_arrays(a, sr, tid);
 }
 
 // One token's second projection with the combine as its epilogue (T = 1,
@@ -1099,7 +1121,7 @@ static int out_cols(const GemmArgs &a) { return a.H ? a.w.N / 2 : a.w.N; }
 
 // One token, gathered input: the persistent kernel, one workgroup per CU (or
 // as many as are resident at once).
-template <int FMT, int C, int U, bool GLU, bool ROUTE>
+template <int FMT, int C, int U, bool GLU, int ROUTE>
 static hipError_t gemv1w_go(const GemmArgs &a, int L_log2, int max_slots, hipStream_t s) {
   static int per_cu = 0;
   if (per_cu == 0) {
@@ -1225,7 +1247,7 @@ static int gemv_pick_u(const GemvVariant &v, int fmt, int cols, int L_log2, int 
 // Rows per wave slot of the one-token gathered kernel for C chunks per lane
 // (measured fastest on the workload shapes, and free of register spills).
 // The SwiGLU epilogue needs an even U (slot u pairs with u + U/2).
-template <int FMT, bool GLU, bool ROUTE>
+template <int FMT, bool GLU, int ROUTE>
 static hipError_t gemv1w_dispatch(const GemmArgs &a, int C, int L_log2, int max_slots,
                                   hipStream_t s) {
   switch (C) {
@@ -1239,13 +1261,17 @@ static hipError_t gemv1w_dispatch(const GemmArgs &a, int C, int L_log2, int max_
   }
 }
 
+template <int FMT, bool GLU>
+static hipError_t gemv1w_route(const GemmArgs &a, int C, int L_log2, int max_slots, hipStream_t s) {
+  if (a.logits) return gemv1w_dispatch<FMT, GLU, 2>(a, C, L_log2, max_slots, s);
+  if (a.ids) return gemv1w_dispatch<FMT, GLU, 1>(a, C, L_log2, max_slots, s);
+  return gemv1w_dispatch<FMT, GLU, 0>(a, C, L_log2, max_slots, s);
+}
+
 template <int FMT>
 static hipError_t gemv1w_any(const GemmArgs &a, int C, int L_log2, int max_slots, hipStream_t s) {
-  const bool glu = a.H != nullptr, route = a.ids != nullptr;
-  if (glu) return route ? gemv1w_dispatch<FMT, true, true>(a, C, L_log2, max_slots, s)
-                        : gemv1w_dispatch<FMT, true, false>(a, C, L_log2, max_slots, s);
-  return route ? gemv1w_dispatch<FMT, false, true>(a, C, L_log2, max_slots, s)
-               : gemv1w_dispatch<FMT, false, false>(a, C, L_log2, max_slots, s);
+  return a.H ? gemv1w_route<FMT, true>(a, C, L_log2, max_slots, s)
+             : gemv1w_route<FMT, false>(a, C, L_log2, max_slots, s);
 }
 
 template <int FMT, int C, int U>

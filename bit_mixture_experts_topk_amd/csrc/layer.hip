@@ -11,32 +11,7 @@ namespace gnf4 {
 
 // ---------------------------------------------------------------- top-k
 
-// Order key of (logit, expert): larger keys rank first. The high half maps
-// the float's bits to an unsigned integer that increases with the value
-// (NaN maps to 0, below -inf); the low half is ~e, so that on equal logits
-// the lower expert ranks first. Absent and already chosen entries use key 0,
-// below every real entry (whose low half is at least ~1023).
-__device__ __forceinline__ uint64_t topk_key(float x, int e) {
-  const uint32_t u = __builtin_bit_cast(uint32_t, x);
-  const uint32_t ord = (x != x) ? 0u : ((u & 0x80000000u) ? ~u : (u | 0x80000000u));
-  return ((uint64_t)ord << 32) | (uint32_t)~(uint32_t)e;
-}
-
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const uint32_t lo = __shfl_xor((uint32_t)v, d, 64);
-    const uint32_t hi = __shfl_xor((uint32_t)(v >> 32), d, 64);
-    const uint64_t o = ((uint64_t)hi << 32) | lo;
-    v = o > v ? o : v;
-  }
-  return v;
-}
-
-// One wave per token; lane l holds the logits of experts l + 64 j (j < NPL).
-// k rounds each take the largest remaining key. Lane j < k then forms the
-// softmax weight of the j-th choice in float64: the largest chosen logit
-// subtracted, the exponentials summed in rank order by every lane alike.
+// One wave per token (topk_row in common.h): four tokens per workgroup.
 template <int NPL>
 __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ logits, int T, int E,
                                                    int k, int32_t *__restrict__ ids,
@@ -44,35 +19,12 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ log
   const int lane = threadIdx.x & 63;
   const int t = (int)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;                           // whole wave
-  const float *row = logits + (int64_t)t * E;
-  uint64_t key[NPL];
-#pragma unroll
-  for (int j = 0; j < NPL; ++j) {
-    const int e = lane + 64 * j;
-    key[j] = e < E ? topk_key(row[e], e) : 0ull;
-  }
-  int mine = 0;                                 // lane r: the expert chosen in round r
-  for (int r = 0; r < k; ++r) {
-    uint64_t best = 0;
-#pragma unroll
-    for (int j = 0; j < NPL; ++j) best = key[j] > best ? key[j] : best;
-    best = wave_max_u64(best);
-    const int e = (int)~(uint32_t)best;
-    if ((e & 63) == lane) {
-#pragma unroll
-      for (int j = 0; j < NPL; ++j)
-        if (j == (e >> 6)) key[j] = 0;
-    }
-    if (lane == r) mine = e;
-  }
-  const double x = lane < k ? (double)row[mine] : 0.0;
-  const double m = __shfl(x, 0, 64);
-  const double ex = exp(x - m);
-  double s = 0.0;
-  for (int j = 0; j < k; ++j) s += __shfl(ex, j, 64);
+  int id;
+  float wt;
+  topk_row<NPL>(logits + (int64_t)t * E, E, k, lane, id, wt);
   if (lane < k) {
-    ids[(int64_t)t * k + lane] = mine;
-    w[(int64_t)t * k + lane] = (float)(ex / s);
+    ids[(int64_t)t * k + lane] = id;
+    w[(int64_t)t * k + lane] = wt;
   }
 }
 

@@ -24,7 +24,8 @@ FORMATS = {"nf4": NF4, "nf4_dq": NF4_DQ, "mxfp4": MXFP4}
 STATUS = {0: "OK", 1: "INVALID_ARG", 2: "UNSUPPORTED", 4: "DEVICE"}
 
 # Every entry point declared in include/gnf4.h.
-EXPORTS = ("gnf4_route", "gnf4_route_logits", "gnf4_route_grouped_gemm", "gnf4_grouped_gemm",
+EXPORTS = ("gnf4_route", "gnf4_route_logits", "gnf4_route_grouped_gemm",
+           "gnf4_route_logits_grouped_gemm", "gnf4_grouped_gemm",
            "gnf4_grouped_gemm_swiglu", "gnf4_grouped_gemm_combine",
            "gnf4_grouped_gemm_dx", "gnf4_swiglu", "gnf4_combine",
            "gnf4_dequant", "gnf4_dequant_experts_bf16", "gnf4_quantize", "gnf4_nf4_codebook",
@@ -64,6 +65,8 @@ def lib():
                                               ctypes.POINTER(CWeights), P, P, P, S]
         L.gnf4_grouped_gemm_combine.argtypes = [ctypes.POINTER(CWeights), P, P, P, P, P, P, P, I, I,
                                                 P, P, S]
+        L.gnf4_route_logits_grouped_gemm.argtypes = [P, I, I, P, P, P, P, P, P, P, P, P,
+                                                     ctypes.POINTER(CWeights), P, P, P, S]
         L.gnf4_grouped_gemm_dx.argtypes = [ctypes.POINTER(CWeights), P, P, I, I, P, S]
         L.gnf4_combine.argtypes = [P, P, P, I, I, I, P, S]
         L.gnf4_dequant.argtypes = [ctypes.POINTER(CWeights), I, P, S]
@@ -221,6 +224,39 @@ def route_grouped_gemm(topk_ids, w, X, out=None, Y=None, H=None, swiglu=False):
            "gnf4_route_grouped_gemm")
     r["perm"] = r["perm"][:T * k]
     r["inv"] = r["inv"][:T * k]
+    return r, res
+
+
+def route_logits_grouped_gemm(logits, k, w, X, out=None, Y=None, H=None, swiglu=False):
+    """route_logits() then grouped_gemm(gather=1) (or grouped_gemm_swiglu),
+    one launch for a single token; returns (route dict with topk_ids and
+    topk_w, Y or H)."""
+    _dev(logits, torch.float32, "logits")
+    if not (X.is_cuda and X.is_contiguous() and X.element_size() == 2):
+        raise ValueError("X must be a contiguous bf16 (or 16-bit bit pattern) CUDA tensor")
+    T, E = logits.shape
+    r = dict(out) if out is not None else route_buffers(T, k, E, logits.device)
+    if "topk_ids" not in r:
+        r["topk_ids"] = torch.empty((max(T, 1), k), dtype=torch.int32, device=logits.device)
+        r["topk_w"] = torch.empty((max(T, 1), k), dtype=torch.float32, device=logits.device)
+    if swiglu:
+        if H is None:
+            H = torch.empty((max(T * k, 1), w.N // 2), dtype=torch.int16, device=X.device)
+        res = H
+    else:
+        if Y is None:
+            Y = torch.empty((max(T * k, 1), w.N), dtype=torch.float32, device=X.device)
+        res = Y
+    cw = w.cstruct()
+    _check(lib().gnf4_route_logits_grouped_gemm(
+        _ptr(logits), T, k, _ptr(r["topk_ids"]), _ptr(r["topk_w"]), _ptr(r["counts"]),
+        _ptr(r["offsets"]), _ptr(r["perm"]), _ptr(r["inv"]), _ptr(r["active"]), _ptr(r["n_active"]),
+        _ptr(r["bad"]), ctypes.byref(cw), _ptr(X), None if swiglu else _ptr(Y),
+        _ptr(H) if swiglu else None, _stream()), "gnf4_route_logits_grouped_gemm")
+    r["perm"] = r["perm"][:T * k]
+    r["inv"] = r["inv"][:T * k]
+    r["topk_ids"] = r["topk_ids"][:T]
+    r["topk_w"] = r["topk_w"][:T]
     return r, res
 
 

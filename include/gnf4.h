@@ -154,6 +154,24 @@ gnf4_status gnf4_route_grouped_gemm(const int32_t *topk_ids, int32_t T, int32_t 
                                     const uint16_t *X, float *Y, uint16_t *H,
                                     gnf4_stream_t stream);
 
+/* gnf4_route_logits_grouped_gemm -- gnf4_route_logits followed by the first
+ * projection (gather = 1), as one call: the router's top-k ids and softmax
+ * weights, the routing arrays and Y (or H with the SwiGLU epilogue) are
+ * bit-identical to gnf4_route_logits then gnf4_grouped_gemm (or
+ * gnf4_grouped_gemm_swiglu). For a single token (T == 1) it is one launch:
+ * every workgroup of the one-token GEMV forms the top-k from the logits
+ * [1][E] and the routing from it; the first writes topk_ids, topk_w and the
+ * routing outputs. Otherwise the separate launches. Exactly one of Y, H is
+ * non-NULL (for T > 0). Arguments, limits and errors as the calls it
+ * replaces (k <= E). */
+gnf4_status gnf4_route_logits_grouped_gemm(const float *logits, int32_t T, int32_t k,
+                                           int32_t *topk_ids, float *topk_w, int32_t *counts,
+                                           int32_t *offsets, int32_t *perm, int32_t *inv,
+                                           int32_t *active, int32_t *n_active,
+                                           int32_t *bad_id_flag, const gnf4_weights *w,
+                                           const uint16_t *X, float *Y, uint16_t *H,
+                                           gnf4_stream_t stream);
+
 /* gnf4_grouped_gemm_swiglu -- the first projection with the SwiGLU step as
  * its epilogue: for every routed row p and i < N/2,
  *   H[p][i] = bf16(silu(Y[p][i]) * Y[p][N/2 + i])

@@ -103,3 +103,44 @@ def test_grouped_gemm_combine_equals_separate_calls(fmt, E, N, K, T, k, ids_kind
     a = got.cpu().numpy()[:T]
     b = ref.cpu().numpy()[:T]
     assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), int((a != b).sum())
+
+
+@pytest.mark.parametrize("fmt", ["nf4", "mxfp4"])
+@pytest.mark.parametrize("swiglu", [False, True])
+@pytest.mark.parametrize("E,N,K,T,k,logits_kind", [
+    (64, 512, 2048, 1, 8, "normal"),
+    (128, 256, 512, 1, 4, "ties"),        # equal logits: lower id first
+    (1024, 64, 256, 1, 64, "normal"),     # E = 1024, k = 64
+    (8, 128, 256, 1, 8, "nan"),           # NaN logits rank last
+    (16, 128, 256, 6, 3, "normal"),       # T > 1: separate launches
+])
+def test_route_logits_grouped_gemm_equals_separate_calls(fmt, swiglu, E, N, K, T, k, logits_kind):
+    g = gnf4()
+    case = synth.small_layer(E, N, K, T, k, seed=10, distinct=True, gather=1)
+    gl = np.random.default_rng([E, N, K, T, k])
+    logits = gl.standard_normal((T, E)).astype(np.float32)
+    if logits_kind == "ties":
+        logits = np.round(logits).astype(np.float32)
+    if logits_kind == "nan":
+        logits[0, ::3] = np.nan
+    codes, scales, scales2 = oracle_pack(fmt, case["W"])
+    pw = packed_to_device(g, fmt, codes, scales, scales2, E, N, K)
+    X = bits_to_device(case["X"])
+    lg = torch.from_numpy(logits).cuda()
+    say("route_logits_grouped_gemm", fmt, "swiglu", swiglu, E, N, K, T, k, logits_kind)
+    r_ref = g.route_logits(lg, k)
+    if swiglu:
+        ref = g.grouped_gemm_swiglu(pw, X, 1, r_ref, T, k)
+    else:
+        ref = g.grouped_gemm(pw, X, 1, r_ref, T, k)
+    r, got = g.route_logits_grouped_gemm(lg, k, pw, X, swiglu=swiglu)
+    torch.cuda.synchronize()
+    same_route(r, r_ref, T * k)
+    assert np.array_equal(r["topk_ids"].cpu().numpy(), r_ref["topk_ids"].cpu().numpy())
+    assert np.array_equal(r["topk_w"].cpu().numpy().view(np.uint32),
+                          r_ref["topk_w"].cpu().numpy().view(np.uint32))
+    nv = int(r_ref["offsets"][-1].item())
+    a = got.cpu().numpy()[:nv]
+    b = ref.cpu().numpy()[:nv]
+    assert np.array_equal(a.view(np.uint32) if a.dtype == np.float32 else a,
+                          b.view(np.uint32) if b.dtype == np.float32 else b), "outputs differ"
