@@ -140,62 +140,118 @@ __device__ __forceinline__ uint16_t swiglu_bf16(float g, float u) {
 
 // ------------------------------------------------ router top-k of one token
 
-// Order key of (logit, expert): larger keys rank first. The high half maps
-// the float's bits to an unsigned integer that increases with the value
-// (NaN maps to 0, below -inf); the low half is ~e, so that on equal logits
-// the lower expert ranks first. Absent and already chosen entries use key 0,
-// below every real entry (whose low half is at least ~1023).
-__device__ __forceinline__ uint64_t topk_key(float x, int e) {
-  const uint32_t u = __builtin_bit_cast(uint32_t, x);
-  const uint32_t ord = (x != x) ? 0u : ((u & 0x80000000u) ? ~u : (u | 0x80000000u));
-  return ((uint64_t)ord << 32) | (uint32_t)~(uint32_t)e;
+// Order of a logit as an unsigned integer that increases with its value:
+// the float's bits mapped monotonically, -0 taken as +0 (so that the two tie
+// like equal values), NaN as 1 (below -inf); 0 marks an absent or already
+// chosen entry. Equal orders rank the lower expert first.
+__device__ __forceinline__ uint32_t topk_ord(float x) {
+  const uint32_t u = x == 0.0f ? 0u : __builtin_bit_cast(uint32_t, x);
+  return (x != x) ? 1u : ((u & 0x80000000u) ? ~u : (u | 0x80000000u));
 }
 
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+// The logit of an order (the map inverted; 1 gives a NaN).
+__device__ __forceinline__ float topk_logit(uint32_t ord) {
+  return __builtin_bit_cast(float, (ord & 0x80000000u) ? (ord & 0x7fffffffu) : ~ord);
+}
+
+// 64-bit value of lane l (a uniform lane index): two readlanes.
+__device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int l) {
+  return ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), l) << 32) |
+         (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, l);
+}
+
+__device__ __forceinline__ double readlane_f64(double x, int l) {
+  return __builtin_bit_cast(double, readlane_u64(__builtin_bit_cast(uint64_t, x), l));
+}
+
+// max(v, the value of the lane CTRL names), a DPP row shift; lanes without a
+// source read 0, the smallest value.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_max_u32(uint32_t v) {
+  const uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xf, 0xf, true);
+  return o > v ? o : v;
+}
+
+// The largest value of the wave, the same in every lane: four DPP right
+// shifts by 1, 2, 4, 8 within each row of 16 lanes leave the row's maximum in
+// its last lane (15, 31, 47, 63), read with readlanes.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = dpp_max_u32<0x111>(v);                    // row_shr:1
+  v = dpp_max_u32<0x112>(v);                    // row_shr:2
+  v = dpp_max_u32<0x114>(v);                    // row_shr:4
+  v = dpp_max_u32<0x118>(v);                    // row_shr:8
+  const uint32_t m0 = (uint32_t)__builtin_amdgcn_readlane((int)v, 15);
+  const uint32_t m1 = (uint32_t)__builtin_amdgcn_readlane((int)v, 31);
+  const uint32_t m2 = (uint32_t)__builtin_amdgcn_readlane((int)v, 47);
+  const uint32_t m3 = (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+  return max(max(m0, m1), max(m2, m3));
+}
+
+// k rounds of the router's top-k over the first M orders of each lane (the
+// ones past M are 0): round r takes the largest remaining order and, among
+// the entries that hold it, the lowest expert (first the lowest j, then the
+// lowest lane); its owner lane clears it, and lane r keeps the expert and
+// the order.
+template <int M, int NPL>
+__device__ __forceinline__ void topk_rounds(uint32_t (&ord)[NPL], int k, int lane, int &mine,
+                                            uint32_t &mine_ord) {
+  for (int r = 0; r < k; ++r) {
+    uint32_t best = ord[0];
 #pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const uint32_t lo = __shfl_xor((uint32_t)v, d, 64);
-    const uint32_t hi = __shfl_xor((uint32_t)(v >> 32), d, 64);
-    const uint64_t o = ((uint64_t)hi << 32) | lo;
-    v = o > v ? o : v;
+    for (int j = 1; j < M; ++j) best = max(best, ord[j]);
+    best = wave_max_u32(best);
+    int e = 0;
+    bool found = false;
+#pragma unroll
+    for (int j = 0; j < M; ++j) {
+      const uint64_t hit = __ballot(ord[j] == best);
+      if (!found && hit) {
+        e = 64 * j + __builtin_ctzll(hit);
+        found = true;
+      }
+    }
+    if ((e & 63) == lane) {
+#pragma unroll
+      for (int j = 0; j < M; ++j)
+        if (j == (e >> 6)) ord[j] = 0;
+    }
+    if (lane == r) {
+      mine = e;
+      mine_ord = best;
+    }
   }
-  return v;
 }
 
 // The router's choice for one token's logits row[0 .. E) (E <= 64 NPL), by
-// one whole wave: lane l holds the logits of experts l + 64 j (j < NPL); k
-// rounds each take the largest remaining key. Lane j < k returns the j-th
-// choice and its softmax weight, formed in float64 (the largest chosen
-// logit subtracted, the exponentials summed in rank order by every lane
-// alike) and rounded to float32. The result does not depend on NPL.
+// one whole wave: lane l holds the orders of experts l + 64 j (j < NPL); k
+// rounds each take the largest remaining one, over as many orders per lane
+// as E needs (a uniform branch picks the compiled width). Lane j < k returns
+// the j-th choice and its softmax weight, formed in float64 (the largest
+// chosen logit subtracted, the exponentials summed in rank order by every
+// lane alike) and rounded to float32. The result does not depend on NPL.
 template <int NPL>
 __device__ __forceinline__ void topk_row(const float *row, int E, int k, int lane, int &id,
                                          float &wt) {
-  uint64_t key[NPL];
+  const int npl = (E + 63) >> 6;                // orders in use per lane (NPL is the most)
+  float v[NPL];
 #pragma unroll
-  for (int j = 0; j < NPL; ++j) {
-    const int e = lane + 64 * j;
-    key[j] = e < E ? topk_key(row[e], e) : 0ull;
-  }
+  for (int j = 0; j < NPL; ++j) v[j] = row[min(lane + 64 * j, E - 1)];   // all loads in flight at once
+  uint32_t ord[NPL];
+#pragma unroll
+  for (int j = 0; j < NPL; ++j) ord[j] = lane + 64 * j < E ? topk_ord(v[j]) : 0u;
   int mine = 0;                                 // lane r: the expert chosen in round r
-  for (int r = 0; r < k; ++r) {
-    uint64_t best = 0;
-#pragma unroll
-    for (int j = 0; j < NPL; ++j) best = key[j] > best ? key[j] : best;
-    best = wave_max_u64(best);
-    const int e = (int)~(uint32_t)best;
-    if ((e & 63) == lane) {
-#pragma unroll
-      for (int j = 0; j < NPL; ++j)
-        if (j == (e >> 6)) key[j] = 0;
-    }
-    if (lane == r) mine = e;
-  }
-  const double x = lane < k ? (double)row[mine] : 0.0;
-  const double m = __shfl(x, 0, 64);
+  uint32_t mine_ord = 0;                        // and its order
+  constexpr int M2 = NPL < 2 ? NPL : 2, M4 = NPL < 4 ? NPL : 4, M8 = NPL < 8 ? NPL : 8;
+  if (npl <= 1) topk_rounds<1, NPL>(ord, k, lane, mine, mine_ord);
+  else if (npl <= 2) topk_rounds<M2, NPL>(ord, k, lane, mine, mine_ord);
+  else if (npl <= 4) topk_rounds<M4, NPL>(ord, k, lane, mine, mine_ord);
+  else if (npl <= 8) topk_rounds<M8, NPL>(ord, k, lane, mine, mine_ord);
+  else topk_rounds<NPL, NPL>(ord, k, lane, mine, mine_ord);
+  const double x = lane < k ? (double)topk_logit(mine_ord) : 0.0;   // the chosen logit
+  const double m = readlane_f64(x, 0);
   const double ex = exp(x - m);
   double s = 0.0;
-  for (int j = 0; j < k; ++j) s += __shfl(ex, j, 64);
+  for (int j = 0; j < k; ++j) s += readlane_f64(ex, j);
   id = mine;
   wt = (float)(ex / s);
 }

@@ -59,6 +59,11 @@ def test_route_logits_ties_nan_and_infinities():
     logits[3, 7] = np.inf
     logits[4, :] = 0.0
     logits[5, ::3] = np.nan
+    logits[6, :] = 0.0
+    logits[6, ::2] = -0.0                   # -0 and +0 tie: lower id first
+    logits[7, :] = -1.0
+    logits[7, 1::4] = -0.0
+    logits[7, 3::4] = 0.0
     say("route_logits ties/nan/inf")
     run_route_logits(logits, 5)
 
