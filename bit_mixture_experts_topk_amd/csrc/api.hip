@@ -435,6 +435,119 @@ gnf4_status gnf4_quantize(int32_t format, const float *W, int32_t rows, int32_t 
                        "quantize launch");
 }
 
+// ------------------------------------------------ expert streaming cache
+
+static gnf4_status check_cache_shape(int32_t E, int32_t S) {
+  if (E < 1 || E > GNF4_MAX_EXPERTS)
+    return fail(GNF4_ERR_INVALID_ARG, "E = %d outside [1, %d]", E, GNF4_MAX_EXPERTS);
+  if (S < 1 || S > E) return fail(GNF4_ERR_INVALID_ARG, "S = %d outside [1, E = %d]", S, E);
+  return ok();
+}
+
+size_t gnf4_expert_cache_state_words(int32_t E, int32_t S) {
+  if (E < 1 || E > GNF4_MAX_EXPERTS || S < 1 || S > E) return 0;
+  return (size_t)1 + (size_t)E + 2 * (size_t)S;
+}
+
+size_t gnf4_expert_cache_copies_words(int32_t T, int32_t k, int32_t E, int32_t S) {
+  if (T < 0 || k < 1 || E < 1 || S < 1) return 0;
+  const int64_t m = std::min<int64_t>(std::min<int64_t>((int64_t)T * k, E), S);
+  return (size_t)(1 + 2 * m);
+}
+
+gnf4_status gnf4_expert_cache_reset(int32_t *state, int32_t E, int32_t S, gnf4_stream_t stream) {
+  gnf4_status st = check_cache_shape(E, S);
+  if (st != GNF4_OK) return st;
+  if (!state) return fail(GNF4_ERR_INVALID_ARG, "state is NULL");
+  return device_status(launch_cache_reset(state, E, S, (hipStream_t)stream), "cache reset launch");
+}
+
+gnf4_status gnf4_expert_cache_stage(const int32_t *topk_ids, int32_t T, int32_t k, int32_t E,
+                                    int32_t S, int32_t *state, int32_t *slot_ids, int32_t *copies,
+                                    gnf4_stream_t stream) {
+  gnf4_status st = check_cache_shape(E, S);
+  if (st != GNF4_OK) return st;
+  if (k < 1 || k > 64) return fail(GNF4_ERR_INVALID_ARG, "k = %d outside [1, 64]", k);
+  if (T < 0) return fail(GNF4_ERR_INVALID_ARG, "T = %d is negative", T);
+  if ((int64_t)T * k >= ((int64_t)1 << 31) - 1024)
+    return fail(GNF4_ERR_INVALID_ARG, "T*k too large");
+  if (!state || !copies) return fail(GNF4_ERR_INVALID_ARG, "state or copies is NULL");
+  if (T > 0 && (!topk_ids || !slot_ids))
+    return fail(GNF4_ERR_INVALID_ARG, "topk_ids or slot_ids is NULL");
+  if ((int64_t)S < std::min<int64_t>(E, (int64_t)T * k))
+    return fail(GNF4_ERR_UNSUPPORTED,
+                "S = %d slots cannot hold the up to %lld distinct experts of T*k = %lld ids", S,
+                (long long)std::min<int64_t>(E, (int64_t)T * k), (long long)T * k);
+  return device_status(launch_cache_stage(topk_ids, T * k, E, S, state, slot_ids, copies,
+                                          (hipStream_t)stream),
+                       "cache stage launch");
+}
+
+// Device address of a pinned host (or device) buffer, or NULL if the GPU
+// cannot address it (pageable host memory).
+static const void *device_view(const void *p) {
+  hipPointerAttribute_t at;
+  if (hipPointerGetAttributes(&at, p) != hipSuccess) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  return at.devicePointer;
+}
+
+gnf4_status gnf4_expert_cache_fill(const gnf4_weights *host_w, const gnf4_weights *cache_w,
+                                   const int32_t *copies, int32_t max_copies,
+                                   gnf4_stream_t stream) {
+  gnf4_status st = check_weights(host_w);
+  if (st != GNF4_OK) return st;
+  st = check_weights(cache_w);
+  if (st != GNF4_OK) return st;
+  if (host_w->format != cache_w->format || host_w->N != cache_w->N || host_w->K != cache_w->K)
+    return fail(GNF4_ERR_INVALID_ARG, "host and cache weights differ in format or shape");
+  if (cache_w->E > host_w->E)
+    return fail(GNF4_ERR_INVALID_ARG, "cache has %d slots for %d experts", cache_w->E, host_w->E);
+  if (max_copies < 0 || max_copies > cache_w->E)
+    return fail(GNF4_ERR_INVALID_ARG, "max_copies = %d outside [0, S = %d]", max_copies,
+                cache_w->E);
+  if (!copies) return fail(GNF4_ERR_INVALID_ARG, "copies is NULL");
+  const int fmt = host_w->format;
+  const int64_t N = host_w->N, K = host_w->K;
+  const int64_t nblk = N * (K / 64);
+  const int64_t seg[3] = {N * (K / 2),
+                          fmt == GNF4_NF4 ? nblk * 4 : fmt == GNF4_NF4_DQ ? nblk : N * (K / 32),
+                          fmt == GNF4_NF4_DQ ? nblk / 256 * 4 : 0};
+  const int nseg = fmt == GNF4_NF4_DQ ? 3 : 2;
+  if (fmt == GNF4_NF4_DQ && nblk % 256)
+    return fail(GNF4_ERR_UNSUPPORTED,
+                "NF4_DQ streaming needs N*K/64 = %lld to be a multiple of 256 (whole "
+                "second-level groups per expert)", (long long)nblk);
+  for (int g = 0; g < nseg; ++g)
+    if (seg[g] % 16)
+      return fail(GNF4_ERR_UNSUPPORTED, "an expert's packed segment of %lld bytes is not a "
+                  "multiple of 16", (long long)seg[g]);
+  const void *hs[3] = {host_w->codes, host_w->scales, host_w->scales2};
+  void *cs[3] = {(void *)cache_w->codes, (void *)cache_w->scales, (void *)cache_w->scales2};
+  for (int g = 0; g < nseg; ++g)
+    if (!aligned16(hs[g]) || !aligned16(cs[g]))
+      return fail(GNF4_ERR_INVALID_ARG, "host and cache arrays must be 16-byte aligned");
+  if (max_copies == 0) return ok();
+  CacheFillArgs f{};
+  for (int g = 0; g < nseg; ++g) {
+    f.src[g] = device_view(hs[g]);
+    if (!f.src[g])
+      return fail(GNF4_ERR_INVALID_ARG, "host weights must be pinned host memory (or device "
+                  "memory) that the GPU can address");
+    f.dst[g] = cs[g];
+    f.seg_units[g] = seg[g] / 16;
+    f.units += seg[g] / 16;
+  }
+  f.nseg = nseg;
+  f.chunks = cache_fill_chunks(f.units);
+  f.E = host_w->E;
+  f.S = cache_w->E;
+  f.copies = copies;
+  return device_status(launch_cache_fill(f, max_copies, (hipStream_t)stream), "cache fill launch");
+}
+
 void gnf4_nf4_codebook(float out[16]) {
   if (!out) return;
   for (int i = 0; i < 16; ++i) {

@@ -77,6 +77,20 @@ struct DxArgs {
   float *dA;
 };
 
+// Copy of listed experts' packed bytes into cache slots: segment g of expert
+// e is seg_units[g] 16-byte units at src[g] + e * seg_units[g] (codes,
+// scales, and for NF4_DQ scales2), written to dst[g] + s * seg_units[g].
+struct CacheFillArgs {
+  const void *src[3];
+  void *dst[3];
+  int64_t seg_units[3];
+  int nseg;
+  int64_t units;                 // sum of seg_units
+  int64_t chunks;                // workgroups per copy
+  int E, S;
+  const int32_t *copies;         // [0] count, then (expert, slot) pairs
+};
+
 // SwiGLU (the activation between a mixture-of-experts layer's projections;
 // not described on the pages, the form of the public models the workloads
 // follow): bf16 of silu(g) * u, silu(x) = x / (1 + exp(-x)), rounded once
@@ -346,6 +360,11 @@ hipError_t launch_gemm_dx(const DxArgs &a, hipStream_t s);
 // One token's second projection with the combine fused (T = 1, routed-order
 // rows); gemv_combine_fits says whether that kernel takes the call.
 bool gemv_combine_fits(const GemmArgs &a);
+hipError_t launch_cache_reset(int32_t *state, int32_t E, int32_t S, hipStream_t s);
+hipError_t launch_cache_stage(const int32_t *ids, int32_t n, int32_t E, int32_t S, int32_t *state,
+                              int32_t *slot_ids, int32_t *copies, hipStream_t s);
+hipError_t launch_cache_fill(const CacheFillArgs &f, int32_t max_copies, hipStream_t s);
+int64_t cache_fill_chunks(int64_t units);
 hipError_t launch_gemv_combine(const GemmArgs &a, const float *topk_w, const int32_t *inv,
                                float *out, hipStream_t s);
 hipError_t launch_combine(const float *Y, const int32_t *inv, const float *w, int32_t T,

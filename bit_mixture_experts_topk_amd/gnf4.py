@@ -29,6 +29,8 @@ EXPORTS = ("gnf4_route", "gnf4_route_logits", "gnf4_route_grouped_gemm",
            "gnf4_grouped_gemm_swiglu", "gnf4_grouped_gemm_combine",
            "gnf4_grouped_gemm_dx", "gnf4_swiglu", "gnf4_combine",
            "gnf4_dequant", "gnf4_dequant_experts_bf16", "gnf4_quantize", "gnf4_nf4_codebook",
+           "gnf4_expert_cache_state_words", "gnf4_expert_cache_copies_words",
+           "gnf4_expert_cache_reset", "gnf4_expert_cache_stage", "gnf4_expert_cache_fill",
            "gnf4_last_error",
            "gnf4_build_id")
 
@@ -72,6 +74,13 @@ def lib():
         L.gnf4_dequant.argtypes = [ctypes.POINTER(CWeights), I, P, S]
         L.gnf4_dequant_experts_bf16.argtypes = [ctypes.POINTER(CWeights), P, P, I, P, S]
         L.gnf4_quantize.argtypes = [I, P, I, I, P, P, P, S]
+        L.gnf4_expert_cache_state_words.argtypes = [I, I]
+        L.gnf4_expert_cache_state_words.restype = ctypes.c_size_t
+        L.gnf4_expert_cache_copies_words.argtypes = [I, I, I, I]
+        L.gnf4_expert_cache_copies_words.restype = ctypes.c_size_t
+        L.gnf4_expert_cache_reset.argtypes = [P, I, I, S]
+        L.gnf4_expert_cache_stage.argtypes = [P, I, I, I, I, P, P, P, S]
+        L.gnf4_expert_cache_fill.argtypes = [ctypes.POINTER(CWeights), ctypes.POINTER(CWeights), P, I, S]
         L.gnf4_nf4_codebook.argtypes = [ctypes.POINTER(ctypes.c_float)]
         L.gnf4_nf4_codebook.restype = None
         L.gnf4_last_error.restype = ctypes.c_char_p
@@ -138,18 +147,21 @@ class PackedWeights:
         return n
 
 
-def empty_packed(fmt, E, N, K, device="cuda"):
+def empty_packed(fmt, E, N, K, device="cuda", pin_memory=False):
+    """Uninitialised packed weights; device="cpu", pin_memory=True gives pinned
+    host memory (the host side of the expert streaming cache)."""
     fmt = FORMATS.get(fmt, fmt)
-    codes = torch.empty((E, N, K // 2), dtype=torch.uint8, device=device)
+    kw = dict(device=device, pin_memory=pin_memory)
+    codes = torch.empty((E, N, K // 2), dtype=torch.uint8, **kw)
     scales2 = None
     if fmt == MXFP4:
-        scales = torch.empty((E, N, K // 32), dtype=torch.uint8, device=device)
+        scales = torch.empty((E, N, K // 32), dtype=torch.uint8, **kw)
     elif fmt == NF4:
-        scales = torch.empty((E, N, K // 64), dtype=torch.float32, device=device)
+        scales = torch.empty((E, N, K // 64), dtype=torch.float32, **kw)
     else:
-        scales = torch.empty((E, N, K // 64), dtype=torch.int8, device=device)
+        scales = torch.empty((E, N, K // 64), dtype=torch.int8, **kw)
         nb = E * N * (K // 64)
-        scales2 = torch.empty(((nb + 255) // 256,), dtype=torch.float32, device=device)
+        scales2 = torch.empty(((nb + 255) // 256,), dtype=torch.float32, **kw)
     return PackedWeights(fmt, E, N, K, codes, scales, scales2)
 
 
@@ -389,3 +401,47 @@ def dequant(w, e):
     cw = w.cstruct()
     _check(lib().gnf4_dequant(ctypes.byref(cw), e, _ptr(out), _stream()), "gnf4_dequant")
     return out
+
+
+# ------------------------------------------------ expert streaming cache
+
+def expert_cache_state(E, S):
+    """A reset residency state for S slots over E experts (device int32)."""
+    n = lib().gnf4_expert_cache_state_words(E, S)
+    if n == 0:
+        raise ValueError("invalid cache shape E=%d S=%d" % (E, S))
+    state = torch.empty((n,), dtype=torch.int32, device="cuda")
+    expert_cache_reset(state, E, S)
+    return state
+
+
+def expert_cache_reset(state, E, S):
+    _dev(state, torch.int32, "state")
+    _check(lib().gnf4_expert_cache_reset(_ptr(state), E, S, _stream()), "gnf4_expert_cache_reset")
+
+
+def expert_cache_copies_words(T, k, E, S):
+    return int(lib().gnf4_expert_cache_copies_words(T, k, E, S))
+
+
+def expert_cache_stage(topk_ids, E, S, state, slot_ids=None, copies=None):
+    """Residency decision for int32 topk_ids [T, k]: (slot_ids [T, k], copies)."""
+    _dev(topk_ids, torch.int32, "topk_ids")
+    _dev(state, torch.int32, "state")
+    T, k = topk_ids.shape
+    if slot_ids is None:
+        slot_ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    if copies is None:
+        copies = torch.empty((max(expert_cache_copies_words(T, k, E, S), 1),), dtype=torch.int32,
+                             device="cuda")
+    _check(lib().gnf4_expert_cache_stage(_ptr(topk_ids), T, k, E, S, _ptr(state), _ptr(slot_ids),
+                                         _ptr(copies), _stream()), "gnf4_expert_cache_stage")
+    return slot_ids, copies
+
+
+def expert_cache_fill(host_w, cache_w, copies, max_copies):
+    """Copy the listed experts of host_w (pinned host memory) into cache_w."""
+    _dev(copies, torch.int32, "copies")
+    hw, cw = host_w.cstruct(), cache_w.cstruct()
+    _check(lib().gnf4_expert_cache_fill(ctypes.byref(hw), ctypes.byref(cw), _ptr(copies), max_copies,
+                                        _stream()), "gnf4_expert_cache_fill")

@@ -26,6 +26,8 @@
  *   gnf4_grouped_gemm_dx   dA[p] = dY[p] . W'[e]    (one launch)
  *   gnf4_combine           with unit weights: dX[t] = sum_j dA[inv[t*k+j]]
  *                          for a projection whose rows were gathered
+ * and a layer whose experts stay in host RAM streams them through an HBM
+ * cache before the route: gnf4_expert_cache_stage, gnf4_expert_cache_fill.
  *
  * Conventions for every entry point:
  *  - All array pointers are DEVICE pointers owned by the caller; the library
@@ -308,6 +310,73 @@ gnf4_status gnf4_dequant_experts_bf16(const gnf4_weights *w, const int32_t *expe
  * scales2 float32 [ceil(rows*(K/64)/256)] for NF4_DQ, else ignored. */
 gnf4_status gnf4_quantize(int32_t format, const float *W, int32_t rows, int32_t K,
                           uint8_t *codes, void *scales, float *scales2, gnf4_stream_t stream);
+
+/* Expert streaming from host RAM (Jordan Anderson,
+ * jordananderson-pages.pages.dev, section "grouped-nf4-gemm & experts-4bit":
+ * the demonstration paragraph of the first bullet streams the 4-bit experts
+ * from pinned host memory over PCIe with the fused kernel as the only expert
+ * compute, per-token time being streamed bytes over link speed plus a fixed
+ * per-host cost; the experts4bit-qlora bullets keep hot experts resident and
+ * stream the cold tail). A layer's packed experts stay in pinned host memory
+ * (host_w, E experts) and S of them at a time in an HBM cache laid out as an
+ * ordinary weight tensor with E = S (cache_w). A decode step is:
+ *   gnf4_expert_cache_stage   ids -> slot ids, residency update, copy list
+ *   gnf4_expert_cache_fill    copy the listed experts host -> slots
+ *   gnf4_route / gnf4_route_grouped_gemm ... on the slot ids over S "experts"
+ *   (and the grouped GEMM on cache_w), exactly as on the resident layer: the
+ *   outputs equal those of the resident layer bit for bit, since every routed
+ *   row meets the same expert bytes and the combine sums in the same order.
+ * The residency state is a caller-owned device int32 array of
+ * gnf4_expert_cache_state_words(E, S) words:
+ *   [0] steps staged since the reset
+ *   [1, 1+E)          slot of expert e, -1 if not resident
+ *   [1+E, 1+E+S)      expert in slot s, -1 if empty
+ *   [1+E+S, 1+E+2S)   last step that used slot s, 0 if never
+ * Limits: 1 <= S <= E <= GNF4_MAX_EXPERTS. Calls that share one state must be
+ * ordered on the caller's streams. */
+
+/* Words of the state array (0 for invalid E, S). */
+size_t gnf4_expert_cache_state_words(int32_t E, int32_t S);
+
+/* Words of a copy list for T tokens with k ids each: 1 + 2 * min(T*k, E, S)
+ * (0 for invalid arguments). */
+size_t gnf4_expert_cache_copies_words(int32_t T, int32_t k, int32_t E, int32_t S);
+
+/* gnf4_expert_cache_reset -- empty cache: step 0, no expert resident. One
+ * small fill kernel (no memset node, so it may be graph-captured). */
+gnf4_status gnf4_expert_cache_reset(int32_t *state, int32_t E, int32_t S, gnf4_stream_t stream);
+
+/* gnf4_expert_cache_stage -- one step's residency decision, on the GPU.
+ * The experts the step needs are the distinct ids of topk_ids [T][k] in
+ * [0, E). A needed expert already in a slot is a hit and keeps its slot. The
+ * misses, taken in ascending expert order, go to the slots no hit uses:
+ * empty slots first, then least recently used (oldest last use), ties to the
+ * lower slot; an evicted expert stops being resident. Every used slot is
+ * stamped with the step. Outputs (device int32):
+ *   slot_ids [T][k]   the slot of each id's expert; -1 for ids outside
+ *                     [0, E), which gnf4_route then drops and flags;
+ *   copies            [0] = number of misses m, then m pairs (expert, slot)
+ *                     in ascending expert order; gnf4_expert_cache_copies_words
+ *                     words.
+ * UNSUPPORTED when S < min(E, T*k) (the step's distinct experts might not
+ * fit). T = 0 still advances the step. */
+gnf4_status gnf4_expert_cache_stage(const int32_t *topk_ids, int32_t T, int32_t k, int32_t E,
+                                    int32_t S, int32_t *state, int32_t *slot_ids, int32_t *copies,
+                                    gnf4_stream_t stream);
+
+/* gnf4_expert_cache_fill -- copy the packed bytes of every (expert, slot)
+ * pair of copies from host_w into cache_w: codes, scales and, for NF4_DQ,
+ * the expert's second-level scales (its N*K/64 blocks must be whole groups
+ * of 256). The GPU reads host_w over the host link; its arrays must be
+ * pinned host memory (hipHostMalloc, or torch pin_memory) or device memory,
+ * anything else is INVALID_ARG. Same format, N and K on both sides,
+ * cache_w->E = S <= host_w->E, every per-expert segment a multiple of 16
+ * bytes and every array 16-byte aligned. The launch covers max_copies pairs
+ * (pass 1 + 2*max_copies words of copies; usually min(T*k, E, S)); pairs past
+ * copies[0], or with an expert or slot out of range, copy nothing. */
+gnf4_status gnf4_expert_cache_fill(const gnf4_weights *host_w, const gnf4_weights *cache_w,
+                                   const int32_t *copies, int32_t max_copies,
+                                   gnf4_stream_t stream);
 
 /* The 16 NF4 codebook values used by every kernel (host copy, float32). */
 void gnf4_nf4_codebook(float out[16]);

@@ -17,6 +17,8 @@ precision, written for a reader checking it against the pages by eye:
                the projections, and exact float64 -> bfloat16 rounding.
 * ``backward`` input gradient of the grouped GEMM through the frozen packed
                weights, and its sum over a token's routed copies.
+* ``streaming`` which experts an HBM cache of S slots holds, step by step,
+               when the layer's experts are streamed from host RAM.
 
 Sources. The pages describe a kernel that computes mixture-of-experts matmuls
 directly on 4-bit packed expert weights, one launch for all active experts,
@@ -30,4 +32,4 @@ Parity status per function is listed in each module header. Every function
 here is pinned by at least one test that does not re-run its own formula.
 """
 
-from . import nf4, mxfp4, routing, grouped_gemm, combine, layer, backward  # noqa: F401
+from . import nf4, mxfp4, routing, grouped_gemm, combine, layer, backward, streaming  # noqa: F401

@@ -235,3 +235,58 @@ def test_grouped_gemm_combine_rejects(L):
     assert call(X=0x1004) == INVALID and "16-byte" in gnf4.last_error()
     assert call(out=0x1008) == INVALID
     assert call(T=0, X=None, out=None) == 0                # nothing to do
+
+
+def test_expert_cache_sizes(L):
+    assert L.gnf4_expert_cache_state_words(64, 16) == 1 + 64 + 32
+    assert L.gnf4_expert_cache_state_words(8, 9) == 0                 # S > E
+    assert L.gnf4_expert_cache_state_words(0, 1) == 0
+    assert L.gnf4_expert_cache_copies_words(1, 8, 64, 16) == 17      # min(8, 64, 16) pairs
+    assert L.gnf4_expert_cache_copies_words(4, 8, 64, 16) == 33      # min(32, 64, 16)
+    assert L.gnf4_expert_cache_copies_words(0, 8, 64, 16) == 1
+
+
+def test_expert_cache_stage_rejects(L):
+    p = 0x1000
+
+    def call(T=1, k=8, E=64, S=16, ids=p, state=p, slot_ids=p, copies=p):
+        return L.gnf4_expert_cache_stage(ids, T, k, E, S, state, slot_ids, copies, None)
+
+    assert call(S=0) == INVALID and "S = 0" in gnf4.last_error()
+    assert call(S=65) == INVALID
+    assert call(E=2000, S=16) == INVALID
+    assert call(k=0) == INVALID
+    assert call(T=-1) == INVALID
+    assert call(state=None) == INVALID
+    assert call(ids=None) == INVALID
+    assert call(S=7) == 2 and "distinct" in gnf4.last_error()        # 8 ids may need 8 slots
+    assert call(T=3, k=8, E=20, S=19) == 2                             # min(E, T*k) = 20
+    assert L.gnf4_expert_cache_reset(None, 64, 16, None) == INVALID
+    assert L.gnf4_expert_cache_reset(p, 64, 65, None) == INVALID
+
+
+def test_expert_cache_fill_rejects(L):
+    host = weights(E=8, N=16, K=64)
+    cache = weights(E=4, N=16, K=64, codes=0x3000, scales=0x4000)
+
+    def call(h=None, c=None, copies=0x5000, m=2):
+        return L.gnf4_expert_cache_fill(ctypes.byref(h or host), ctypes.byref(c or cache), copies, m,
+                                        None)
+
+    assert call(c=weights(fmt=2, E=4, N=16, K=64)) == INVALID and "differ" in gnf4.last_error()
+    assert call(c=weights(E=4, N=8, K=64)) == INVALID
+    assert call(c=weights(E=9, N=16, K=64)) == INVALID and "slots" in gnf4.last_error()
+    assert call(m=5) == INVALID and "max_copies" in gnf4.last_error()
+    assert call(m=-1) == INVALID
+    assert call(copies=None) == INVALID
+    # NF4 scales of one expert: 16 rows x 1 block x 4 B = 64 B; N = 3 gives 12 B
+    assert call(h=weights(E=8, N=3, K=64), c=weights(E=4, N=3, K=64, codes=0x3000,
+                                                      scales=0x4000)) == 2
+    assert "multiple of 16" in gnf4.last_error()
+    # NF4_DQ: 16 x 1 blocks per expert is not a whole group of 256
+    dq = dict(fmt=1, E=8, N=16, K=64, scales2=0x6000)
+    assert call(h=weights(**dq), c=weights(**dict(dq, E=4, codes=0x3000, scales=0x4000,
+                                                  scales2=0x7000))) == 2
+    assert "multiple of 256" in gnf4.last_error()
+    assert call(c=weights(E=4, N=16, K=64, codes=0x3000, scales=0x4004)) == INVALID
+    assert call(m=0) == 0                                              # nothing to copy
