@@ -24,6 +24,10 @@ Reported (one JSON line on stdout):
   ffn_layer  the whole FFN layer step (router top-k from logits, gate_up with
              the SwiGLU epilogue, down on its bf16 output, combine) at the
              same T's
+  streaming  decode steps with the packed experts in pinned host memory and
+             an HBM cache of max(k, E/4) expert slots per projection: step
+             time, experts and bytes streamed per step, the link ceilings, and
+             the bytes / link + resident-step model
   cpu_baseline  the float64 CPU oracle (dequant + matmul + combine) timed on
              this host on one decode step of the same workload
 Inputs are resident in device memory before timing starts.
@@ -55,9 +59,9 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-dequant-path", action="store_true",
                     help="skip the dequantize-then-matmul comparison leg")
-    ap.add_argument("--only", choices=["decode", "prefill", "backward"], default=None,
-                    help="run only the forward decode leg, the forward prefill leg, or the "
-                         "backward legs")
+    ap.add_argument("--only", choices=["decode", "prefill", "backward", "streaming"], default=None,
+                    help="run only the forward decode leg, the forward prefill leg, the "
+                         "backward legs, or the host-RAM streaming leg")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
     ap.add_argument("--kernel-only", choices=["decode", "prefill"], default=None,
@@ -532,6 +536,129 @@ def cpu_baseline(cfg, T):
                       "float64 matmul + combine), %.1f s" % (reps, T, len(active), t_total)}
 
 
+class StreamSlot:
+    """One decode step of the layer streamed from host RAM: the residency
+    decision, the fill of the missing experts into both projections' caches,
+    then the step on the slot ids (route fused into the first projection,
+    the second with the combine fused)."""
+
+    def __init__(self, torch, gnf4, cfg, host, cache, state, S, ids, tw, X, Xd):
+        k = cfg.k
+        self.cfg, self.host, self.cache, self.state, self.S = cfg, host, cache, state, S
+        self.ids = torch.from_numpy(np.ascontiguousarray(ids.reshape(1, k))).cuda()
+        self.tw = torch.from_numpy(np.ascontiguousarray(tw.reshape(1, k))).cuda()
+        self.X, self.Xd = X, Xd
+        self.slot_ids = torch.empty((1, k), dtype=torch.int32, device="cuda")
+        self.max_copies = min(k, cfg.E, S)
+        self.copies = torch.zeros((1 + 2 * self.max_copies,), dtype=torch.int32, device="cuda")
+        self.r = gnf4.route_buffers(1, k, S)
+        self.Y = [torch.empty((k, pw.N), dtype=torch.float32, device="cuda") for pw in cache]
+        self.out = torch.empty((1, cache[-1].N), dtype=torch.float32, device="cuda")
+
+    def run(self, gnf4, resident=None):
+        k = self.cfg.k
+        if resident is not None:                 # the same step on the HBM-resident layer
+            r, _ = gnf4.route_grouped_gemm(self.ids, resident[0], self.X, out=self.rr, Y=self.Y[0])
+            gnf4.grouped_gemm_combine(resident[1], self.Xd, r, self.tw, 1, k, self.out, Y=self.Y[1])
+            return
+        gnf4.expert_cache_stage(self.ids, self.cfg.E, self.S, self.state, self.slot_ids, self.copies)
+        for h, c in zip(self.host, self.cache):
+            gnf4.expert_cache_fill(h, c, self.copies, self.max_copies)
+        r, _ = gnf4.route_grouped_gemm(self.slot_ids, self.cache[0], self.X, out=self.r, Y=self.Y[0])
+        gnf4.grouped_gemm_combine(self.cache[1], self.Xd, r, self.tw, 1, k, self.out, Y=self.Y[1])
+
+
+def streaming(torch, gnf4, cfg, base, steps):
+    """Decode steps (T = 1) of the layer with its packed experts in pinned host
+    memory and an HBM cache of S = max(k, E/4) expert slots per projection,
+    over a sequence of tokens routed by the workload's router. Returns the
+    step time, the bytes streamed per step, the hit rate, the link ceilings
+    (the fill kernel on all-miss copies; a pinned host-to-device copy) and
+    the same steps on the HBM-resident layer."""
+    import synth
+    E, k = cfg.E, cfg.k
+    S = max(k, E // 4)
+    host = []
+    for pw in base.projs:
+        host.append(type(pw)(pw.format, pw.E, pw.N, pw.K, pw.codes.cpu().pin_memory(),
+                             pw.scales.cpu().pin_memory(),
+                             pw.scales2.cpu().pin_memory() if pw.scales2 is not None else None))
+    cache = [gnf4.empty_packed(cfg.fmt, S, pw.N, pw.K) for pw in base.projs]
+    state = gnf4.expert_cache_state(E, S)
+    n = max(16, steps)
+    ids, tw = synth.routing_inputs(cfg, n, seed=700)
+    X = torch.from_numpy(synth.token_inputs(cfg, n, seed=700).view(np.int16)).cuda()
+    Xd = torch.from_numpy(synth.activations(cfg, k, cfg.inter, synth.T_X_DOWN, 700, 1)
+                          .view(np.int16)).cuda()
+    slots = [StreamSlot(torch, gnf4, cfg, host, cache, state, S, ids[t], tw[t], X[t:t + 1], Xd)
+             for t in range(n)]
+    chain = torch.cuda.CUDAGraph()
+    for sl in slots[:2]:
+        sl.run(gnf4)                             # warm the launch path outside capture
+    torch.cuda.synchronize()
+    with torch.cuda.graph(chain):
+        for sl in slots:
+            sl.run(gnf4)
+    torch.cuda.synchronize()
+    chain.replay()                               # one pass to reach a steady cache
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    chain.replay()
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / n
+    misses = np.array([int(sl.copies[0].item()) for sl in slots])
+    per_expert = sum(pw.nbytes() // pw.E for pw in base.projs)
+    n_need = np.array([np.unique(ids[t]).size for t in range(n)])
+    streamed = float(misses.mean()) * per_expert
+
+    # the same steps with the layer resident in HBM
+    for sl in slots:
+        sl.rr = gnf4.route_buffers(1, k, E)
+    res = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(res):
+        for sl in slots:
+            sl.run(gnf4, resident=base.projs)
+    torch.cuda.synchronize()
+    res.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    res.replay()
+    torch.cuda.synchronize()
+    dt_res = (time.perf_counter() - t0) / n
+
+    # link ceilings for k experts' bytes: the fill kernel with every copy a
+    # miss, and a pinned host-to-device copy of the same bytes
+    m = min(k, S)
+    cp = torch.tensor([m] + [v for i in range(m) for v in (i, i)], dtype=torch.int32, device="cuda")
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for h, c in zip(host, cache):
+        gnf4.expert_cache_fill(h, c, cp, m)
+    torch.cuda.synchronize()
+    reps = 5
+    a.record()
+    for _ in range(reps):
+        for h, c in zip(host, cache):
+            gnf4.expert_cache_fill(h, c, cp, m)
+    b.record()
+    torch.cuda.synchronize()
+    fill_gbs = reps * m * per_expert / (a.elapsed_time(b) * 1e-3) / 1e9
+    src = torch.empty((m * per_expert,), dtype=torch.uint8).pin_memory()
+    dst = torch.empty((m * per_expert,), dtype=torch.uint8, device="cuda")
+    dst.copy_(src, non_blocking=True)
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(reps):
+        dst.copy_(src, non_blocking=True)
+    b.record()
+    torch.cuda.synchronize()
+    copy_gbs = reps * m * per_expert / (a.elapsed_time(b) * 1e-3) / 1e9
+    del slots, chain, res, cache, host, src, dst
+    torch.cuda.empty_cache()
+    return dict(S=S, n=n, dt=dt, dt_res=dt_res, streamed=streamed, per_expert=per_expert,
+                misses=float(misses.mean()), needed=float(n_need.mean()), fill_gbs=fill_gbs,
+                copy_gbs=copy_gbs)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -680,6 +807,9 @@ def main():
             torch.cuda.empty_cache()
         out["backward"] = bw
 
+    if len(cfg.projs) > 1 and args.only in (None, "streaming") and T_dec * cfg.k <= 64:
+        out["streaming"] = streaming(torch, gnf4, cfg, base, min(args.steps, 256))
+
     if args.calib_copy:
         a = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
         b = torch.empty_like(a)
@@ -786,6 +916,24 @@ def main():
                       "weights), sum of each token's routed copies (gnf4_combine, unit weights); "
                       "dequant_path: bf16 decode of the routed experts + torch.bmm / torch.mm")
         result["backward"] = b
+    if out.get("streaming"):
+        st = out["streaming"]
+        link = st["fill_gbs"]
+        model = st["streamed"] / (link * 1e9) + st["dt_res"]
+        result["streaming"] = {
+            "T": 1, "cache_slots": st["S"], "steps": st["n"],
+            "step_us": round(st["dt"] * 1e6, 2), "resident_step_us": round(st["dt_res"] * 1e6, 2),
+            "experts_needed_per_step": round(st["needed"], 3),
+            "experts_streamed_per_step": round(st["misses"], 3),
+            "hit_rate": round(1 - st["misses"] / st["needed"], 4),
+            "streamed_MB_per_step": round(st["streamed"] / 1e6, 3),
+            "fill_link_GBps": round(st["fill_gbs"], 2), "h2d_copy_GBps": round(st["copy_gbs"], 2),
+            "model_step_us": round(model * 1e6, 2),
+            "step_over_model": round(st["dt"] / model, 3),
+            "steps_desc": ("gnf4_expert_cache_stage, gnf4_expert_cache_fill of both projections "
+                           "from pinned host memory, then the decode step on the slot ids; model = "
+                           "streamed bytes / fill_link_GBps + resident_step_us"),
+        }
     if not args.no_cpu and decode_ok:
         result["cpu_baseline"] = cpu_baseline(cfg, T_dec)
     print(json.dumps(result), flush=True)
