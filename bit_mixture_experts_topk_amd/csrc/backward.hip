@@ -450,55 +450,68 @@ __global__ __launch_bounds__(kDxThreads, 2) void mfma_dx_kernel(DxArgs a, int n_
 
 // ================================================ few rows per expert
 
-// gemv_dx_kernel: one workgroup per item (expert e, up to MT routed rows of
-// its segment, 32 output columns). Wave w takes the 64-row groups
-// R = w, w + 4, w + 8, ... of the weight rows, lane l row 64 R + l: it reads
-// the 16 code bytes of the item's columns in that row (one 128-bit load),
-// the row's scale and dY[p][n] of its MT rows p, and accumulates s * c[q] in
-// float32 with s = dY[p][n] * absmax (exact codebook values, no bf16
-// rounding of the weights). Each wave reduces its 32 MT partial sums over
-// its 64 lanes by halving exchanges (xor 32, 16, 8, 4, 2, then 1), after
-// which lanes 2j, 2j + 1 hold column j; the four waves' sums meet in LDS.
-//
-// Rows advance in batches of U per lane (4, or 2 for four rows per item),
-// two batches in flight: every load of the main loop is unconditional and in
-// range; the remaining groups (including a partial last one) run after it
-// with each lane's row clamped to N - 1 and its contribution zeroed.
 constexpr int kGemvDxMaxRows = 64;   // routed rows (T*k) up to which the GEMV path is used
 
-template <int FMT, int MT>
-__global__ __launch_bounds__(kDxThreads, 2) void gemv_dx_kernel(DxArgs a, int n_items) {
+// gemv_dx_kernel: the few-row path. One workgroup of 8 waves per item
+// (expert e, up to MT routed rows of its segment, 32 * LPR output columns).
+// LPR lanes share a weight row: lane l reads the 16 code bytes of chunk
+// l % LPR of the item (32 columns) in row RPG * R + l / LPR, RPG = 64 / LPR,
+// for the row groups R = w, w + 8, ... of wave w, so one 128-bit load covers
+// RPG rows with LPR lanes on consecutive bytes of each. The lane also reads
+// the row's scale and dY[p][n] of its MT rows p, and accumulates
+// s * c[q] in float32 with s = dY[p][n] * absmax (exact codebook values, no
+// bf16 rounding of the weights; MXFP4 decodes exactly with its e8m0 scale).
+// Rows advance in batches of U per lane, two batches in flight: every load
+// of the main loop is unconditional and in range; the remaining groups
+// (including a partial last one) run after it with each lane's row clamped
+// to N - 1 and its contribution zeroed. Each wave reduces over the RPG lanes
+// of each chunk by halving exchanges; the 8 waves' sums meet in LDS, added
+// in wave order.
+constexpr int kDxGemvThreads = 512;
+
+template <int FMT, int MT, int LPR>
+__global__ __launch_bounds__(kDxGemvThreads, MT == 1 ? 4 : 2) void gemv_dx_kernel(DxArgs a) {
+  using Set0 = std::integral_constant<int, 0>;
+  using Set1 = std::integral_constant<int, 1>;
   constexpr bool kNF = FMT != GNF4_MXFP4;
   constexpr bool kDQ = FMT == GNF4_NF4_DQ;
-  constexpr int U = MT >= 4 ? 2 : 4;              // rows per lane per batch
+  constexpr int kWaves = kDxGemvThreads / 64;
+  constexpr int U = MT == 1 ? 2 : (MT >= 4 ? 2 : 4);   // rows per lane per batch
+  constexpr int RPG = 64 / LPR;                   // weight rows per load (one per LPR lanes)
+  constexpr int BC = 32 * LPR;                    // output columns per item
   __shared__ float tab[kNF ? kDxPairWords : 1];
-  __shared__ float red[4][MT][32];
+  __shared__ float red[kWaves][MT][BC];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar offsets
   const int N = a.w.N, K = a.w.K, E = a.w.E;
-  // items: expert by expert, row block, then 32-column chunk (fastest), so
-  // the 8 chunks that share a 128-byte code line are neighbours; they are
+  // items: expert by expert, row block, then 64-column block (fastest),
   // dealt to the XCDs in contiguous runs of the real item count
-  const int nchunk = K >> 5;
-  const int total = dx_total_tiles<MT>(a.offsets, E, nchunk, lane);
+  const int nchunk = K >> 5, nblk = (nchunk + LPR - 1) / LPR;
+  const int total = dx_total_tiles<MT>(a.offsets, E, nblk, lane);
   const int per = (total + 7) >> 3;
   const int bid = blockIdx.x, jb = bid >> 3;
   const int logical = (bid & 7) * per + jb;
   if (jb >= per || logical >= total) return;      // whole workgroup
   int e, start, mtiles;
-  dx_find_tile<MT>(a.offsets, E, nchunk, logical, lane, e, start, mtiles);
+  dx_find_tile<MT>(a.offsets, E, nblk, logical, lane, e, start, mtiles);
   if (e < 0) return;
   const int local = logical - start;
-  const int rb = local / nchunk, kc = local - rb * nchunk;
+  const int rb = local / nblk, cb = local - rb * nblk;
   const int seg0 = a.offsets[e];
   const int count = a.offsets[e + 1] - seg0;
   const int prow0 = rb * MT;                      // first row of the item within the segment
 
+  // this lane's chunk; MXFP4 with an odd chunk count: the last block's
+  // second chunk is past K (loads clamped to chunk nchunk - 1, no sums kept)
+  const int par = lane & (LPR - 1);
+  const int kc_raw = LPR * cb + par;
+  const bool chunk_ok = kc_raw < nchunk;
+  const uint32_t kc = (uint32_t)min(kc_raw, nchunk - 1);
   const uint32_t half_k = (uint32_t)K >> 1, nkb = (uint32_t)K >> 6, ngrp = (uint32_t)K >> 5;
-  const uint32_t col0 = (uint32_t)kc * 32u;
+  const uint32_t col0 = kc * 32u;
   const uint32_t kb = col0 >> 6;
   const uint32_t scale_row = FMT == GNF4_NF4 ? nkb * 4u : kDQ ? nkb : ngrp;
-  const uint32_t scale_col = FMT == GNF4_NF4 ? kb * 4u : kDQ ? kb : (uint32_t)kc;
+  const uint32_t scale_col = FMT == GNF4_NF4 ? kb * 4u : kDQ ? kb : kc;
   const int64_t erow = (int64_t)e * N;
   const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
       (void *)(a.w.codes + erow * half_k), (short)0, (int)((uint32_t)N * half_k), kDxBufferDword3);
@@ -515,26 +528,26 @@ __global__ __launch_bounds__(kDxThreads, 2) void gemv_dx_kernel(DxArgs a, int n_
 #pragma unroll
   for (int m = 0; m < MT; ++m) dyrow[m] = (uint32_t)min(prow0 + m, count - 1) * (uint32_t)N * 2u;
 
-  // this wave's 64-row groups: R = wave + 4 i; the first `nfull` are whole
-  const int groups = (N + 63) >> 6;
-  const int nfull_w = ((N >> 6) - wave + 3) >> 2 > 0 ? ((N >> 6) - wave + 3) >> 2 : 0;
-  const int nall_w = (groups - wave + 3) >> 2 > 0 ? (groups - wave + 3) >> 2 : 0;
+  // this wave's 32-row groups: R = wave + 8 i; the first `nfull_w` are whole
+  const int rl = lane / LPR;                      // row within a group
+  const int groups = (N + RPG - 1) / RPG;
+  const int nfull_w = (N / RPG - wave + kWaves - 1) / kWaves > 0 ? (N / RPG - wave + kWaves - 1) / kWaves : 0;
+  const int nall_w = (groups - wave + kWaves - 1) / kWaves > 0 ? (groups - wave + kWaves - 1) / kWaves : 0;
   const int nb = nfull_w / U;                     // full batches of this wave
 
   uint4 cq[2][U];
   uint32_t sq[2][U], yq[2][U][MT];
   float tq[2][U];
-  // iterations i0 .. i0 + U - 1 of this wave into register set S; `clamp`
-  // for iterations that may pass N (rows clamped per lane)
   auto issue = [&](auto SET, int i0, bool clamp) {
     constexpr int S = decltype(SET)::value;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const uint32_t g0 = (uint32_t)(64 * (wave + 4 * (i0 + u)));    // first row of the group
-      uint32_t row = g0 + (uint32_t)lane;
+      const uint32_t g0 = (uint32_t)(RPG * (wave + kWaves * (i0 + u)));   // first row of the group
+      uint32_t row = g0 + (uint32_t)rl;
       if (clamp) row = min(row, (uint32_t)N - 1u);
-      const uint32_t vc = (clamp ? row : (uint32_t)lane) * half_k + col0 / 2u;
-      const uint32_t vs = (clamp ? row : (uint32_t)lane) * scale_row + scale_col;
+      const uint32_t lr = clamp ? row : (uint32_t)rl;
+      const uint32_t vc = lr * half_k + col0 / 2u;
+      const uint32_t vs = lr * scale_row + scale_col;
       const uint32_t sc = clamp ? 0u : g0 * half_k, ss = clamp ? 0u : g0 * scale_row;
       cq[S][u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rc, vc, sc, 0));
       if constexpr (FMT == GNF4_NF4) sq[S][u] = __builtin_amdgcn_raw_buffer_load_b32(rs, vs, ss, 0);
@@ -546,8 +559,8 @@ __global__ __launch_bounds__(kDxThreads, 2) void gemv_dx_kernel(DxArgs a, int n_
       }
 #pragma unroll
       for (int m = 0; m < MT; ++m)
-        yq[S][u][m] = __builtin_amdgcn_raw_buffer_load_b16(
-            rd, dyrow[m] + (clamp ? row : (uint32_t)lane) * 2u, clamp ? 0u : g0 * 2u, 0);
+        yq[S][u][m] = __builtin_amdgcn_raw_buffer_load_b16(rd, dyrow[m] + lr * 2u,
+                                                           clamp ? 0u : g0 * 2u, 0);
     }
   };
 
@@ -566,7 +579,7 @@ __global__ __launch_bounds__(kDxThreads, 2) void gemv_dx_kernel(DxArgs a, int n_
       if constexpr (FMT == GNF4_NF4) sc = __builtin_bit_cast(float, sq[S][u]);
       else if constexpr (kDQ) sc = (float)(int8_t)sq[S][u] * tq[S][u];
       else sc = e8m0_to_f32(sq[S][u]);
-      const int row = 64 * (wave + 4 * (i0 + u)) + lane;
+      const int row = RPG * (wave + kWaves * (i0 + u)) + rl;
       const bool live = !clamp || (i0 + u < nall_w && row < N);
       float sv[MT];
 #pragma unroll
@@ -608,10 +621,10 @@ __global__ __launch_bounds__(kDxThreads, 2) void gemv_dx_kernel(DxArgs a, int n_
     }
   };
 
-  using Set0 = std::integral_constant<int, 0>;
-  using Set1 = std::integral_constant<int, 1>;
   if (nb > 0) issue(Set0{}, 0, false);            // in flight while the table fills
-  if constexpr (kNF) fill_dx_table(tab, tid);
+  if constexpr (kNF) {
+    if (tid < kDxThreads) fill_dx_table(tab, tid);
+  }
   __syncthreads();
   for (int b = 0; b < nb; b += 2) {
     issue(Set1{}, U * min(b + 1, nb - 1), false);
@@ -626,45 +639,56 @@ __global__ __launch_bounds__(kDxThreads, 2) void gemv_dx_kernel(DxArgs a, int n_
     consume(Set0{}, i0, true);
   }
 
-  // reduce over the wave's 64 lanes: at mask d the lane keeps the half of its
-  // values selected by (lane & d) and adds the partner's copy of that half;
-  // values are ordered v = j * MT + m, so the halvings leave lanes 2j, 2j + 1
-  // with column j = (lane >> 1) & 31 of every row
+  // reduce over the RPG lanes of each chunk (lane bits 5 .. log2 LPR): values
+  // are ordered v = j * MT + m, so the halvings leave the lane with chunk par
+  // and group row rl holding columns (32 / RPG) * rl + i, i < 32 / RPG
+  constexpr int KEEP = 32 / RPG;                  // columns per lane after the halvings
   float v[32 * MT];
 #pragma unroll
   for (int j = 0; j < 32; ++j)
 #pragma unroll
-    for (int m = 0; m < MT; ++m) v[j * MT + m] = acc[m][j];
+    for (int m = 0; m < MT; ++m) v[j * MT + m] = chunk_ok ? acc[m][j] : 0.0f;
   halve<16 * MT>(v, 32, lane);
   halve<8 * MT>(v, 16, lane);
   halve<4 * MT>(v, 8, lane);
-  halve<2 * MT>(v, 4, lane);
-  halve<MT>(v, 2, lane);
+  if constexpr (LPR <= 4) halve<2 * MT>(v, 4, lane);
+  if constexpr (LPR <= 2) halve<MT>(v, 2, lane);
 #pragma unroll
-  for (int m = 0; m < MT; ++m) v[m] += __shfl_xor(v[m], 1, 64);
-  const int jc = (lane >> 1) & 31;
-  if ((lane & 1) == 0) {
+  for (int i = 0; i < KEEP; ++i)
 #pragma unroll
-    for (int m = 0; m < MT; ++m) red[wave][m][jc] = v[m];
-  }
+    for (int m = 0; m < MT; ++m) red[wave][m][32 * par + KEEP * rl + i] = v[i * MT + m];
   __syncthreads();
-  // threads 0 .. 32 MT - 1: row m = tid / 32, column tid % 32, waves in order
-  if (tid < 32 * MT) {
-    const int m = tid >> 5, j = tid & 31;
-    const float sum = ((red[0][m][j] + red[1][m][j]) + red[2][m][j]) + red[3][m][j];
-    if (prow0 + m < count) a.dA[(int64_t)(seg0 + prow0 + m) * K + col0 + j] = sum;
+  // threads 0 .. BC MT - 1: row m = tid / BC, column tid % BC, waves in order
+  for (int t = tid; t < BC * MT; t += kDxGemvThreads) {
+    const int m = t / BC, c = t % BC;
+    float sum = red[0][m][c];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) sum += red[w][m][c];
+    const int col = BC * cb + c;
+    if (prow0 + m < count && col < K) a.dA[(int64_t)(seg0 + prow0 + m) * K + col] = sum;
   }
 }
 
-template <int FMT, int MT>
+template <int FMT, int MT, int LPR>
 static hipError_t gemv_dx_go(const DxArgs &a, hipStream_t s) {
   const int rows = a.rows;
-  const int nchunk = a.w.K / 32;
-  const int64_t items = ((int64_t)(rows + MT - 1) / MT + std::min<int>(a.w.E, rows)) * nchunk;
+  const int nblk = (a.w.K / 32 + LPR - 1) / LPR;
+  const int64_t items = ((int64_t)(rows + MT - 1) / MT + std::min<int>(a.w.E, rows)) * nblk;
   const int64_t grid = (items + 7) / 8 * 8;
-  hipLaunchKernelGGL((gemv_dx_kernel<FMT, MT>), dim3((unsigned)grid), dim3(kDxThreads), 0, s, a,
-                     (int)items);
+  hipLaunchKernelGGL((gemv_dx_kernel<FMT, MT, LPR>), dim3((unsigned)grid), dim3(kDxGemvThreads), 0, s,
+                     a);
   return hipGetLastError();
+}
+
+// Lanes per weight row: 4 (128-column items, half the lines per load of 2)
+// when that still gives every CU an item, else 2 (measured: 4 wins on the
+// Qwen3-235B shape, 2 on the OLMoE, Qwen3-30B and gpt-oss shapes).
+template <int FMT, int MT>
+static hipError_t gemv_dx_pick(const DxArgs &a, hipStream_t s) {
+  const int64_t experts = std::min<int64_t>(a.w.E, a.rows);
+  const int64_t items4 = experts * ((a.w.K / 32 + 3) / 4);
+  if (items4 >= device_cu_count()) return gemv_dx_go<FMT, MT, 4>(a, s);
+  return gemv_dx_go<FMT, MT, 2>(a, s);
 }
 
 template <int FMT, int RT, int CT>
@@ -688,9 +712,9 @@ static hipError_t dx_pick(const DxArgs &a, hipStream_t s) {
   const int64_t experts = std::min<int64_t>(a.w.E, a.rows);
   const int64_t mean = experts > 0 ? (a.rows + experts - 1) / experts : 0;
   if (a.rows <= kGemvDxMaxRows) {
-    if (mean <= 1) return gemv_dx_go<FMT, 1>(a, s);
-    if (mean <= 2) return gemv_dx_go<FMT, 2>(a, s);
-    if (mean <= 4) return gemv_dx_go<FMT, 4>(a, s);
+    if (mean <= 1) return gemv_dx_pick<FMT, 1>(a, s);
+    if (mean <= 2) return gemv_dx_pick<FMT, 2>(a, s);
+    if (mean <= 4) return gemv_dx_pick<FMT, 4>(a, s);
   }
   if (mean <= 16) return dx_go<FMT, 1, 4>(a, s);
   if (mean <= 32) return dx_go<FMT, 2, 4>(a, s);
