@@ -1010,6 +1010,7 @@ __global__ __launch_bounds__(kThreads, 2) void mfma16_kernel(GemmArgs a, int n_t
     /* accumulates in the MFMAs */                                                        \
     bf16x8_t fb[2][2];                                                                    \
     GNF4_DECODE(Q, B, 0, fb[0], scl[0]);                                                  \
+    __builtin_amdgcn_s_setprio(1); /* priority while issuing the MFMAs (about 2 % faster) */ \
     f32x4_t Pp[2];                                                                        \
     _Pragma("unroll") for (int ct = 0; ct < 4; ++ct) {                                   \
       __builtin_amdgcn_sched_barrier(0);                                                  \
@@ -1036,6 +1037,7 @@ __global__ __launch_bounds__(kThreads, 2) void mfma16_kernel(GemmArgs a, int n_t
       }                                                                                   \
     }                                                                                     \
     __builtin_amdgcn_sched_barrier(0);                                                    \
+    __builtin_amdgcn_s_setprio(0);                                                       \
     /* stage S + 2 reuses this stage's slot once block 1 is decoded */                   \
     if ((B) == 1) GNF4_LOAD_STAGE((S) + 2, Q);                                            \
     if constexpr (kLut) {                                                                 \
