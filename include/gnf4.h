@@ -384,7 +384,7 @@ void gnf4_nf4_codebook(float out[16]);
 /* Thread-local text describing the last non-OK status ("" if none). */
 const char *gnf4_last_error(void);
 
-/* Source revision and target of this build, e.g. "gnf4 1a2b3c4 gfx950". */
+/* Source revision and target of the compiled library, e.g. "gnf4 1a2b3c4 gfx950". */
 const char *gnf4_build_id(void);
 
 #ifdef __cplusplus
