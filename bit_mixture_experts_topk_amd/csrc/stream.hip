@@ -40,20 +40,39 @@ __global__ __launch_bounds__(256) void cache_reset_kernel(int32_t *__restrict__ 
 __global__ __launch_bounds__(kStageThreads) void cache_stage_kernel(
     const int32_t *__restrict__ ids, int n, int E, int S, int32_t *__restrict__ state,
     int32_t *__restrict__ slot_ids, int32_t *__restrict__ copies) {
+  __shared__ int slot_of[GNF4_MAX_EXPERTS];    // the state, read once into LDS
+  __shared__ int expert_of[GNF4_MAX_EXPERTS];
+  __shared__ int last_used[GNF4_MAX_EXPERTS];
   __shared__ int need[GNF4_MAX_EXPERTS];       // expert needed by this step
-  __shared__ int now[GNF4_MAX_EXPERTS];        // its slot after the step
   __shared__ int inuse[GNF4_MAX_EXPERTS];      // slot holds a hit
   __shared__ uint64_t key[GNF4_MAX_EXPERTS];   // eviction order of the free slots
   __shared__ int wtot[kStageThreads / 64];
   __shared__ int s_step;
-  int32_t *slot_of = state + 1, *expert_of = state + 1 + E, *last_used = state + 1 + E + S;
+  int32_t *g_slot_of = state + 1, *g_expert_of = state + 1 + E, *g_last_used = state + 1 + E + S;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
+  // One memory round trip: the whole state and this thread's first ids.
+  constexpr int kIds = 4;                       // ids held per thread (more are read again)
+  int idr[kIds];
+#pragma unroll
+  for (int r = 0; r < kIds; ++r) {
+    const int i = tid + r * kStageThreads;
+    idr[r] = i < n ? ids[i] : -1;
+  }
+  for (int i = tid; i < 1 + E + 2 * S; i += kStageThreads) {
+    const int w = state[i];
+    if (i == 0) s_step = w + 1;
+    else if (i < 1 + E) slot_of[i - 1] = w;
+    else if (i < 1 + E + S) expert_of[i - 1 - E] = w;
+    else last_used[i - 1 - E - S] = w;
+  }
   for (int e = tid; e < E; e += kStageThreads) need[e] = 0;
   for (int s = tid; s < S; s += kStageThreads) inuse[s] = 0;
-  if (tid == 0) s_step = state[0] + 1;
   __syncthreads();
-  for (int i = tid; i < n; i += kStageThreads) {
+#pragma unroll
+  for (int r = 0; r < kIds; ++r)
+    if ((unsigned)idr[r] < (unsigned)E) need[idr[r]] = 1;
+  for (int i = tid + kIds * kStageThreads; i < n; i += kStageThreads) {
     const int e = ids[i];
     if ((unsigned)e < (unsigned)E) need[e] = 1;
   }
@@ -98,10 +117,10 @@ __global__ __launch_bounds__(kStageThreads) void cache_stage_kernel(
       for (int i = tid; i < P; i += kStageThreads) {
         const int ixj = i ^ j;
         if (ixj > i) {
-          const uint64_t a = key[i], b = key[ixj];
-          if ((a > b) == ((i & kk) == 0)) {
-            key[i] = b;
-            key[ixj] = a;
+          const uint64_t x = key[i], y = key[ixj];
+          if ((x > y) == ((i & kk) == 0)) {
+            key[i] = y;
+            key[ixj] = x;
           }
         }
       }
@@ -110,32 +129,40 @@ __global__ __launch_bounds__(kStageThreads) void cache_stage_kernel(
   }
 
   // Miss m takes the m-th slot of the eviction order (there are enough when
-  // S >= the step's distinct experts, which the host checks).
+  // S >= the step's distinct experts, which the host checks). The changed
+  // words go to the state in HBM, the new slot of every needed expert to LDS
+  // (need[] now holds it).
   int slot = cur;
   if (miss) {
     const uint64_t kk = m < P ? key[m] : ~0ull;
     slot = kk == ~0ull ? -1 : (int)(uint32_t)kk;
     if (slot >= 0) {
       const int old = expert_of[slot];
-      if ((unsigned)old < (unsigned)E) slot_of[old] = -1;
-      expert_of[slot] = e;
-      slot_of[e] = slot;
-      last_used[slot] = step;
+      if ((unsigned)old < (unsigned)E) g_slot_of[old] = -1;
+      g_expert_of[slot] = e;
+      g_slot_of[e] = slot;
+      g_last_used[slot] = step;
     }
     copies[1 + 2 * m] = e;
     copies[2 + 2 * m] = slot;
   } else if (hit) {
-    last_used[cur] = step;
+    g_last_used[cur] = step;
   }
-  if (e < E) now[e] = slot;
+  __syncthreads();                              // every read of need[] done
+  if (e < E) need[e] = slot;
   if (tid == 0) {
     state[0] = step;
     copies[0] = M;
   }
   __syncthreads();
-  for (int i = tid; i < n; i += kStageThreads) {
+#pragma unroll
+  for (int r = 0; r < kIds; ++r) {
+    const int i = tid + r * kStageThreads;
+    if (i < n) slot_ids[i] = (unsigned)idr[r] < (unsigned)E ? need[idr[r]] : -1;
+  }
+  for (int i = tid + kIds * kStageThreads; i < n; i += kStageThreads) {
     const int id = ids[i];
-    slot_ids[i] = (unsigned)id < (unsigned)E ? now[id] : -1;
+    slot_ids[i] = (unsigned)id < (unsigned)E ? need[id] : -1;
   }
 }
 
