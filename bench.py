@@ -533,7 +533,19 @@ def cpu_baseline(cfg, T):
     return {"value": round(byts / t_total / 1e9, 4), "unit": "GB/s", "cores": threads,
             "kind": "oracle",
             "sample": "%d full decode step(s) (T=%d, %d routed experts, both projections: dequant + "
-                      "float64 matmul + combine), %.1f s" % (reps, T, len(active), t_total)}
+                      "float64 matmul + combine), %.1f s" % (reps, T, len(active), t_total),
+            "cpu_model": cpu_model()}
+
+
+def cpu_model():
+    """The host CPU's model name from /proc/cpuinfo (None if unreadable)."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 class StreamSlot:
