@@ -537,6 +537,18 @@ def cpu_baseline(cfg, T):
             "cpu_model": cpu_model()}
 
 
+def packed_digest(layer):
+    """sha256 of the layer's packed bytes (every projection's codes, scales and
+    second-level scales, in order), read back from the device."""
+    import hashlib
+    h = hashlib.sha256()
+    for pw in layer.projs:
+        for t in (pw.codes, pw.scales, pw.scales2):
+            if t is not None:
+                h.update(t.contiguous().cpu().numpy().tobytes())
+    return h.hexdigest()
+
+
 def cpu_model():
     """The host CPU's model name from /proc/cpuinfo (None if unreadable)."""
     try:
@@ -835,7 +847,7 @@ def main():
                                                      T_dec if decode_ok else "-",
                                                      T_pre if prefill_ok else "-"),
           "global_batch": T_dec if decode_ok else T_pre, "layer_packed_MB": round(layer_bytes / 1e6, 2),
-          "parallelism": "single GPU"}
+          "packed_sha256": packed_digest(base), "parallelism": "single GPU"}
     result["config"] = wl
     if "decode" in out:
         d = out["decode"]
