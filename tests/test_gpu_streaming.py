@@ -47,6 +47,7 @@ def step_ids(rng, hot, E, T, k, bad):
     (200, 50, 8, 6, 20, 6),
     (8, 2, 1, 2, 30, 7),
     (5, 5, 0, 3, 3, 8),                # T = 0: the step still advances
+    (1024, 1024, 80, 64, 3, 9),        # 5120 ids: more than the 4096 a thread block holds
 ])
 def test_stage_matches_oracle(E, S, T, k, steps, seed):
     g = gnf4()
