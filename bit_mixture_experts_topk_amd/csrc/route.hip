@@ -50,13 +50,25 @@ __global__ __launch_bounds__(THREADS) void route_kernel(
   }
   __syncthreads();
 
-  // Histogram of valid ids; ids outside [0, E) only raise the flag.
-  for (int f = tid; f < n; f += THREADS) {
-    int e = THREADS == 64 ? id0 : ids[f];
-    if ((unsigned)e < (unsigned)E)
-      atomicAdd(&cursor[e], 1);
-    else
-      sbad = 1;
+  // Histogram of valid ids; ids outside [0, E) only raise the flag. Eight
+  // loads per thread are issued before their atomics, so the memory latency
+  // is paid once per eight tiles rather than once per tile.
+  constexpr int kHB = THREADS == 64 ? 1 : 8;
+  for (int f0 = 0; f0 < n; f0 += THREADS * kHB) {
+    int ev[kHB];
+#pragma unroll
+    for (int u = 0; u < kHB; ++u) {
+      const int f = f0 + u * THREADS + tid;
+      ev[u] = THREADS == 64 ? id0 : (f < n ? ids[f] : 0);
+    }
+#pragma unroll
+    for (int u = 0; u < kHB; ++u) {
+      if (f0 + u * THREADS + tid >= n) continue;
+      if ((unsigned)ev[u] < (unsigned)E)
+        atomicAdd(&cursor[ev[u]], 1);
+      else
+        sbad = 1;
+    }
   }
   __syncthreads();
 
@@ -105,10 +117,15 @@ __global__ __launch_bounds__(THREADS) void route_kernel(
   // Within a wave, lanes holding the same expert are found by matching the id
   // bit by bit with ballots; the rank among them is the count of matching
   // lower lanes. Lower waves' counts for that expert come from wcnt.
+  // The ids of the tile two ahead are loaded before a tile is processed.
   const uint64_t lower = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  int e_cur = THREADS == 64 ? id0 : (tid < n ? ids[tid] : -1);
+  int e_nxt = THREADS == 64 ? -1 : (THREADS + tid < n ? ids[THREADS + tid] : -1);
   for (int base = 0; base < n; base += THREADS) {
     const int f = base + tid;
-    const int e = THREADS == 64 ? id0 : (f < n ? ids[f] : -1);
+    const int e = e_cur;
+    e_cur = e_nxt;
+    if (THREADS > 64) e_nxt = f + 2 * THREADS < n ? ids[f + 2 * THREADS] : -1;
     const bool valid = (unsigned)e < (unsigned)E;
     uint64_t match = __ballot(valid);
     for (int b = 0; b < nbits; ++b) {
