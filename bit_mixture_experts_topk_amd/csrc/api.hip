@@ -556,6 +556,12 @@ void gnf4_nf4_codebook(float out[16]) {
   }
 }
 
+void gnf4_nf4_codebook_bf16(uint16_t out[16], float *scale) {
+  if (out)
+    for (int i = 0; i < 16; ++i) out[i] = (uint16_t)nf4_bf16_bits((uint32_t)i);
+  if (scale) *scale = kNF4Scale;
+}
+
 const char *gnf4_last_error(void) { return g_err; }
 
 const char *gnf4_build_id(void) { return "gnf4 " GNF4_REVISION " gfx950"; }

@@ -21,9 +21,26 @@ static constexpr uint32_t kNF4Bits[16] = {
     0xbdba7869u, 0x00000000u, 0x3da2fb01u, 0x3e24cadfu, 0x3e7c04dau, 0x3ead0336u,
     0x3ee1a4b5u, 0x3f1007a9u, 0x3f3913b0u, 0x3f800000u};
 
-// bfloat16 of each codebook value (round to nearest even of kNF4Bits).
+// bfloat16 bits of a float32 value (round to nearest even).
 __host__ __device__ constexpr uint32_t bf16_rne(uint32_t f) {
   return (f + 0x7fffu + ((f >> 16) & 1u)) >> 16;
+}
+
+// The bf16 operand of the NF4 contractions. bf16 keeps 8 significant bits,
+// so each codebook value enters the products with a fixed rounding error,
+// and these errors add up over K in every output. The kernels use
+// bf16(s * c[q]) instead and scale each 64-value partial by absmax / s:
+//   y = sum_blocks fp32(absmax * (1/s)) * sum_k x[k] * bf16(s * c[q[k]]).
+// s is the float32 in [1, 2) that minimizes the mean over the 16 codes of
+// (bf16(fp32(s * c[q])) / s - c[q])^2: 2.9x below the unscaled codebook's
+// (s = 1), which the error of an output grows with (a sum of x * absmax *
+// rounding error over K). The extra float32 rounding of absmax / s is 2^-24
+// relative.
+static constexpr float kNF4Scale = 1.43700611591339111328125f;   // 0x3fb7efd1
+static constexpr float kNF4InvScale = 1.0f / kNF4Scale;
+
+__host__ __device__ constexpr uint32_t nf4_bf16_bits(uint32_t q) {
+  return bf16_rne(__builtin_bit_cast(uint32_t, __builtin_bit_cast(float, kNF4Bits[q & 15u]) * kNF4Scale));
 }
 
 // e2m1 magnitudes by the low three code bits.
@@ -270,11 +287,11 @@ __device__ __forceinline__ void topk_row(const float *row, int E, int k, int lan
   wt = (float)(ex / s);
 }
 
-// NF4 byte -> two bf16 codebook values as one dword (element 2i, the high
-// nibble, in the low half): the operand layout of v_dot2 and of the MFMA
-// fragments, where consecutive K values sit low half first.
+// NF4 byte -> two bf16 operand values (nf4_bf16_bits) as one dword (element
+// 2i, the high nibble, in the low half): the operand layout of v_dot2 and of
+// the MFMA fragments, where consecutive K values sit low half first.
 __host__ __device__ constexpr uint32_t nf4_pair(uint32_t byte) {
-  return bf16_rne(kNF4Bits[byte >> 4]) | (bf16_rne(kNF4Bits[byte & 15u]) << 16);
+  return nf4_bf16_bits(byte >> 4) | (nf4_bf16_bits(byte & 15u) << 16);
 }
 
 // LDS decode table of NF4 byte pairs, replicated once per lane of a wave so
@@ -283,17 +300,17 @@ __host__ __device__ constexpr uint32_t nf4_pair(uint32_t byte) {
 constexpr int kLutCopies = 64;
 constexpr int kLutWords = 256 * kLutCopies;
 
-// bf16 of codebook value q (0..15) without memory: the 16 values packed into
-// four 64-bit constants.
+// bf16 operand value of code q (0..15) without memory: the 16 values packed
+// into four 64-bit constants.
 __device__ __forceinline__ uint32_t nf4_bf16(uint32_t q) {
-  constexpr uint64_t w0 = (uint64_t)bf16_rne(kNF4Bits[0]) | ((uint64_t)bf16_rne(kNF4Bits[1]) << 16) |
-                          ((uint64_t)bf16_rne(kNF4Bits[2]) << 32) | ((uint64_t)bf16_rne(kNF4Bits[3]) << 48);
-  constexpr uint64_t w1 = (uint64_t)bf16_rne(kNF4Bits[4]) | ((uint64_t)bf16_rne(kNF4Bits[5]) << 16) |
-                          ((uint64_t)bf16_rne(kNF4Bits[6]) << 32) | ((uint64_t)bf16_rne(kNF4Bits[7]) << 48);
-  constexpr uint64_t w2 = (uint64_t)bf16_rne(kNF4Bits[8]) | ((uint64_t)bf16_rne(kNF4Bits[9]) << 16) |
-                          ((uint64_t)bf16_rne(kNF4Bits[10]) << 32) | ((uint64_t)bf16_rne(kNF4Bits[11]) << 48);
-  constexpr uint64_t w3 = (uint64_t)bf16_rne(kNF4Bits[12]) | ((uint64_t)bf16_rne(kNF4Bits[13]) << 16) |
-                          ((uint64_t)bf16_rne(kNF4Bits[14]) << 32) | ((uint64_t)bf16_rne(kNF4Bits[15]) << 48);
+  constexpr uint64_t w0 = (uint64_t)nf4_bf16_bits(0) | ((uint64_t)nf4_bf16_bits(1) << 16) |
+                          ((uint64_t)nf4_bf16_bits(2) << 32) | ((uint64_t)nf4_bf16_bits(3) << 48);
+  constexpr uint64_t w1 = (uint64_t)nf4_bf16_bits(4) | ((uint64_t)nf4_bf16_bits(5) << 16) |
+                          ((uint64_t)nf4_bf16_bits(6) << 32) | ((uint64_t)nf4_bf16_bits(7) << 48);
+  constexpr uint64_t w2 = (uint64_t)nf4_bf16_bits(8) | ((uint64_t)nf4_bf16_bits(9) << 16) |
+                          ((uint64_t)nf4_bf16_bits(10) << 32) | ((uint64_t)nf4_bf16_bits(11) << 48);
+  constexpr uint64_t w3 = (uint64_t)nf4_bf16_bits(12) | ((uint64_t)nf4_bf16_bits(13) << 16) |
+                          ((uint64_t)nf4_bf16_bits(14) << 32) | ((uint64_t)nf4_bf16_bits(15) << 48);
   const uint64_t w = (q < 8u) ? ((q < 4u) ? w0 : w1) : ((q < 12u) ? w2 : w3);
   return (uint32_t)(w >> ((q & 3u) * 16u)) & 0xffffu;
 }
@@ -307,7 +324,7 @@ __device__ __forceinline__ void fill_nf4_lut_256(uint32_t *lut, int tid) {
   const uint32_t lo = nf4_bf16((uint32_t)tid >> 4) << 16;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
-    const uint32_t v = bf16_rne(kNF4Bits[i]) | lo;
+    const uint32_t v = nf4_bf16_bits(i) | lo;
     *reinterpret_cast<uint4 *>(lut + (tid + 256 * i) * 4) = make_uint4(v, v, v, v);
   }
 }

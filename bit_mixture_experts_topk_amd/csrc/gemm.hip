@@ -96,7 +96,9 @@ template <int FMT, int U, int C, bool GLU = false>
 __device__ __forceinline__ void gemv_load_rows(const GemmArgs &a, const GemvGeom &g, int e, int n0,
                                                GemvRows<U, C> &R) {
   const int N = a.w.N, K = a.w.K;
-  const int rmax = N - 1 - n0;
+  // Callers pass n0 < N (an item past the last row issues no loads); the
+  // clamp keeps every row offset non-negative regardless.
+  const int rmax = max(N - 1 - n0, 0);
   const int64_t row0 = (int64_t)e * N + n0;
   const uint8_t *cb = a.w.codes + row0 * (K / 2);
   uint32_t r[U], ch[C];
@@ -214,9 +216,11 @@ __device__ __forceinline__ void gemv_dot(const GemvGeom &g, const uint32_t *lut,
       }
       // A lane past the last chunk adds exactly zero. The mask is applied to
       // both factors with bitwise ANDs rather than a branch, which would let
-      // the compiler sink this row's loads into it.
+      // the compiler sink this row's loads into it. NF4: the table holds
+      // bf16(s * c), so the block's absmax enters divided by s.
       const uint32_t keep = g.li + c * g.L < g.KCH ? 0xffffffffu : 0u;
-      const float s = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, R.sc[u][c]) & keep);
+      const float sc = kLut ? R.sc[u][c] * kNF4InvScale : R.sc[u][c];
+      const float s = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, sc) & keep);
 #pragma unroll
       for (int t = 0; t < MT; ++t)
         acc[t] = __builtin_fmaf(s, __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, part[t]) & keep),
@@ -665,9 +669,13 @@ __global__ __launch_bounds__(kGemvCombineThreads, 2) void gemv1c_kernel(GemmArgs
   }
   __syncthreads();
 
-  // task q = (row block q / k, copy q % k)
+  // task q = (row block q / k, copy q % k). The last workgroup may hold
+  // fewer than G row blocks (ceil(N / rows per block) need not be a multiple
+  // of G): a task whose block starts at or past N loads nothing (the branch
+  // is uniform over the wave) and its rows are never stored.
   for (int q = wave; q < G * k; q += kWaves) {
     const int b = q / k, j = q - b * k;
+    if ((nb0 + b) * g.rows_per_item >= N) continue;
     const int p = s_p[j];
     uint32_t x[1][C][16];
     gemv_load_x_row<C>(a, g, max(p, 0), x);
@@ -911,17 +919,21 @@ __global__ __launch_bounds__(kThreads, 2) void mfma16_kernel(GemmArgs a, int n_t
       sn[ct] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rs, soff[ct], 32 * (W), 0)); \
     }                                                                                     \
   }
-  // NF4_DQ: the window's absmax as float32, int8 value times its group's scale
+  // The window's absmax divided by the operand scale s (the table holds
+  // bf16(s * c)); NF4_DQ forms the float32 absmax first, int8 value times its
+  // group's scale
 #define GNF4_TAKE_WINDOW()                                                                \
   _Pragma("unroll") for (int ct = 0; ct < 4; ++ct) {                                     \
+    float a0_, a1_;                                                                       \
     if constexpr (kDQ) {                                                                  \
-      sw[ct].x = __builtin_bit_cast(uint32_t, (float)(int8_t)(dn[ct] & 0xffu) *           \
-                                                  __builtin_bit_cast(float, tn[ct].x));   \
-      sw[ct].y = __builtin_bit_cast(uint32_t, (float)(int8_t)((dn[ct] >> 8) & 0xffu) *    \
-                                                  __builtin_bit_cast(float, tn[ct].y));   \
+      a0_ = (float)(int8_t)(dn[ct] & 0xffu) * __builtin_bit_cast(float, tn[ct].x);        \
+      a1_ = (float)(int8_t)((dn[ct] >> 8) & 0xffu) * __builtin_bit_cast(float, tn[ct].y); \
     } else {                                                                              \
-      sw[ct] = sn[ct];                                                                    \
+      a0_ = __builtin_bit_cast(float, sn[ct].x);                                          \
+      a1_ = __builtin_bit_cast(float, sn[ct].y);                                          \
     }                                                                                     \
+    sw[ct].x = __builtin_bit_cast(uint32_t, a0_ * kNF4InvScale);                          \
+    sw[ct].y = __builtin_bit_cast(uint32_t, a1_ * kNF4InvScale);                          \
   }
 #define GNF4_LOAD_SBYTES(KB, SB)                                                          \
   _Pragma("unroll") for (int ct = 0; ct < 4; ++ct)                                       \

@@ -29,6 +29,7 @@ EXPORTS = ("gnf4_route", "gnf4_route_logits", "gnf4_route_grouped_gemm",
            "gnf4_grouped_gemm_swiglu", "gnf4_grouped_gemm_combine",
            "gnf4_grouped_gemm_dx", "gnf4_swiglu", "gnf4_combine",
            "gnf4_dequant", "gnf4_dequant_experts_bf16", "gnf4_quantize", "gnf4_nf4_codebook",
+           "gnf4_nf4_codebook_bf16",
            "gnf4_expert_cache_state_words", "gnf4_expert_cache_copies_words",
            "gnf4_expert_cache_reset", "gnf4_expert_cache_stage", "gnf4_expert_cache_fill",
            "gnf4_last_error",
@@ -83,6 +84,8 @@ def lib():
         L.gnf4_expert_cache_fill.argtypes = [ctypes.POINTER(CWeights), ctypes.POINTER(CWeights), P, I, S]
         L.gnf4_nf4_codebook.argtypes = [ctypes.POINTER(ctypes.c_float)]
         L.gnf4_nf4_codebook.restype = None
+        L.gnf4_nf4_codebook_bf16.argtypes = [ctypes.POINTER(ctypes.c_uint16), ctypes.POINTER(ctypes.c_float)]
+        L.gnf4_nf4_codebook_bf16.restype = None
         L.gnf4_last_error.restype = ctypes.c_char_p
         L.gnf4_build_id.restype = ctypes.c_char_p
         for name in ("gnf4_route", "gnf4_grouped_gemm", "gnf4_combine", "gnf4_dequant", "gnf4_quantize"):
@@ -103,6 +106,15 @@ def nf4_codebook():
     buf = (ctypes.c_float * 16)()
     lib().gnf4_nf4_codebook(buf)
     return [buf[i] for i in range(16)]
+
+
+def nf4_codebook_bf16():
+    """(bf16 bits of the 16 NF4 operand values, their scale s): the values
+    are bf16(s * c[q]) and the kernels scale partial sums by absmax / s."""
+    buf = (ctypes.c_uint16 * 16)()
+    sc = ctypes.c_float()
+    lib().gnf4_nf4_codebook_bf16(buf, ctypes.byref(sc))
+    return [buf[i] for i in range(16)], sc.value
 
 
 def _check(status, what):

@@ -123,9 +123,11 @@ gnf4_status gnf4_route(const int32_t *topk_ids, int32_t T, int32_t k, int32_t E,
  * activations) and A[p] = X[p] when gather = 0 (X is bf16 [T*k][K], already
  * in routed order, e.g. the second projection's input). Rows p >= offsets[E]
  * of Y are not written. W' is the packed weight decoded in registers: NF4 as
- * bf16(codebook) with the float32 absmax applied to each 64-value partial
- * sum, MXFP4 exactly (e2m1 * 2^(s-127)). The route outputs (offsets, perm,
- * active, n_active) must come from gnf4_route with the same T, k, E.
+ * the bf16 operand values bf16(s * codebook) with fp32(absmax * (1/s))
+ * applied to each 64-value partial sum (gnf4_nf4_codebook_bf16 gives the
+ * values and s), MXFP4 exactly (e2m1 * 2^(e8m0 - 127)). The route outputs
+ * (offsets, perm, active, n_active) must come from gnf4_route with the same
+ * T, k, E.
  * X: uint16 bf16 bits, 16-byte aligned. Y: float32 [T*k][N], 16-byte aligned.
  * The path (wavefront GEMV for decode, LDS-staged bf16 MFMA for prefill) is
  * chosen from T*k on the host; nothing is read back from the device. */
@@ -380,6 +382,16 @@ gnf4_status gnf4_expert_cache_fill(const gnf4_weights *host_w, const gnf4_weight
 
 /* The 16 NF4 codebook values used by every kernel (host copy, float32). */
 void gnf4_nf4_codebook(float out[16]);
+
+/* The bf16 operand values of the NF4 contractions (forward GEMV and MFMA
+ * paths): out[q] = bf16 bits of fp32(s * c[q]) (nearest even), and *scale =
+ * s, the float32 in [1, 2) minimizing the mean over q of
+ * (bf16(s * c[q]) / s - c[q])^2; the kernels scale each 64-value partial
+ * sum by fp32(absmax * fp32(1/s)). Reading of the pages' in-register
+ * codebook decode (section cited at the top): a bf16 operand of the
+ * codebook scaled so that its rounding error is smallest. Either pointer
+ * may be NULL. */
+void gnf4_nf4_codebook_bf16(uint16_t out[16], float *scale);
 
 /* Thread-local text describing the last non-OK status ("" if none). */
 const char *gnf4_last_error(void);

@@ -48,6 +48,37 @@ def test_codebook_matches_oracle(L):
     assert np.array_equal(got.view(np.uint32), nf4.codebook().view(np.uint32))
 
 
+def _bf16_rne(f32):
+    u = np.ascontiguousarray(f32, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+def test_bf16_operand_codebook_is_the_least_squares_scale(L):
+    """The NF4 contractions use bf16(s * c[q]) with the absmax divided by s.
+    Search every float32 s in [1, 2) from the oracle's codebook: the
+    library's s is the one whose operand values, divided by s, deviate least
+    from the codebook in mean square, and its 16 values are bf16 of
+    fp32(s * c[q])."""
+    vals, s_lib = gnf4.nf4_codebook_bf16()
+    cb = nf4.codebook().astype(np.float32)
+    cb64 = cb.astype(np.float64)
+    best_m, best_s = np.inf, None
+    one = int(np.float32(1.0).view(np.uint32))
+    for start in range(0, 1 << 23, 1 << 20):
+        s = (np.arange(start, start + (1 << 20), dtype=np.uint32) + one).view(np.float32)
+        r = (_bf16_rne((s[:, None] * cb[None, :]).astype(np.float32)).astype(np.uint32) << 16)
+        d = r.view(np.float32).astype(np.float64) / s.astype(np.float64)[:, None] - cb64[None, :]
+        m = (d * d).mean(axis=1)
+        i = int(np.argmin(m))
+        if m[i] < best_m:
+            best_m, best_s = float(m[i]), s[i]
+    assert np.float32(s_lib) == best_s, (s_lib, best_s)
+    assert np.array_equal(np.array(vals, dtype=np.uint16), _bf16_rne(np.float32(s_lib) * cb))
+    # the unscaled codebook's mean square is larger by more than 2.5x
+    d1 = (_bf16_rne(cb).astype(np.uint32) << 16).view(np.float32).astype(np.float64) - cb64
+    assert np.mean(d1 * d1) > 2.5 * best_m
+
+
 def weights(fmt=0, E=4, N=8, K=64, codes=0x1000, scales=0x2000, scales2=None):
     return gnf4.CWeights(fmt, E, N, K, codes, scales, scales2)
 

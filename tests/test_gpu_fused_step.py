@@ -1,15 +1,42 @@
 """The fused entry points of the decode step give what the separate calls
 give: gnf4_route_grouped_gemm equals gnf4_route followed by the first
 projection (routing arrays and Y or H bit for bit), on the one-launch path
-(T = 1) and on the two-launch path (T > 1)."""
+(T = 1) and on the two-launch path (T > 1); and every output of each fused
+call is also compared with the float64 oracle directly (routing, top-k ids
+and weights bit for bit, Y and out at the per-call bars, H at the layer
+bar)."""
 
 import numpy as np
 import pytest
 import torch
 
 import synth
+from oracle import combine as ocombine
+from oracle import grouped_gemm as ogemm
+from oracle import layer as olayer
+from oracle import routing
 
-from .gpu_util import bits_to_device, gnf4, oracle_pack, packed_to_device, say
+from .gpu_util import bits_to_device, check_route, gnf4, oracle_pack, packed_to_device, say
+from .tolerance import assert_within, assert_within_h, assert_within_layer
+
+
+def oracle_first_projection(fmt, packed, X, ids, E, N, K, k, swiglu, got):
+    """got (Y float32, or H bf16 bits with the SwiGLU epilogue) against the
+    oracle's grouped GEMM of the same routing."""
+    codes, scales, scales2 = packed
+    r_ref = routing.route(ids, E)
+    nv = int(r_ref["offsets"][-1])
+    Y_ref = ogemm.grouped_gemm(fmt, codes, scales, scales2, X, 1, r_ref["offsets"], r_ref["perm"],
+                               k, N, K)[:nv]
+    if not swiglu:
+        assert_within(got[:nv], Y_ref, "Y vs oracle")
+        return r_ref
+    H_ref = olayer.swiglu(Y_ref, N // 2)
+    Hg = (got[:nv].view(np.uint16).astype(np.uint32) << 16).view(np.float32)
+    Hr = (H_ref.astype(np.uint32) << 16).view(np.float32)
+    assert_within_h(Hg, Hr, "H vs oracle")
+    return r_ref
+
 
 pytestmark = pytest.mark.gpu
 
@@ -65,6 +92,9 @@ def test_route_grouped_gemm_equals_separate_calls(fmt, swiglu, E, N, K, T, k, id
                           b.view(np.uint32) if b.dtype == np.float32 else b), "outputs differ"
     if ids_kind == "bad":
         assert int(r["bad"].item()) == 1 and nv == T * k - 2
+    r_ref = oracle_first_projection(fmt, (codes, scales, scales2), case["X"], ids, E, N, K, k, swiglu,
+                                    got.cpu().numpy())
+    check_route(r, r_ref, T * k)
 
 
 @pytest.mark.parametrize("fmt", ["nf4", "nf4_dq", "mxfp4"])
@@ -79,6 +109,8 @@ def test_route_grouped_gemm_equals_separate_calls(fmt, swiglu, E, N, K, T, k, id
     (1024, 64, 256, 1, 64, "distinct"),   # k = 64
     (6, 64, 6144, 1, 5, "distinct"),      # K = 6144: four chunks per lane
     (3, 64, 256, 1, 1, "distinct"),       # k = 1
+    (8, 200, 256, 1, 2, "distinct"),      # 25 row blocks, 4 per workgroup: the last holds 1
+    (8, 3000, 2048, 1, 2, "distinct"),    # 750 row blocks, 4 per workgroup: the last holds 2
     (8, 64, 8192, 1, 4, "distinct"),      # K = 8192: the largest K of the one-launch path
     (8, 64, 8256, 1, 5, "distinct"),      # K past it: two launches (MFMA GEMM, then combine)
     (8, 256, 256, 7, 2, "duplicates"),    # T > 1: two launches
@@ -103,6 +135,11 @@ def test_grouped_gemm_combine_equals_separate_calls(fmt, E, N, K, T, k, ids_kind
     a = got.cpu().numpy()[:T]
     b = ref.cpu().numpy()[:T]
     assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), int((a != b).sum())
+    r_ref = routing.route(ids, E)
+    check_route(r, r_ref, T * k)
+    Y_ref = ogemm.grouped_gemm(fmt, codes, scales, scales2, case["X"], 0, r_ref["offsets"],
+                               r_ref["perm"], k, N, K)
+    assert_within(a, ocombine.combine(Y_ref, r_ref["inv"], case["tw"], T, k), "out vs oracle")
 
 
 @pytest.mark.parametrize("fmt", ["nf4", "mxfp4"])
@@ -144,3 +181,11 @@ def test_route_logits_grouped_gemm_equals_separate_calls(fmt, swiglu, E, N, K, T
     b = ref.cpu().numpy()[:nv]
     assert np.array_equal(a.view(np.uint32) if a.dtype == np.float32 else a,
                           b.view(np.uint32) if b.dtype == np.float32 else b), "outputs differ"
+    ids_o, w_o = olayer.topk_softmax(logits, k)
+    assert np.array_equal(r["topk_ids"].cpu().numpy(), ids_o), "top-k ids vs oracle"
+    w = r["topk_w"].cpu().numpy()
+    assert np.array_equal(np.isnan(w), np.isnan(w_o))
+    assert np.array_equal(w[~np.isnan(w)], w_o[~np.isnan(w_o)]), "top-k weights vs oracle"
+    ro = oracle_first_projection(fmt, (codes, scales, scales2), case["X"], ids_o, E, N, K, k, swiglu,
+                                 got.cpu().numpy())
+    check_route(r, ro, T * k)

@@ -28,7 +28,8 @@ SHAPES = [
     (5, 96, 2880, 1, 4),       # K = 2880 (45 NF4 / 90 MXFP4 blocks)
     (16, 336, 768, 8, 8),      # 64 rows, K = 768
     (8, 320, 512, 40, 2),      # prefill, ragged M and N tails, several tiles
-    (4, 256, 1024, 200, 2),    # prefill, 400 rows over 4 experts (BM = 128)
+    (4, 256, 1024, 200, 2),    # prefill, 400 rows over 4 experts: ~100 rows each, so
+                               # one whole 64-row tile and a ragged tail per expert
     (3, 130, 2880, 37, 3),     # prefill, K = 2880, ragged N
 ]
 
@@ -118,9 +119,9 @@ def one_hot_case(fmt, T, k, E=4, N=96, K=256):
 @pytest.mark.parametrize("T,k", [(3, 2), (60, 2)])      # decode and prefill path
 def test_one_hot_rows_are_exact(fmt, T, k):
     """A one-hot activation row selects one weight per output. NF4 enters the
-    product as bf16(codebook) times the float32 absmax, so the output must be
-    exactly fp32(absmax * bf16(c)); MXFP4 decodes exactly, so the output is
-    the dequantized weight itself."""
+    product as the bf16 operand value bf16(s * c) times fp32(absmax * (1/s)),
+    so the output must be exactly fp32(fp32(absmax * fp32(1/s)) * bf16(s * c));
+    MXFP4 decodes exactly, so the output is the dequantized weight itself."""
     g = gnf4()
     case, X, cols = one_hot_case(fmt, T, k)
     E, N, K = case["W"].shape
@@ -131,9 +132,11 @@ def test_one_hot_rows_are_exact(fmt, T, k):
     r = g.route(torch.from_numpy(ids).cuda(), E)
     Y = g.grouped_gemm(pw, bits_to_device(X), 1, r, T, k).cpu().numpy()
     ref = routing.route(ids, E)
-    cb = nf4.codebook()
+    vals, s_op = g.nf4_codebook_bf16()          # pinned to the oracle codebook on the CPU
+    cb = (np.float32(s_op) * nf4.codebook()).astype(np.float32)
     cb_bf16 = (np.ascontiguousarray(cb).view(np.uint32) + 0x7FFF + ((cb.view(np.uint32) >> 16) & 1)) >> 16
     cb_bf16 = (cb_bf16 << 16).astype(np.uint32).view(np.float32)
+    inv_s = np.float32(1.0) / np.float32(s_op)
     for t in range(T):
         for j in range(k):
             e = int(ids[t, j])
@@ -147,7 +150,7 @@ def test_one_hot_rows_are_exact(fmt, T, k):
                 else:
                     a = nf4.dq_absmax(scales, scales2).reshape(E, N, K // 64)[e][:, col // 64]
                 q = nf4.unpack(codes[e].reshape(-1)).reshape(N, K)[:, col]
-                expect = (a * cb_bf16[q]).astype(np.float32)
+                expect = ((a * inv_s).astype(np.float32) * cb_bf16[q]).astype(np.float32)
             # exact values (a zero may come out as +0 where the weight is -0)
             assert np.array_equal(Y[p], expect), (t, j)
 

@@ -13,7 +13,7 @@ from oracle import layer as olayer
 from oracle import routing
 
 from .gpu_util import bits_to_device, check_route, gnf4, oracle_pack, packed_to_device, say
-from .tolerance import assert_within_layer
+from .tolerance import assert_within_h, assert_within_layer
 
 pytestmark = pytest.mark.gpu
 
@@ -136,7 +136,7 @@ def test_ffn_layer_end_to_end(fmt, T, fused):
     # near a bf16 rounding boundary may land one bf16 step away
     fg = (H.cpu().numpy().view(np.uint16)[:T * k].astype(np.uint32) << 16).view(np.float32)
     fr = (H_ref.astype(np.uint32) << 16).view(np.float32)
-    assert np.max(np.abs(fg - fr)) <= 2.0 ** -6 * np.max(np.abs(fr))
+    assert_within_h(fg, fr, "H %s T=%d fused=%d" % (fmt, T, fused))
 
 
 @pytest.mark.parametrize("fmt", ["nf4", "nf4_dq", "mxfp4"])
