@@ -1,21 +1,26 @@
 """Benchmark of the grouped 4-bit MoE layer step on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config olmoe]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config qwen235]
 
 A step is one pass of the hot path over one batch of synthetic tokens:
 gnf4_route -> gnf4_grouped_gemm (gate_up, rows gathered from the token
 activations) -> gnf4_grouped_gemm (down, input already in routed order) ->
-gnf4_combine. Decode steps (T = 1) and prefill steps (the workload's largest
-T) are captured as HIP graphs, one per input slot and one chain holding a step
-per slot (as a model captures its layers), and replayed; successive steps
-rotate over input slots and over copies of the layer's packed weights so that
-no step finds its weights in the 256 MB Infinity Cache.
+gnf4_combine (at T = 1 two launches: the routing fused into the gate_up GEMV,
+the combine into the down GEMV). The default workload is the
+Qwen3-235B-A22B-shaped layer, decode T = 1 and prefill T = 4096. Exactly K
+consecutive steps are captured as HIP graphs (at most 256 steps per graph,
+replayed back to back on one stream) and timed with HIP events on that
+stream; successive steps rotate over input slots and over copies of the
+layer's packed weights so that no step finds its weights in the 256 MB
+Infinity Cache. The step time therefore does not depend on K.
 
 Reported (one JSON line on stdout):
   value      decode packed-weight GB/s of the whole step (codes + scales of
              the experts the step routes to, both projections, / step time)
   roofline   the decode gate_up GEMM kernel: algorithmic packed bytes per
-             launch / its mean duration from HIP events on the launch stream
+             launch / its mean duration from HIP events on the launch stream,
+             beside the achievable read rate for the same bytes
+             (gnf4_read_probe, a plain streaming read timed the same way)
   prefill    TFLOP/s of the prefill step and the roofline of its gate_up
              MFMA kernel (algorithmic flops 2*rows*N*K per launch)
   dequant_path  the same step through the dequantize-then-matmul path the
@@ -55,7 +60,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", default="olmoe")
+    ap.add_argument("--config", default="qwen235")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-dequant-path", action="store_true",
                     help="skip the dequantize-then-matmul comparison leg")
@@ -192,7 +197,6 @@ class StepSlot:
             self.Xd = torch.from_numpy(synth.activations(cfg, T * k, down.K, synth.T_X_DOWN, seed, T)
                                        .view(np.int16)).cuda()
         self.out = torch.empty((T, cfg.projs[-1].N), dtype=torch.float32, device="cuda")
-        self.graph = None
 
     def run(self, gnf4):
         cfg, T, k = self.layer.cfg, self.T, self.layer.cfg.k
@@ -211,18 +215,6 @@ class StepSlot:
                                       Y=self.Y[1])
         else:
             gnf4.combine(self.Y[0], r["inv"], self.tw, T, k, self.out)
-
-    def capture(self, torch, gnf4):
-        s = torch.cuda.Stream()
-        s.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(s):
-            self.run(gnf4)                     # warm the launch path outside capture
-        torch.cuda.current_stream().wait_stream(s)
-        torch.cuda.synchronize()
-        self.graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(self.graph):
-            self.run(gnf4)
-        torch.cuda.synchronize()
 
     def weight_bytes(self):
         return sum(self.n_active * pw.nbytes() // pw.E for pw in self.layer.projs)
@@ -348,34 +340,109 @@ class DequantBackwardSlot(BackwardSlot):
         gnf4.combine(self.dA[0], r["inv"], self.ones, T, k, self.dX)
 
 
-def capture_chain(torch, gnf4, slots):
-    """One graph holding one step per slot, in slot order: a replay runs
-    len(slots) consecutive steps with no host launch between them."""
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
-        for sl in slots:
-            sl.run(gnf4)
-    torch.cuda.synchronize()
-    return g
+CHAIN_MAX = 256     # steps per captured graph
 
 
-def time_steps(torch, slots, chain, steps, warmup):
-    """Time exactly `steps` steps: whole replays of the slot chain, then single
-    slot graphs for the remainder. Step i uses slot i % len(slots)."""
+def gpu_lead(torch):
+    """A short device-side spin on the current stream, enqueued just before a
+    timed region: the host then submits the region's events and graph
+    launches while the GPU is still busy, so the region starts with its
+    work already queued and holds no host submission gap."""
+    torch.cuda._sleep(2_000_000)
+
+
+def time_steps(torch, gnf4, slots, steps, warmup):
+    """Time exactly `steps` consecutive steps, step i on slot i % len(slots).
+
+    After `warmup` untimed eager steps, the steps are captured as graphs of
+    at most CHAIN_MAX consecutive steps (one graph of L = min(steps,
+    CHAIN_MAX) steps replayed steps // L times, then one of the remaining
+    steps). That sequence is replayed twice back to back on one stream, and
+    HIP events recorded on that stream bracket the second pass: its graphs
+    are queued while the first pass runs, so the timed steps hold no host
+    submission latency (the first pass is more untimed warmup). The whole is
+    bracketed by device synchronizations. Returns (GPU seconds per step from
+    the events, mean packed bytes of the experts a step routes to, mean
+    flops)."""
     G = len(slots)
-    for i in range(warmup):
-        slots[i % G].graph.replay()
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        for i in range(max(warmup, 1)):              # also warms the launch path for capture
+            slots[i % G].run(gnf4)
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(steps // G):
-        chain.replay()
-    for i in range(steps - steps % G, steps):
-        slots[i % G].graph.replay()
+    L = min(steps, CHAIN_MAX)
+    graphs = []
+    for n, reps in ((L, steps // L), (steps % L, 1)):
+        if n == 0 or reps == 0:
+            continue
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for i in range(n):
+                slots[i % G].run(gnf4)
+        graphs.append((g, reps))
     torch.cuda.synchronize()
-    dt = (time.perf_counter() - t0) / steps
-    per = np.mean([slots[i % G].weight_bytes() for i in range(steps)])
-    fl = np.mean([slots[i % G].flops() for i in range(steps)])
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        gpu_lead(torch)
+        for timed in (False, True):
+            if timed:
+                a.record(stream)
+            for g, reps in graphs:
+                for _ in range(reps):
+                    g.replay()
+        b.record(stream)
+    torch.cuda.synchronize()
+    dt = a.elapsed_time(b) * 1e-3 / steps
+    # step i of the timed run is slot (i mod L) mod G: every graph starts at slot 0
+    idx = [(i % L) % G for i in range(steps)]
+    per = np.mean([slots[j].weight_bytes() for j in idx])
+    fl = np.mean([slots[j].flops() for j in idx])
+    del graphs
     return dt, per, fl
+
+
+def time_read_probe(torch, gnf4, nbytes, launches=64):
+    """Achievable HBM read rate for `nbytes` read once: gnf4_read_probe over
+    rotating buffers that together exceed 3x the Infinity Cache, `launches`
+    back-to-back launches in one graph bracketed by HIP events, the median
+    per-launch time over the replays; the best of a few grid sizes. Returns
+    (GB/s, us per launch, workgroups)."""
+    n = -(-int(nbytes) // 16) * 16
+    copies = int(max(4, np.ceil(3 * MALL_BYTES / n)))
+    bufs = [torch.ones(n // 4, dtype=torch.int32, device="cuda") for _ in range(copies)]
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    best = None
+    for wg in (0, 512, 1024, 2048, 4096):
+        with torch.cuda.stream(stream):
+            for i in range(copies):
+                gnf4.read_probe(bufs[i], n, wg, sink)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for i in range(launches):
+                gnf4.read_probe(bufs[i % copies], n, wg, sink)
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(5)]
+        with torch.cuda.stream(stream):
+            g.replay()
+            gpu_lead(torch)
+            for a, b in evs:
+                a.record(stream)
+                g.replay()
+                b.record(stream)
+        torch.cuda.synchronize()
+        us = float(np.median([a.elapsed_time(b) for a, b in evs])) * 1e3 / launches
+        if best is None or us < best[1]:
+            best = (n / (us * 1e-6) / 1e9, us, wg)
+        del g
+    del bufs
+    torch.cuda.empty_cache()
+    return best
 
 
 def gate_up_launch(gnf4, sl):
@@ -420,6 +487,7 @@ def time_kernel(torch, gnf4, slots, steps, warmup, launch=gate_up_launch):
         graph.replay()                                  # warm
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(reps)]
+        gpu_lead(torch)
         for a, b in evs:
             a.record(stream)
             graph.replay()
@@ -719,30 +787,25 @@ def main():
         layers = [base] + [base.clone(torch) for _ in range(copies - 1)]
         slots = [StepSlot(torch, gnf4, cfg, layers[i % copies], T_dec, seed=100 + i)
                  for i in range(max(copies, 16))]
-        for sl in slots:
-            sl.capture(torch, gnf4)
-        chain = capture_chain(torch, gnf4, slots)
-        dt, byts, _ = time_steps(torch, slots, chain, args.steps, args.warmup)
+        dt, byts, _ = time_steps(torch, gnf4, slots, args.steps, args.warmup)
         kms, kbytes, _, glaunch = time_kernel(torch, gnf4, slots, args.steps, args.warmup)
         out["decode"] = dict(T=T_dec, ms_per_step=dt * 1e3, gbs=byts / dt / 1e9,
                              kernel_us=kms * 1e3, kernel_bytes=kbytes, copies=copies,
                              graph_launches=glaunch)
-        del slots, layers, chain
+        del slots, layers
         torch.cuda.empty_cache()
+        out["decode"]["read"] = time_read_probe(torch, gnf4, kbytes)
     if prefill_ok:
         copies = int(min(8, max(2, np.ceil(3 * MALL_BYTES / max(layer_bytes, 1)))))
         layers = [base] + [base.clone(torch) for _ in range(copies - 1)]
         slots = [StepSlot(torch, gnf4, cfg, layers[i % copies], T_pre, seed=200 + i)
                  for i in range(copies)]
-        for sl in slots:
-            sl.capture(torch, gnf4)
-        chain = capture_chain(torch, gnf4, slots)
         steps = max(10, args.steps // 10)
-        dt, byts, fl = time_steps(torch, slots, chain, steps, max(2, args.warmup // 5))
+        dt, byts, fl = time_steps(torch, gnf4, slots, steps, max(2, args.warmup // 5))
         kms, kbytes, kfl, _ = time_kernel(torch, gnf4, slots, steps, max(2, args.warmup // 5))
-        out["prefill"] = dict(T=T_pre, ms_per_step=dt * 1e3, tflops=fl / dt / 1e12,
+        out["prefill"] = dict(T=T_pre, ms_per_step=dt * 1e3, tflops=fl / dt / 1e12, steps=steps,
                               kernel_us=kms * 1e3, kernel_flops=kfl, copies=copies)
-        del slots, layers, chain
+        del slots, layers
         torch.cuda.empty_cache()
 
     if len(cfg.projs) > 1 and args.only is None:
@@ -758,13 +821,10 @@ def main():
             nsl = max(copies, 16) if tag == "decode" else copies
             slots = [StepSlot(torch, gnf4, cfg, layers[i % copies], T, seed=300 + i, ffn=True)
                      for i in range(nsl)]
-            for sl in slots:
-                sl.capture(torch, gnf4)
-            chain = capture_chain(torch, gnf4, slots)
             steps = args.steps if tag == "decode" else max(10, args.steps // 10)
-            dt, byts, fl = time_steps(torch, slots, chain, steps, max(2, args.warmup // 5))
+            dt, byts, fl = time_steps(torch, gnf4, slots, steps, max(2, args.warmup // 5))
             ffn[tag] = (T, dt, byts, fl)
-            del slots, layers, chain
+            del slots, layers
             torch.cuda.empty_cache()
         out["ffn"] = ffn
 
@@ -783,13 +843,10 @@ def main():
             nsl = max(copies, 16) if tag == "decode" else copies
             slots = [DequantSlot(torch, gnf4, cfg, layers[i % copies], T, 400 + i, wbuf)
                      for i in range(nsl)]
-            for sl in slots:
-                sl.capture(torch, gnf4)
-            chain = capture_chain(torch, gnf4, slots)
             steps = args.steps if tag == "decode" else max(10, args.steps // 10)
-            dt, byts, fl = time_steps(torch, slots, chain, steps, max(2, args.warmup // 5))
+            dt, byts, fl = time_steps(torch, gnf4, slots, steps, max(2, args.warmup // 5))
             dq[tag] = (T, dt)
-            del slots, layers, chain, wbuf
+            del slots, layers, wbuf
             torch.cuda.empty_cache()
         out["dequant"] = dq
 
@@ -806,26 +863,20 @@ def main():
             nsl = max(copies, 16) if tag == "decode" else copies
             slots = [BackwardSlot(torch, gnf4, cfg, layers[i % copies], T, seed=500 + i)
                      for i in range(nsl)]
-            for sl in slots:
-                sl.capture(torch, gnf4)
-            chain = capture_chain(torch, gnf4, slots)
             steps = args.steps if tag == "decode" else max(10, args.steps // 10)
             wu = max(2, args.warmup // 5)
-            dt, byts, fl = time_steps(torch, slots, chain, steps, wu)
+            dt, byts, fl = time_steps(torch, gnf4, slots, steps, wu)
             kms, kbytes, kfl, _ = time_kernel(torch, gnf4, slots, steps, wu, gate_up_dx_launch)
             entry = dict(T=T, dt=dt, byts=byts, fl=fl, kms=kms, kbytes=kbytes, kfl=kfl)
-            del slots, chain
+            del slots
             if not args.no_dequant_path:
                 ms = min(cfg.E, T * cfg.k)
                 wbuf = [torch.empty((ms, pw.N, pw.K), dtype=torch.int16, device="cuda") for pw in base.projs]
                 nd = min(nsl, 16 if tag == "decode" else 4)
                 dslots = [DequantBackwardSlot(torch, gnf4, cfg, layers[i % copies], T, 600 + i, wbuf)
                           for i in range(nd)]
-                for sl in dslots:
-                    sl.capture(torch, gnf4)
-                dchain = capture_chain(torch, gnf4, dslots)
-                entry["dq_dt"], _, _ = time_steps(torch, dslots, dchain, steps, wu)
-                del dslots, dchain, wbuf
+                entry["dq_dt"] = time_steps(torch, gnf4, dslots, steps, wu)[0]
+                del dslots, wbuf
             bw[tag] = entry
             del layers
             torch.cuda.empty_cache()
@@ -855,13 +906,20 @@ def main():
         result["ms_per_step"] = round(d["ms_per_step"], 5)
         ach = d["kernel_bytes"] / (d["kernel_us"] * 1e-6) / 1e9
         traffic, tsrc = profile_traffic(cfg.name, "decode")
+        rd_gbs, rd_us, rd_wg = d["read"]
         result["roofline"] = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
                               "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic,
                               "traffic_unit": "HBM bytes/launch", "traffic_source": tsrc,
                               "kernel": "%s (gate_up, T=%d)" % (gemm_kernel_name(cfg, d["T"]), d["T"]),
                               "kernel_us": round(d["kernel_us"], 3),
                               "launches_per_graph": d["graph_launches"],
-                              "bytes_per_launch": int(d["kernel_bytes"])}
+                              "bytes_per_launch": int(d["kernel_bytes"]),
+                              "achievable_read_GBps": round(rd_gbs, 1),
+                              "achievable_read_us": round(rd_us, 3),
+                              "frac_of_achievable_read": round(ach / rd_gbs, 4),
+                              "achievable_read_kernel": "read_probe_kernel (gnf4_read_probe, %s "
+                                                        "workgroups, the same bytes per launch)"
+                                                        % (rd_wg or "8/CU")}
         result["decode"] = {"step_us": round(d["ms_per_step"] * 1e3, 3),
                             "pct_hbm_peak_step": round(100 * d["gbs"] / HBM_PEAK_GBS, 2),
                             "weight_copies": d["copies"]}
@@ -869,7 +927,7 @@ def main():
         p = out["prefill"]
         kt = p["kernel_flops"] / (p["kernel_us"] * 1e-6) / 1e12
         ptraffic, ptsrc = profile_traffic(cfg.name, "prefill")
-        result["prefill"] = {"T": p["T"], "step_ms": round(p["ms_per_step"], 4),
+        result["prefill"] = {"T": p["T"], "steps": p["steps"], "step_ms": round(p["ms_per_step"], 4),
                              "tflops": round(p["tflops"], 2),
                              "pct_mfma_peak_step": round(100 * p["tflops"] / BF16_PEAK_TFLOPS, 2),
                              "roofline": {"bound": "mfma", "achieved": round(kt, 2),

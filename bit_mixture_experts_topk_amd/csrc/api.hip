@@ -37,6 +37,20 @@ static gnf4_status device_status(hipError_t e, const char *what) {
 
 static bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
+// The route's workspace: at least route_workspace_bytes(T*k, E) bytes,
+// 16-byte aligned (NULL allowed when none is needed).
+static gnf4_status check_route_workspace(int32_t T, int32_t k, int32_t E, const void *workspace,
+                                         size_t workspace_bytes) {
+  const size_t need = route_workspace_bytes((int64_t)T * k, E);
+  if (need == 0) return ok();
+  if (workspace_bytes < need)
+    return fail(GNF4_ERR_WORKSPACE, "route workspace of %zu bytes given, %zu needed for T*k = %lld, "
+                "E = %d", workspace_bytes, need, (long long)T * k, E);
+  if (!workspace || !aligned16(workspace))
+    return fail(GNF4_ERR_INVALID_ARG, "route workspace must be a 16-byte aligned device pointer");
+  return ok();
+}
+
 int device_cu_count() {
   static std::mutex mu;
   static int cached[64] = {0};
@@ -102,9 +116,17 @@ using namespace gnf4;
 
 extern "C" {
 
+size_t gnf4_route_workspace_bytes(int32_t T, int32_t k, int32_t E) {
+  if (T < 0 || k < 1 || k > 64 || E < 1 || E > GNF4_MAX_EXPERTS ||
+      (int64_t)T * k >= ((int64_t)1 << 31) - 1024)
+    return 0;
+  return route_workspace_bytes((int64_t)T * k, E);
+}
+
 gnf4_status gnf4_route(const int32_t *topk_ids, int32_t T, int32_t k, int32_t E, int32_t *counts,
                        int32_t *offsets, int32_t *perm, int32_t *inv, int32_t *active,
-                       int32_t *n_active, int32_t *bad_id_flag, gnf4_stream_t stream) {
+                       int32_t *n_active, int32_t *bad_id_flag, void *workspace,
+                       size_t workspace_bytes, gnf4_stream_t stream) {
   if (E < 1 || E > GNF4_MAX_EXPERTS)
     return fail(GNF4_ERR_INVALID_ARG, "E = %d outside [1, %d]", E, GNF4_MAX_EXPERTS);
   if (k < 1 || k > 64) return fail(GNF4_ERR_INVALID_ARG, "k = %d outside [1, 64]", k);
@@ -115,15 +137,18 @@ gnf4_status gnf4_route(const int32_t *topk_ids, int32_t T, int32_t k, int32_t E,
     return fail(GNF4_ERR_INVALID_ARG, "an output pointer is NULL");
   if (T > 0 && (!topk_ids || !perm || !inv))
     return fail(GNF4_ERR_INVALID_ARG, "topk_ids, perm or inv is NULL");
+  gnf4_status st = check_route_workspace(T, k, E, workspace, workspace_bytes);
+  if (st != GNF4_OK) return st;
   return device_status(launch_route(topk_ids, T, k, E, counts, offsets, perm, inv, active,
-                                    n_active, bad_id_flag, (hipStream_t)stream),
+                                    n_active, bad_id_flag, workspace, (hipStream_t)stream),
                        "route launch");
 }
 
 gnf4_status gnf4_route_logits(const float *logits, int32_t T, int32_t k, int32_t E,
                               int32_t *topk_ids, float *topk_w, int32_t *counts,
                               int32_t *offsets, int32_t *perm, int32_t *inv, int32_t *active,
-                              int32_t *n_active, int32_t *bad_id_flag, gnf4_stream_t stream) {
+                              int32_t *n_active, int32_t *bad_id_flag, void *workspace,
+                              size_t workspace_bytes, gnf4_stream_t stream) {
   if (E < 1 || E > GNF4_MAX_EXPERTS)
     return fail(GNF4_ERR_INVALID_ARG, "E = %d outside [1, %d]", E, GNF4_MAX_EXPERTS);
   if (k < 1 || k > 64 || k > E)
@@ -135,10 +160,12 @@ gnf4_status gnf4_route_logits(const float *logits, int32_t T, int32_t k, int32_t
     return fail(GNF4_ERR_INVALID_ARG, "an output pointer is NULL");
   if (T > 0 && (!logits || !topk_ids || !topk_w || !perm || !inv))
     return fail(GNF4_ERR_INVALID_ARG, "logits, topk_ids, topk_w, perm or inv is NULL");
+  gnf4_status st = check_route_workspace(T, k, E, workspace, workspace_bytes);
+  if (st != GNF4_OK) return st;
   hipError_t e = launch_topk(logits, T, E, k, topk_ids, topk_w, (hipStream_t)stream);
   if (e != hipSuccess) return device_status(e, "top-k launch");
   return device_status(launch_route(topk_ids, T, k, E, counts, offsets, perm, inv, active,
-                                    n_active, bad_id_flag, (hipStream_t)stream),
+                                    n_active, bad_id_flag, workspace, (hipStream_t)stream),
                        "route launch");
 }
 
@@ -167,6 +194,7 @@ struct FusedRoute {
   const float *logits;        // instead of ids: the router's top-k first
   int32_t *topk_ids;
   float *topk_w;
+  void *workspace;            // the route's (checked by the caller)
 };
 
 static gnf4_status grouped_gemm_any(const gnf4_weights *w, const uint16_t *X, int32_t gather,
@@ -222,7 +250,8 @@ static gnf4_status grouped_gemm_any(const gnf4_weights *w, const uint16_t *X, in
       if (e != hipSuccess) return device_status(e, "top-k launch");
     }
     e = launch_route(fr->logits ? fr->topk_ids : fr->ids, T, k, w->E, fr->counts, fr->offsets,
-                     fr->perm, fr->inv, fr->active, fr->n_active, fr->bad, (hipStream_t)stream);
+                     fr->perm, fr->inv, fr->active, fr->n_active, fr->bad, fr->workspace,
+                     (hipStream_t)stream);
     if (e != hipSuccess) return device_status(e, "route launch");
   }
   if (rows <= kGemvMaxRows && w->K <= kGemvMaxK)
@@ -249,6 +278,7 @@ gnf4_status gnf4_grouped_gemm(const gnf4_weights *w, const uint16_t *X, int32_t 
 gnf4_status gnf4_route_grouped_gemm(const int32_t *topk_ids, int32_t T, int32_t k,
                                     int32_t *counts, int32_t *offsets, int32_t *perm, int32_t *inv,
                                     int32_t *active, int32_t *n_active, int32_t *bad_id_flag,
+                                    void *workspace, size_t workspace_bytes,
                                     const gnf4_weights *w, const uint16_t *X, float *Y, uint16_t *H,
                                     gnf4_stream_t stream) {
   gnf4_status st = check_weights(w);
@@ -263,11 +293,13 @@ gnf4_status gnf4_route_grouped_gemm(const int32_t *topk_ids, int32_t T, int32_t 
     return fail(GNF4_ERR_INVALID_ARG, "topk_ids, perm or inv is NULL");
   if (T > 0 && (Y == nullptr) == (H == nullptr))
     return fail(GNF4_ERR_INVALID_ARG, "exactly one of Y and H must be given");
+  st = check_route_workspace(T, k, w->E, workspace, workspace_bytes);
+  if (st != GNF4_OK) return st;
   if (T == 0)                                     // routing of nothing: counts, offsets, flags
     return gnf4_route(topk_ids, T, k, w->E, counts, offsets, perm, inv, active, n_active,
-                      bad_id_flag, stream);
+                      bad_id_flag, workspace, workspace_bytes, stream);
   const FusedRoute fr = {topk_ids, counts, offsets, perm, inv, active, n_active, bad_id_flag,
-                         nullptr, nullptr, nullptr};
+                         nullptr, nullptr, nullptr, workspace};
   return grouped_gemm_any(w, X, 1, offsets, perm, active, n_active, T, k, Y, H, stream, &fr);
 }
 
@@ -275,7 +307,8 @@ gnf4_status gnf4_route_logits_grouped_gemm(const float *logits, int32_t T, int32
                                            int32_t *topk_ids, float *topk_w, int32_t *counts,
                                            int32_t *offsets, int32_t *perm, int32_t *inv,
                                            int32_t *active, int32_t *n_active,
-                                           int32_t *bad_id_flag, const gnf4_weights *w,
+                                           int32_t *bad_id_flag, void *workspace,
+                                           size_t workspace_bytes, const gnf4_weights *w,
                                            const uint16_t *X, float *Y, uint16_t *H,
                                            gnf4_stream_t stream) {
   gnf4_status st = check_weights(w);
@@ -291,11 +324,13 @@ gnf4_status gnf4_route_logits_grouped_gemm(const float *logits, int32_t T, int32
     return fail(GNF4_ERR_INVALID_ARG, "logits, topk_ids, topk_w, perm or inv is NULL");
   if (T > 0 && (Y == nullptr) == (H == nullptr))
     return fail(GNF4_ERR_INVALID_ARG, "exactly one of Y and H must be given");
+  st = check_route_workspace(T, k, w->E, workspace, workspace_bytes);
+  if (st != GNF4_OK) return st;
   if (T == 0)
     return gnf4_route_logits(logits, T, k, w->E, topk_ids, topk_w, counts, offsets, perm, inv,
-                             active, n_active, bad_id_flag, stream);
+                             active, n_active, bad_id_flag, workspace, workspace_bytes, stream);
   const FusedRoute fr = {nullptr, counts, offsets, perm, inv, active, n_active, bad_id_flag,
-                         logits, topk_ids, topk_w};
+                         logits, topk_ids, topk_w, workspace};
   return grouped_gemm_any(w, X, 1, offsets, perm, active, n_active, T, k, Y, H, stream, &fr);
 }
 
@@ -554,6 +589,18 @@ void gnf4_nf4_codebook(float out[16]) {
     uint32_t b = kNF4Bits[i];
     std::memcpy(&out[i], &b, 4);
   }
+}
+
+gnf4_status gnf4_read_probe(const void *src, size_t nbytes, int32_t workgroups, uint32_t *sink,
+                            gnf4_stream_t stream) {
+  if (nbytes == 0) return ok();
+  if (!src || !sink) return fail(GNF4_ERR_INVALID_ARG, "src or sink is NULL");
+  if (!aligned16(src) || nbytes % 16)
+    return fail(GNF4_ERR_INVALID_ARG, "src must be 16-byte aligned and nbytes a multiple of 16");
+  if (workgroups < 0) return fail(GNF4_ERR_INVALID_ARG, "workgroups = %d is negative", workgroups);
+  if (nbytes > ((size_t)1 << 46)) return fail(GNF4_ERR_UNSUPPORTED, "nbytes too large");
+  return device_status(launch_read_probe(src, (int64_t)nbytes, workgroups, sink, (hipStream_t)stream),
+                       "read probe launch");
 }
 
 void gnf4_nf4_codebook_bf16(uint16_t out[16], float *scale) {

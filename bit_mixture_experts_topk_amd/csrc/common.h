@@ -367,7 +367,10 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
 // Host-side launchers (one per kernel family), defined in the .hip files.
 hipError_t launch_route(const int32_t *ids, int32_t T, int32_t k, int32_t E, int32_t *counts,
                         int32_t *offsets, int32_t *perm, int32_t *inv, int32_t *active,
-                        int32_t *n_active, int32_t *bad, hipStream_t s);
+                        int32_t *n_active, int32_t *bad, void *workspace, hipStream_t s);
+// Workspace bytes the route of n assignments over E experts needs (0 when
+// one workgroup routes them).
+size_t route_workspace_bytes(int64_t n, int32_t E);
 hipError_t launch_topk(const float *logits, int32_t T, int32_t E, int32_t k, int32_t *ids,
                        float *w, hipStream_t s);
 hipError_t launch_swiglu(const float *Y, int32_t rows, int32_t I, uint16_t *H, hipStream_t s);
@@ -391,6 +394,9 @@ hipError_t launch_dequant_bf16(const Weights &w, const int32_t *experts, const i
                                int32_t max_experts, uint16_t *out, hipStream_t s);
 hipError_t launch_quantize(int32_t fmt, const float *W, int32_t rows, int32_t K, uint8_t *codes,
                            void *scales, float *scales2, hipStream_t s);
+
+hipError_t launch_read_probe(const void *src, int64_t nbytes, int32_t workgroups, uint32_t *sink,
+                             hipStream_t s);
 
 // Number of compute units of the current device (cached per device).
 int device_cu_count();

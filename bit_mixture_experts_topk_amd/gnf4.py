@@ -21,15 +21,15 @@ LIB_PATH = os.path.join(_HERE, "libgnf4.so")
 
 NF4, NF4_DQ, MXFP4 = 0, 1, 2
 FORMATS = {"nf4": NF4, "nf4_dq": NF4_DQ, "mxfp4": MXFP4}
-STATUS = {0: "OK", 1: "INVALID_ARG", 2: "UNSUPPORTED", 4: "DEVICE"}
+STATUS = {0: "OK", 1: "INVALID_ARG", 2: "UNSUPPORTED", 3: "WORKSPACE", 4: "DEVICE"}
 
 # Every entry point declared in include/gnf4.h.
-EXPORTS = ("gnf4_route", "gnf4_route_logits", "gnf4_route_grouped_gemm",
+EXPORTS = ("gnf4_route", "gnf4_route_workspace_bytes", "gnf4_route_logits", "gnf4_route_grouped_gemm",
            "gnf4_route_logits_grouped_gemm", "gnf4_grouped_gemm",
            "gnf4_grouped_gemm_swiglu", "gnf4_grouped_gemm_combine",
            "gnf4_grouped_gemm_dx", "gnf4_swiglu", "gnf4_combine",
            "gnf4_dequant", "gnf4_dequant_experts_bf16", "gnf4_quantize", "gnf4_nf4_codebook",
-           "gnf4_nf4_codebook_bf16",
+           "gnf4_nf4_codebook_bf16", "gnf4_read_probe",
            "gnf4_expert_cache_state_words", "gnf4_expert_cache_copies_words",
            "gnf4_expert_cache_reset", "gnf4_expert_cache_stage", "gnf4_expert_cache_fill",
            "gnf4_last_error",
@@ -59,16 +59,19 @@ def lib():
             raise RuntimeError("libgnf4.so is not built; run `python -m bit_mixture_experts_topk_amd.build`")
         L = ctypes.CDLL(LIB_PATH)
         P, I, S = ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p
-        L.gnf4_route.argtypes = [P, I, I, I, P, P, P, P, P, P, P, S]
-        L.gnf4_route_logits.argtypes = [P, I, I, I, P, P, P, P, P, P, P, P, P, S]
+        Z = ctypes.c_size_t
+        L.gnf4_route_workspace_bytes.argtypes = [I, I, I]
+        L.gnf4_route_workspace_bytes.restype = Z
+        L.gnf4_route.argtypes = [P, I, I, I, P, P, P, P, P, P, P, P, Z, S]
+        L.gnf4_route_logits.argtypes = [P, I, I, I, P, P, P, P, P, P, P, P, P, P, Z, S]
         L.gnf4_swiglu.argtypes = [P, I, I, P, S]
         L.gnf4_grouped_gemm.argtypes = [ctypes.POINTER(CWeights), P, I, P, P, P, P, I, I, P, S]
         L.gnf4_grouped_gemm_swiglu.argtypes = [ctypes.POINTER(CWeights), P, I, P, P, P, P, I, I, P, S]
-        L.gnf4_route_grouped_gemm.argtypes = [P, I, I, P, P, P, P, P, P, P,
+        L.gnf4_route_grouped_gemm.argtypes = [P, I, I, P, P, P, P, P, P, P, P, Z,
                                               ctypes.POINTER(CWeights), P, P, P, S]
         L.gnf4_grouped_gemm_combine.argtypes = [ctypes.POINTER(CWeights), P, P, P, P, P, P, P, I, I,
                                                 P, P, S]
-        L.gnf4_route_logits_grouped_gemm.argtypes = [P, I, I, P, P, P, P, P, P, P, P, P,
+        L.gnf4_route_logits_grouped_gemm.argtypes = [P, I, I, P, P, P, P, P, P, P, P, P, P, Z,
                                                      ctypes.POINTER(CWeights), P, P, P, S]
         L.gnf4_grouped_gemm_dx.argtypes = [ctypes.POINTER(CWeights), P, P, I, I, P, S]
         L.gnf4_combine.argtypes = [P, P, P, I, I, I, P, S]
@@ -86,6 +89,7 @@ def lib():
         L.gnf4_nf4_codebook.restype = None
         L.gnf4_nf4_codebook_bf16.argtypes = [ctypes.POINTER(ctypes.c_uint16), ctypes.POINTER(ctypes.c_float)]
         L.gnf4_nf4_codebook_bf16.restype = None
+        L.gnf4_read_probe.argtypes = [P, ctypes.c_size_t, I, P, S]
         L.gnf4_last_error.restype = ctypes.c_char_p
         L.gnf4_build_id.restype = ctypes.c_char_p
         for name in ("gnf4_route", "gnf4_grouped_gemm", "gnf4_combine", "gnf4_dequant", "gnf4_quantize"):
@@ -201,13 +205,26 @@ def quantize_into(fmt, W, pw, e0):
            "gnf4_quantize")
 
 
+def route_workspace_bytes(T, k, E):
+    return int(lib().gnf4_route_workspace_bytes(T, k, E))
+
+
 def route_buffers(T, k, E, device="cuda"):
-    """Output buffers for route(): counts, offsets, perm, inv, active, n_active, bad."""
+    """Output buffers for route(): counts, offsets, perm, inv, active,
+    n_active, bad, and the route's workspace (empty when none is needed)."""
     i32 = dict(dtype=torch.int32, device=device)
+    ws = route_workspace_bytes(T, k, E)
     return {"counts": torch.empty(E, **i32), "offsets": torch.empty(E + 1, **i32),
             "perm": torch.empty(max(T * k, 1), **i32), "inv": torch.empty(max(T * k, 1), **i32),
             "active": torch.empty(E, **i32), "n_active": torch.empty(1, **i32),
-            "bad": torch.empty(1, **i32)}
+            "bad": torch.empty(1, **i32),
+            "workspace": torch.empty(max(ws, 16), dtype=torch.uint8, device=device)}
+
+
+def _ws(r):
+    """(pointer, bytes) of a route dict's workspace."""
+    w = r.get("workspace")
+    return (None, 0) if w is None else (_ptr(w), w.numel())
 
 
 def route(topk_ids, E, out=None):
@@ -217,7 +234,7 @@ def route(topk_ids, E, out=None):
     r = dict(out) if out is not None else route_buffers(T, k, E, topk_ids.device)
     _check(lib().gnf4_route(_ptr(topk_ids), T, k, E, _ptr(r["counts"]), _ptr(r["offsets"]),
                             _ptr(r["perm"]), _ptr(r["inv"]), _ptr(r["active"]),
-                            _ptr(r["n_active"]), _ptr(r["bad"]), _stream()), "gnf4_route")
+                            _ptr(r["n_active"]), _ptr(r["bad"]), *_ws(r), _stream()), "gnf4_route")
     r["perm"] = r["perm"][:T * k]
     r["inv"] = r["inv"][:T * k]
     return r
@@ -242,7 +259,7 @@ def route_grouped_gemm(topk_ids, w, X, out=None, Y=None, H=None, swiglu=False):
     cw = w.cstruct()
     _check(lib().gnf4_route_grouped_gemm(_ptr(topk_ids), T, k, _ptr(r["counts"]), _ptr(r["offsets"]),
                                          _ptr(r["perm"]), _ptr(r["inv"]), _ptr(r["active"]),
-                                         _ptr(r["n_active"]), _ptr(r["bad"]), ctypes.byref(cw),
+                                         _ptr(r["n_active"]), _ptr(r["bad"]), *_ws(r), ctypes.byref(cw),
                                          _ptr(X), None if swiglu else _ptr(Y),
                                          _ptr(H) if swiglu else None, _stream()),
            "gnf4_route_grouped_gemm")
@@ -275,7 +292,7 @@ def route_logits_grouped_gemm(logits, k, w, X, out=None, Y=None, H=None, swiglu=
     _check(lib().gnf4_route_logits_grouped_gemm(
         _ptr(logits), T, k, _ptr(r["topk_ids"]), _ptr(r["topk_w"]), _ptr(r["counts"]),
         _ptr(r["offsets"]), _ptr(r["perm"]), _ptr(r["inv"]), _ptr(r["active"]), _ptr(r["n_active"]),
-        _ptr(r["bad"]), ctypes.byref(cw), _ptr(X), None if swiglu else _ptr(Y),
+        _ptr(r["bad"]), *_ws(r), ctypes.byref(cw), _ptr(X), None if swiglu else _ptr(Y),
         _ptr(H) if swiglu else None, _stream()), "gnf4_route_logits_grouped_gemm")
     r["perm"] = r["perm"][:T * k]
     r["inv"] = r["inv"][:T * k]
@@ -296,7 +313,7 @@ def route_logits(logits, k, out=None):
     _check(lib().gnf4_route_logits(_ptr(logits), T, k, E, _ptr(r["topk_ids"]), _ptr(r["topk_w"]),
                                    _ptr(r["counts"]), _ptr(r["offsets"]), _ptr(r["perm"]),
                                    _ptr(r["inv"]), _ptr(r["active"]), _ptr(r["n_active"]),
-                                   _ptr(r["bad"]), _stream()), "gnf4_route_logits")
+                                   _ptr(r["bad"]), *_ws(r), _stream()), "gnf4_route_logits")
     r["perm"] = r["perm"][:T * k]
     r["inv"] = r["inv"][:T * k]
     r["topk_ids"] = r["topk_ids"][:T]
@@ -406,6 +423,18 @@ def dequant_experts_bf16(w, experts, count, max_experts, out=None):
     _check(lib().gnf4_dequant_experts_bf16(ctypes.byref(cw), _ptr(experts), _ptr(count), max_experts,
                                            _ptr(out), _stream()), "gnf4_dequant_experts_bf16")
     return out
+
+
+def read_probe(buf, nbytes=None, workgroups=0, sink=None):
+    """Read nbytes (default: all) of the CUDA tensor buf once (the achievable
+    HBM read rate; over more than 256 MB it also evicts the Infinity Cache)."""
+    if not (buf.is_cuda and buf.is_contiguous()):
+        raise ValueError("buf must be a contiguous CUDA tensor")
+    n = buf.numel() * buf.element_size() if nbytes is None else nbytes
+    if sink is None:
+        sink = torch.empty(1, dtype=torch.int32, device=buf.device)
+    _check(lib().gnf4_read_probe(_ptr(buf), n, workgroups, _ptr(sink), _stream()), "gnf4_read_probe")
+    return sink
 
 
 def dequant(w, e):

@@ -71,6 +71,7 @@ typedef enum {
   GNF4_OK = 0,
   GNF4_ERR_INVALID_ARG = 1, /* null pointer, bad size, misalignment */
   GNF4_ERR_UNSUPPORTED = 2, /* valid but outside what the kernels handle */
+  GNF4_ERR_WORKSPACE = 3,   /* the workspace given is smaller than the call needs */
   GNF4_ERR_DEVICE = 4       /* a HIP call or launch failed */
 } gnf4_status;
 
@@ -91,6 +92,15 @@ typedef struct {
 #define GNF4_MAX_K 65536
 #define GNF4_MAX_N 262144
 
+/* gnf4_route_workspace_bytes -- device bytes of workspace that gnf4_route
+ * (and every call that routes: gnf4_route_logits, gnf4_route_grouped_gemm,
+ * gnf4_route_logits_grouped_gemm) needs for T tokens with k ids each over E
+ * experts: 0 up to T*k = 1024 (one workgroup routes them), else about
+ * 4 * (E + 1) bytes per chunk of 1024 or more consecutive assignments (at
+ * most about 256 chunks), rounded up to 256 bytes; 0 for invalid arguments.
+ * 128 experts at T*k = 32768: 16,640 bytes. */
+size_t gnf4_route_workspace_bytes(int32_t T, int32_t k, int32_t E);
+
 /* gnf4_route -- group the flat top-k assignments f = t*k + j by expert.
  *
  * Computes a counting sort of topk_ids (int32 [T][k], row-major):
@@ -106,6 +116,12 @@ typedef struct {
  * The result is deterministic (no order-dependent atomics). T = 0 is a valid
  * no-op apart from zeroing counts/offsets/n_active/bad_id_flag and filling
  * active with -1. Duplicate ids within a token are routed as separate rows.
+ * workspace: caller-owned device memory of workspace_bytes >=
+ * gnf4_route_workspace_bytes(T, k, E), 16-byte aligned (NULL when that is
+ * 0); its contents on entry do not matter and on return are unspecified;
+ * GNF4_ERR_WORKSPACE when workspace_bytes is smaller. Up to T*k = 1024 the
+ * route is one launch; above, three (chunk histograms, one scan over them,
+ * chunk scatters), each a multi-workgroup launch except the scan.
  * Limits: 1 <= E <= GNF4_MAX_EXPERTS, 1 <= k <= 64, 0 <= T, T*k < 2^31.
  * The pages describe the kernel running one launch for all active experts
  * behind a real router (section cited at the top); the grouping itself is
@@ -113,7 +129,7 @@ typedef struct {
 gnf4_status gnf4_route(const int32_t *topk_ids, int32_t T, int32_t k, int32_t E,
                        int32_t *counts, int32_t *offsets, int32_t *perm, int32_t *inv,
                        int32_t *active, int32_t *n_active, int32_t *bad_id_flag,
-                       gnf4_stream_t stream);
+                       void *workspace, size_t workspace_bytes, gnf4_stream_t stream);
 
 /* gnf4_grouped_gemm -- one launch for all active experts.
  *
@@ -150,11 +166,13 @@ gnf4_status gnf4_grouped_gemm(const gnf4_weights *w, const uint16_t *X, int32_t 
  * jordananderson-pages.pages.dev, section "grouped-nf4-gemm &
  * experts-4bit", demonstration paragraph of the first bullet). Otherwise
  * the two launches of the separate calls. Exactly one of Y, H is non-NULL
- * (for T > 0). Arguments, limits and errors as the two calls. */
+ * (for T > 0). Arguments (the workspace is gnf4_route's), limits and errors
+ * as the two calls. */
 gnf4_status gnf4_route_grouped_gemm(const int32_t *topk_ids, int32_t T, int32_t k,
                                     int32_t *counts, int32_t *offsets, int32_t *perm,
                                     int32_t *inv, int32_t *active, int32_t *n_active,
-                                    int32_t *bad_id_flag, const gnf4_weights *w,
+                                    int32_t *bad_id_flag, void *workspace,
+                                    size_t workspace_bytes, const gnf4_weights *w,
                                     const uint16_t *X, float *Y, uint16_t *H,
                                     gnf4_stream_t stream);
 
@@ -172,7 +190,8 @@ gnf4_status gnf4_route_logits_grouped_gemm(const float *logits, int32_t T, int32
                                            int32_t *topk_ids, float *topk_w, int32_t *counts,
                                            int32_t *offsets, int32_t *perm, int32_t *inv,
                                            int32_t *active, int32_t *n_active,
-                                           int32_t *bad_id_flag, const gnf4_weights *w,
+                                           int32_t *bad_id_flag, void *workspace,
+                                           size_t workspace_bytes, const gnf4_weights *w,
                                            const uint16_t *X, float *Y, uint16_t *H,
                                            gnf4_stream_t stream);
 
@@ -267,7 +286,8 @@ gnf4_status gnf4_combine(const float *Y, const int32_t *inv, const float *topk_w
 gnf4_status gnf4_route_logits(const float *logits, int32_t T, int32_t k, int32_t E,
                               int32_t *topk_ids, float *topk_w, int32_t *counts,
                               int32_t *offsets, int32_t *perm, int32_t *inv, int32_t *active,
-                              int32_t *n_active, int32_t *bad_id_flag, gnf4_stream_t stream);
+                              int32_t *n_active, int32_t *bad_id_flag, void *workspace,
+                              size_t workspace_bytes, gnf4_stream_t stream);
 
 /* gnf4_swiglu -- the activation between the two projections.
  *   H[p][i] = bf16(silu(Y[p][i]) * Y[p][I + i]),  silu(x) = x / (1 + exp(-x))
@@ -379,6 +399,22 @@ gnf4_status gnf4_expert_cache_stage(const int32_t *topk_ids, int32_t T, int32_t 
 gnf4_status gnf4_expert_cache_fill(const gnf4_weights *host_w, const gnf4_weights *cache_w,
                                    const int32_t *copies, int32_t max_copies,
                                    gnf4_stream_t stream);
+
+/* gnf4_read_probe -- the achievable HBM read rate of the device, the
+ * ceiling the decode GEMV's packed-weight bandwidth is compared with (the
+ * pages measure the ceilings they report against rather than assume them:
+ * GitHub profile pjordanandrsn, NVMe-tier bullets; Jordan Anderson,
+ * jordananderson-pages.pages.dev, section "grouped-nf4-gemm & experts-4bit",
+ * demonstration paragraph). Reads bytes [0, nbytes) of the device buffer src
+ * once with 16-byte non-temporal loads, eight in flight per thread, in
+ * `workgroups` workgroups of 256 threads (0: eight per compute unit; fewer
+ * if the buffer is small), and computes nothing from them but an XOR fold;
+ * sink (one device word) is written only if the fold equals one fixed
+ * constant. Over a buffer larger than the 256 MB Infinity Cache the call also
+ * evicts that cache. src 16-byte aligned, nbytes % 16 == 0 (0 is a no-op);
+ * INVALID_ARG otherwise. */
+gnf4_status gnf4_read_probe(const void *src, size_t nbytes, int32_t workgroups, uint32_t *sink,
+                            gnf4_stream_t stream);
 
 /* The 16 NF4 codebook values used by every kernel (host copy, float32). */
 void gnf4_nf4_codebook(float out[16]);

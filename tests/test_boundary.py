@@ -126,17 +126,50 @@ def test_gemm_empty_is_ok(L):
 
 def test_route_rejects(L):
     p = 0x1000
-    assert L.gnf4_route(p, 4, 8, 0, p, p, p, p, p, p, p, None) == INVALID
+    assert L.gnf4_route(p, 4, 8, 0, p, p, p, p, p, p, p, None, 0, None) == INVALID
     assert "E = 0" in gnf4.last_error()
-    assert L.gnf4_route(p, 4, 0, 8, p, p, p, p, p, p, p, None) == INVALID
-    assert L.gnf4_route(p, -1, 2, 8, p, p, p, p, p, p, p, None) == INVALID
-    assert L.gnf4_route(None, 4, 2, 8, p, p, p, p, p, p, p, None) == INVALID
-    assert L.gnf4_route(p, 4, 2, 8, p, None, p, p, p, p, p, None) == INVALID
+    assert L.gnf4_route(p, 4, 0, 8, p, p, p, p, p, p, p, None, 0, None) == INVALID
+    assert L.gnf4_route(p, -1, 2, 8, p, p, p, p, p, p, p, None, 0, None) == INVALID
+    assert L.gnf4_route(None, 4, 2, 8, p, p, p, p, p, p, p, None, 0, None) == INVALID
+    assert L.gnf4_route(p, 4, 2, 8, p, None, p, p, p, p, p, None, 0, None) == INVALID
+
+
+WORKSPACE = 3
+
+
+def test_route_workspace_bytes(L):
+    f = L.gnf4_route_workspace_bytes
+    # one workgroup routes up to 1024 assignments: no workspace
+    assert f(1, 8, 128) == 0 and f(128, 8, 128) == 0 and f(1024, 1, 1024) == 0
+    # above: 4 * (E + 1) bytes per chunk of 1024 assignments, rounded up to 256
+    assert f(129, 8, 128) == (2 * 129 * 4 + 255) // 256 * 256
+    assert f(4096, 8, 128) == 16640                        # 32 chunks
+    assert f(512, 8, 64) == (4 * 65 * 4 + 255) // 256 * 256
+    # past 256 chunks the chunks grow (whole 1024-assignment tiles)
+    n = (1 << 20) + 77
+    chunk = -(-(-(-n // 256)) // 1024) * 1024
+    assert f(n, 1, 4) == (-(-n // chunk) * 5 * 4 + 255) // 256 * 256
+    assert f(-1, 8, 128) == 0 and f(4, 0, 8) == 0 and f(4, 2, 0) == 0 and f(4, 2, 2000) == 0
+
+
+def test_route_workspace_too_small(L):
+    p = 0x1000
+    need = L.gnf4_route_workspace_bytes(4096, 8, 128)
+    assert L.gnf4_route(p, 4096, 8, 128, p, p, p, p, p, p, p, p, need - 1, None) == WORKSPACE
+    assert "workspace" in gnf4.last_error()
+    assert L.gnf4_route(p, 4096, 8, 128, p, p, p, p, p, p, p, None, need, None) == INVALID
+    assert L.gnf4_route(p, 4096, 8, 128, p, p, p, p, p, p, p, p + 4, need, None) == INVALID
+    assert L.gnf4_route_logits(p, 4096, 8, 128, p, p, p, p, p, p, p, p, p, p, 0, None) == WORKSPACE
+    w = weights(E=128)
+    assert L.gnf4_route_grouped_gemm(p, 4096, 8, p, p, p, p, p, p, p, p, need - 16,
+                                     ctypes.byref(w), p, p, None, None) == WORKSPACE
+    assert L.gnf4_route_logits_grouped_gemm(p, 4096, 8, p, p, p, p, p, p, p, p, p, None, 0,
+                                            ctypes.byref(w), p, p, None, None) == WORKSPACE
 
 
 def test_route_logits_rejects(L):
     p = 0x1000
-    ok_args = [p, 4, 2, 8, p, p, p, p, p, p, p, p, p, None]
+    ok_args = [p, 4, 2, 8, p, p, p, p, p, p, p, p, p, None, 0, None]
 
     def call(**kw):
         a = list(ok_args)
@@ -237,7 +270,7 @@ def test_route_grouped_gemm_rejects(L):
     p = 0x1000
 
     def call(T=1, k=2, ids=p, Y=p, H=None, counts=p, wt=None):
-        return L.gnf4_route_grouped_gemm(ids, T, k, counts, p, p, p, p, p, p,
+        return L.gnf4_route_grouped_gemm(ids, T, k, counts, p, p, p, p, p, p, None, 0,
                                          ctypes.byref(wt or w), p, Y, H, None)
 
     assert call(k=0) == INVALID and "k = 0" in gnf4.last_error()
@@ -321,3 +354,13 @@ def test_expert_cache_fill_rejects(L):
     assert "multiple of 256" in gnf4.last_error()
     assert call(c=weights(E=4, N=16, K=64, codes=0x3000, scales=0x4004)) == INVALID
     assert call(m=0) == 0                                              # nothing to copy
+
+
+def test_read_probe_rejects(L):
+    p = 0x1000
+    assert L.gnf4_read_probe(None, 0, 0, None, None) == 0                 # nothing to read
+    assert L.gnf4_read_probe(None, 64, 0, p, None) == INVALID
+    assert L.gnf4_read_probe(p, 64, 0, None, None) == INVALID
+    assert L.gnf4_read_probe(p + 8, 64, 0, p, None) == INVALID            # misaligned
+    assert L.gnf4_read_probe(p, 72, 0, p, None) == INVALID                # not whole 16 B
+    assert L.gnf4_read_probe(p, 64, -1, p, None) == INVALID

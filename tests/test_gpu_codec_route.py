@@ -107,18 +107,62 @@ def test_route_workloads(name, T):
     check_route(r, routing.route(ids, cfg.E), T * cfg.k)
     r2 = g.route(torch.from_numpy(ids).cuda(), cfg.E)
     for key in r:
-        assert torch.equal(r[key], r2[key]), key       # deterministic
+        if key != "workspace":                         # scratch: contents unspecified
+            assert torch.equal(r[key], r2[key]), key   # deterministic
 
 
-@pytest.mark.parametrize("E,T,k", [(1, 5, 1), (7, 33, 3), (1024, 100, 8), (300, 4000, 8), (5, 0, 4)])
+@pytest.mark.parametrize("E,T,k", [
+    (1, 5, 1), (7, 33, 3), (1024, 100, 8), (300, 4000, 8), (5, 0, 4),
+    (64, 128, 8),          # 1024 assignments: the largest one-workgroup route
+    (64, 1025, 1),         # 1025: two chunks, the second holding one assignment
+    (128, 257, 8),         # 2056: three chunks, a ragged last chunk
+    (1, 3000, 1),          # one expert: every chunk adds to one segment
+    (1024, 4096, 8),       # 32 chunks over 1024 experts
+    (16, 40000, 8),        # 320,000: past 256 chunks, chunks of 2048
+])
 def test_route_edge_cases(E, T, k):
     g = gnf4()
     rs = np.random.default_rng(E * 1000 + T)
     ids = rs.integers(-2, E + 2, size=(T, k)).astype(np.int32)   # duplicates and bad ids
-    say("route edge", E, T, k)
+    say("route edge", E, T, k, "workspace", g.route_workspace_bytes(T, k, E))
     r = g.route(torch.from_numpy(ids).cuda().reshape(T, k), E)
     ref = routing.route(ids, E)
     check_route(r, ref, T * k)
+
+
+@pytest.mark.parametrize("where", ["first", "last", "none"])
+def test_route_bad_id_flag_from_any_chunk(where):
+    """The flag is the OR over chunks: one bad id in the first or the last of
+    five chunks raises it; none leaves it 0."""
+    g = gnf4()
+    E, T, k = 32, 4100, 1
+    ids = np.random.default_rng(5).integers(0, E, size=(T, k)).astype(np.int32)
+    if where == "first":
+        ids[3, 0] = E
+    elif where == "last":
+        ids[T - 1, 0] = -7
+    say("route bad id", where)
+    r = g.route(torch.from_numpy(ids).cuda(), E)
+    check_route(r, routing.route(ids, E), T * k)
+    assert int(r["bad"].item()) == (0 if where == "none" else 1)
+
+
+def test_route_workspace_contents_do_not_matter():
+    """The same call with a workspace full of garbage gives the same result."""
+    g = gnf4()
+    E, T, k = 128, 4096, 8
+    ids = np.random.default_rng(9).integers(0, E, size=(T, k)).astype(np.int32)
+    ids_d = torch.from_numpy(ids).cuda()
+    out = g.route_buffers(T, k, E)
+    out["workspace"].fill_(0xA5)
+    say("route garbage workspace")
+    r1 = g.route(ids_d, E, out=out)
+    a = {key: v.clone() for key, v in r1.items() if key != "workspace"}
+    out["workspace"].fill_(0x3C)
+    r2 = g.route(ids_d, E, out=out)
+    for key in a:
+        assert torch.equal(a[key], r2[key]), key
+    check_route(r2, routing.route(ids, E), T * k)
 
 
 def dequant_bf16_ref(fmt, codes, scales, scales2, e, N, K):
