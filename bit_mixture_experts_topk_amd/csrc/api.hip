@@ -144,6 +144,36 @@ gnf4_status gnf4_route(const int32_t *topk_ids, int32_t T, int32_t k, int32_t E,
                        "route launch");
 }
 
+gnf4_status gnf4_route_noalloc(const int32_t *topk_ids, int32_t T, int32_t k, int32_t E,
+                               int32_t *counts, int32_t *offsets, int32_t *perm, int32_t *inv,
+                               int32_t *active, int32_t *n_active, int32_t *bad_id_flag,
+                               gnf4_stream_t stream) {
+  if (E < 1 || E > GNF4_MAX_EXPERTS)
+    return fail(GNF4_ERR_INVALID_ARG, "E = %d outside [1, %d]", E, GNF4_MAX_EXPERTS);
+  if (k < 1 || k > 64) return fail(GNF4_ERR_INVALID_ARG, "k = %d outside [1, 64]", k);
+  if (T < 0) return fail(GNF4_ERR_INVALID_ARG, "T = %d is negative", T);
+  if ((int64_t)T * k >= ((int64_t)1 << 31) - 1024)
+    return fail(GNF4_ERR_INVALID_ARG, "T*k too large");
+  if (!counts || !offsets || !active || !n_active || !bad_id_flag)
+    return fail(GNF4_ERR_INVALID_ARG, "an output pointer is NULL");
+  if (T > 0 && (!topk_ids || !perm || !inv))
+    return fail(GNF4_ERR_INVALID_ARG, "topk_ids, perm or inv is NULL");
+  const size_t need = route_workspace_bytes((int64_t)T * k, E);
+  if (need > route_scratch_bytes())
+    return fail(GNF4_ERR_WORKSPACE, "T*k = %lld over E = %d needs %zu bytes of route workspace, "
+                "more than the %zu-byte static one (use gnf4_route with a workspace)",
+                (long long)T * k, E, need, route_scratch_bytes());
+  void *ws = nullptr;
+  if (need > 0) {
+    hipError_t e = hipSuccess;
+    ws = route_scratch_ptr(&e);
+    if (!ws) return device_status(e, "route scratch address");
+  }
+  return device_status(launch_route(topk_ids, T, k, E, counts, offsets, perm, inv, active,
+                                    n_active, bad_id_flag, ws, (hipStream_t)stream),
+                       "route launch");
+}
+
 gnf4_status gnf4_route_logits(const float *logits, int32_t T, int32_t k, int32_t E,
                               int32_t *topk_ids, float *topk_w, int32_t *counts,
                               int32_t *offsets, int32_t *perm, int32_t *inv, int32_t *active,

@@ -371,6 +371,10 @@ hipError_t launch_route(const int32_t *ids, int32_t T, int32_t k, int32_t E, int
 // Workspace bytes the route of n assignments over E experts needs (0 when
 // one workgroup routes them).
 size_t route_workspace_bytes(int64_t n, int32_t E);
+// The per-device file-scope route workspace (gnf4_route_noalloc): its size,
+// and its device address on the current device (resolved once per device).
+size_t route_scratch_bytes();
+void *route_scratch_ptr(hipError_t *err);
 hipError_t launch_topk(const float *logits, int32_t T, int32_t E, int32_t k, int32_t *ids,
                        float *w, hipStream_t s);
 hipError_t launch_swiglu(const float *Y, int32_t rows, int32_t I, uint16_t *H, hipStream_t s);

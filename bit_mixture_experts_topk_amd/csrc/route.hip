@@ -21,6 +21,7 @@
 // Workspace (int32): chunk c's count, then first position, of expert e at
 // c * E + e; the chunk's bad-id flag at nchunks * E + c.
 #include <algorithm>
+#include <mutex>
 
 #include "common.h"
 
@@ -349,6 +350,44 @@ hipError_t launch_route(const int32_t *ids, int32_t T, int32_t k, int32_t E, int
   hipLaunchKernelGGL(route_scatter_kernel, dim3(nchunks), dim3(kRouteThreads), 0, s, ids, n, E,
                      nbits, chunk, ws, perm, inv);
   return hipGetLastError();
+}
+
+// ------------------------------------------- route without caller memory
+
+// The chunked route's workspace for callers that cannot allocate (code under
+// graph capture, serving loops, harnesses that forbid hipMalloc): one
+// file-scope array per device, held until the process ends. 1 MiB covers
+// every route with E <= 1023 (at most 256 chunks of 4 * (E + 1) bytes) and
+// E = 1024 up to 255 chunks of 1024 assignments.
+constexpr size_t kRouteScratchBytes = (size_t)1 << 20;
+static __device__ __align__(256) int32_t route_scratch[kRouteScratchBytes / 4];
+
+size_t route_scratch_bytes() { return kRouteScratchBytes; }
+
+// Device address of this device's route_scratch, resolved once per device
+// with that device current (in host code the array's name is not a device
+// address). NULL if the lookup fails.
+void *route_scratch_ptr(hipError_t *err) {
+  static std::mutex mu;
+  static void *ptrs[64] = {nullptr};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0 || dev >= 64) {
+    *err = e != hipSuccess ? e : hipErrorInvalidDevice;
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  if (!ptrs[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(route_scratch));
+    if (e != hipSuccess || !p) {
+      *err = e != hipSuccess ? e : hipErrorInvalidSymbol;
+      return nullptr;
+    }
+    ptrs[dev] = p;
+  }
+  *err = hipSuccess;
+  return ptrs[dev];
 }
 
 }  // namespace gnf4

@@ -24,7 +24,7 @@ FORMATS = {"nf4": NF4, "nf4_dq": NF4_DQ, "mxfp4": MXFP4}
 STATUS = {0: "OK", 1: "INVALID_ARG", 2: "UNSUPPORTED", 3: "WORKSPACE", 4: "DEVICE"}
 
 # Every entry point declared in include/gnf4.h.
-EXPORTS = ("gnf4_route", "gnf4_route_workspace_bytes", "gnf4_route_logits", "gnf4_route_grouped_gemm",
+EXPORTS = ("gnf4_route", "gnf4_route_workspace_bytes", "gnf4_route_noalloc", "gnf4_route_logits", "gnf4_route_grouped_gemm",
            "gnf4_route_logits_grouped_gemm", "gnf4_grouped_gemm",
            "gnf4_grouped_gemm_swiglu", "gnf4_grouped_gemm_combine",
            "gnf4_grouped_gemm_dx", "gnf4_swiglu", "gnf4_combine",
@@ -64,6 +64,7 @@ def lib():
         L.gnf4_route_workspace_bytes.restype = Z
         L.gnf4_route.argtypes = [P, I, I, I, P, P, P, P, P, P, P, P, Z, S]
         L.gnf4_route_logits.argtypes = [P, I, I, I, P, P, P, P, P, P, P, P, P, P, Z, S]
+        L.gnf4_route_noalloc.argtypes = [P, I, I, I, P, P, P, P, P, P, P, S]
         L.gnf4_swiglu.argtypes = [P, I, I, P, S]
         L.gnf4_grouped_gemm.argtypes = [ctypes.POINTER(CWeights), P, I, P, P, P, P, I, I, P, S]
         L.gnf4_grouped_gemm_swiglu.argtypes = [ctypes.POINTER(CWeights), P, I, P, P, P, P, I, I, P, S]
@@ -235,6 +236,21 @@ def route(topk_ids, E, out=None):
     _check(lib().gnf4_route(_ptr(topk_ids), T, k, E, _ptr(r["counts"]), _ptr(r["offsets"]),
                             _ptr(r["perm"]), _ptr(r["inv"]), _ptr(r["active"]),
                             _ptr(r["n_active"]), _ptr(r["bad"]), *_ws(r), _stream()), "gnf4_route")
+    r["perm"] = r["perm"][:T * k]
+    r["inv"] = r["inv"][:T * k]
+    return r
+
+
+def route_noalloc(topk_ids, E, out=None):
+    """route() through gnf4_route_noalloc: the library's static workspace,
+    no workspace argument (out's "workspace" entry, if any, is not used)."""
+    _dev(topk_ids, torch.int32, "topk_ids")
+    T, k = topk_ids.shape
+    r = dict(out) if out is not None else route_buffers(T, k, E, topk_ids.device)
+    _check(lib().gnf4_route_noalloc(_ptr(topk_ids), T, k, E, _ptr(r["counts"]), _ptr(r["offsets"]),
+                                    _ptr(r["perm"]), _ptr(r["inv"]), _ptr(r["active"]),
+                                    _ptr(r["n_active"]), _ptr(r["bad"]), _stream()),
+           "gnf4_route_noalloc")
     r["perm"] = r["perm"][:T * k]
     r["inv"] = r["inv"][:T * k]
     return r

@@ -131,6 +131,23 @@ gnf4_status gnf4_route(const int32_t *topk_ids, int32_t T, int32_t k, int32_t E,
                        int32_t *active, int32_t *n_active, int32_t *bad_id_flag,
                        void *workspace, size_t workspace_bytes, gnf4_stream_t stream);
 
+/* gnf4_route_noalloc -- gnf4_route for callers that cannot allocate device
+ * memory (code under graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the same arguments and results without the workspace
+ * pair. The route's workspace is a file-scope 1 MiB device array, one per
+ * GPU, held until the process ends; its address is looked up once per
+ * device (hipGetSymbolAddress with that device current) on the first call
+ * there, and nothing is allocated. That covers every route with
+ * E <= 1023, and E = 1024 up to T*k = 261,120; a larger need returns
+ * GNF4_ERR_WORKSPACE with the sizes in gnf4_last_error(). All calls on one GPU share the
+ * array: two that overlap on that GPU (unordered streams) race and may give
+ * wrong results; calls ordered on the caller's streams do not interfere.
+ * Nothing in the array needs to start at any value. */
+gnf4_status gnf4_route_noalloc(const int32_t *topk_ids, int32_t T, int32_t k, int32_t E,
+                               int32_t *counts, int32_t *offsets, int32_t *perm, int32_t *inv,
+                               int32_t *active, int32_t *n_active, int32_t *bad_id_flag,
+                               gnf4_stream_t stream);
+
 /* gnf4_grouped_gemm -- one launch for all active experts.
  *
  * For every expert e and routed row p in [offsets[e], offsets[e+1]):

@@ -364,3 +364,18 @@ def test_read_probe_rejects(L):
     assert L.gnf4_read_probe(p + 8, 64, 0, p, None) == INVALID            # misaligned
     assert L.gnf4_read_probe(p, 72, 0, p, None) == INVALID                # not whole 16 B
     assert L.gnf4_read_probe(p, 64, -1, p, None) == INVALID
+
+
+def test_route_noalloc_rejects(L):
+    """Host validation of the static-workspace route, before any HIP call:
+    the usual argument checks, and a workspace need beyond its 1 MiB array."""
+    p = 0x1000
+    assert L.gnf4_route_noalloc(p, 4, 2, 0, p, p, p, p, p, p, p, None) == INVALID
+    assert L.gnf4_route_noalloc(p, 4, 65, 128, p, p, p, p, p, p, p, None) == INVALID
+    assert L.gnf4_route_noalloc(p, -1, 2, 8, p, p, p, p, p, p, p, None) == INVALID
+    assert L.gnf4_route_noalloc(None, 4, 2, 8, p, p, p, p, p, p, p, None) == INVALID
+    assert L.gnf4_route_noalloc(p, 4, 2, 8, p, p, None, p, p, p, p, None) == INVALID
+    T = 261120 // 64 + 1                  # E = 1024: 256 chunks of 1025 words > 1 MiB
+    assert L.gnf4_route_workspace_bytes(T, 64, 1024) > (1 << 20)
+    assert L.gnf4_route_noalloc(p, T, 64, 1024, p, p, p, p, p, p, p, None) == WORKSPACE
+    assert "static" in gnf4.last_error()
