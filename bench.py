@@ -57,6 +57,20 @@ MALL_BYTES = 256 << 20
 
 def parse():
     ap = argparse.ArgumentParser()
+    ap.add_argument("--summarize", default=None, metavar="TITLE",
+                    help="print a profile summary from rocprofv3 csv output (--trace, --pmc) "
+                         "instead of benchmarking")
+    ap.add_argument("--trace", nargs=2, action="append", default=[], metavar=("DIR", "CMD"),
+                    help="a --kernel-trace output directory and the command that made it")
+    ap.add_argument("--pmc", nargs=2, action="append", default=[], metavar=("DIR", "CMD"),
+                    help="a --pmc output directory and the command that made it")
+    ap.add_argument("--kernel", default=None,
+                    help="with --summarize: the kernel (name substring) whose HBM traffic is "
+                         "computed from FETCH_SIZE / WRITE_SIZE")
+    ap.add_argument("--alg-bytes", type=int, default=None,
+                    help="with --summarize: algorithmic bytes per launch of --kernel")
+    ap.add_argument("--source", default="bit_mixture_experts_topk_amd/csrc/gemm.hip",
+                    help="with --summarize: the source file of --kernel (its sha256 is recorded)")
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
@@ -72,14 +86,18 @@ def parse():
     ap.add_argument("--kernel-only", choices=["decode", "prefill"], default=None,
                     help="launch only the gate_up grouped GEMM of one step, --steps times "
                          "(for hardware-counter passes); prints no JSON")
-    ap.add_argument("--proj", default=None, help="projection for --kernel-only (default gate_up)")
+    ap.add_argument("--proj", default=None, help="projection for --kernel-only (default gate_up): "
+                    "gate_up runs gnf4_route_grouped_gemm, down gnf4_grouped_gemm_combine")
     ap.add_argument("--dx", action="store_true",
                     help="with --kernel-only: launch the input-gradient GEMM instead")
     return ap.parse_args()
 
 
 def kernel_only(args):
-    """One grouped-GEMM launch shape, repeated: the unit that counter passes measure."""
+    """One grouped-GEMM launch shape, repeated: the unit that counter passes
+    measure. Launches rotate over copies of the projection's packed weights
+    and over routing slots (token ids and activations), so that, as in the
+    timed steps, a launch does not find its weights in the Infinity Cache."""
     import torch
 
     import synth
@@ -94,23 +112,34 @@ def kernel_only(args):
     W = torch.randn((cfg.E, proj.N, proj.K), generator=g, device="cuda") * 0.02
     gnf4.quantize(cfg.fmt, W, pw)
     del W
-    ids, _ = synth.routing_inputs(cfg, T)
+    per_launch = pw.nbytes() * min(1.0, T * cfg.k / cfg.E)
+    copies = int(min(8, max(1, np.ceil(3 * MALL_BYTES / per_launch))))
+    pws = [pw] + [type(pw)(pw.format, pw.E, pw.N, pw.K, pw.codes.clone(), pw.scales.clone(),
+                           pw.scales2.clone() if pw.scales2 is not None else None)
+                  for _ in range(copies - 1)]
+    nslots = max(copies, 16 if T == 1 else 2)
     rows = T if proj.gather else T * cfg.k
-    X = torch.from_numpy(synth.activations(cfg, rows, proj.K, synth.T_X, 0, T).view(np.int16)).cuda()
-    r = gnf4.route(torch.from_numpy(ids).cuda(), cfg.E)
+    slots = []
+    for i in range(nslots):
+        ids, tw = synth.routing_inputs(cfg, T, seed=900 + i)
+        X = torch.from_numpy(synth.activations(cfg, rows, proj.K, synth.T_X, 900 + i, T)
+                             .view(np.int16)).cuda()
+        ids_d = torch.from_numpy(ids).cuda()
+        slots.append(dict(ids=ids_d, tw=torch.from_numpy(tw).cuda(), X=X, r=gnf4.route(ids_d, cfg.E)))
     Y = torch.empty((T * cfg.k, proj.N), dtype=torch.float32, device="cuda")
+    out = torch.empty((T, proj.N), dtype=torch.float32, device="cuda")
     if args.dx:
         dY = torch.from_numpy(synth.grad_rows(cfg, T * cfg.k, proj.N, 0, T).view(np.int16)).cuda()
         dA = torch.empty((T * cfg.k, proj.K), dtype=torch.float32, device="cuda")
     torch.cuda.synchronize()
-    ids_d = torch.from_numpy(ids).cuda()
-    for _ in range(args.steps):
+    for i in range(args.steps):
+        sl, w = slots[i % nslots], pws[i % copies]
         if args.dx:
-            gnf4.grouped_gemm_dx(pw, dY, r, T, cfg.k, dA)
-        elif T == 1 and proj.gather:              # as the decode step runs it: routing fused in
-            gnf4.route_grouped_gemm(ids_d, pw, X, out=r, Y=Y)
-        else:
-            gnf4.grouped_gemm(pw, X, proj.gather, r, T, cfg.k, Y)
+            gnf4.grouped_gemm_dx(w, dY, sl["r"], T, cfg.k, dA)
+        elif proj.gather:                         # as the step runs it (routing fused in at T = 1)
+            gnf4.route_grouped_gemm(sl["ids"], w, sl["X"], out=sl["r"], Y=Y)
+        else:                                     # as the step runs it (combine fused in at T = 1)
+            gnf4.grouped_gemm_combine(w, sl["X"], sl["r"], sl["tw"], T, cfg.k, out, Y=Y)
     if args.calib_copy:
         a = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
         b = torch.empty_like(a)
@@ -119,6 +148,118 @@ def kernel_only(args):
     print("kernel-only %s %s %s%s T=%d x%d done" % (cfg.name, proj.name, args.kernel_only,
                                                     " dx" if args.dx else "", T, args.steps),
           file=sys.stderr, flush=True)
+
+
+# ------------------------------------------------ rocprofv3 summaries
+
+CALIB_COPY_BYTES = 1 << 30
+
+
+def _csvs(d, suffix):
+    import glob
+    return sorted(glob.glob(os.path.join(d, "**", "*" + suffix), recursive=True))
+
+
+def short_name(name):
+    """A kernel's name without namespaces' argument lists: 'gnf4::x<1, 2>(...)' -> 'gnf4::x<1, 2>'."""
+    name = name.replace("void ", "", 1) if name.startswith("void ") else name
+    depth = 0
+    for i, ch in enumerate(name):
+        if ch == "<":
+            depth += 1
+        elif ch == ">":
+            depth -= 1
+        elif ch == "(" and depth == 0:
+            return name[:i]
+    return name
+
+
+def trace_table(d):
+    """Rows (kernel, grid, workgroup, lds, vgpr, calls, avg, min, p10, p50, p90 in us) of the
+    dispatches in a rocprofv3 kernel-trace directory, by kernel and launch shape."""
+    import csv
+    groups = {}
+    for f in _csvs(d, "kernel_trace.csv"):
+        for r in csv.DictReader(open(f)):
+            key = (short_name(r["Kernel_Name"]), int(r["Grid_Size_X"]), int(r["Workgroup_Size_X"]),
+                   int(r["LDS_Block_Size"]), int(r["VGPR_Count"]) + int(r.get("Accum_VGPR_Count") or 0))
+            us = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3
+            groups.setdefault(key, []).append(us)
+    rows = []
+    for key, v in groups.items():
+        a = np.array(v)
+        rows.append(key + (len(a), a.mean(), a.min(), np.percentile(a, 10), np.median(a),
+                           np.percentile(a, 90)))
+    rows.sort(key=lambda r: -r[5] * r[6])
+    return rows
+
+
+def pmc_table(d):
+    """{(kernel, grid): {counter: [values per dispatch]}} of a --pmc directory."""
+    import csv
+    out = {}
+    for f in _csvs(d, "counter_collection.csv"):
+        for r in csv.DictReader(open(f)):
+            key = (short_name(r["Kernel_Name"]), int(r["Grid_Size"]))
+            out.setdefault(key, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    return out
+
+
+def summarize(args):
+    """The profile summary text: kernel-duration tables of the trace runs,
+    per-dispatch counter means of the --pmc runs, and the HBM bytes per
+    launch of --kernel from FETCH_SIZE and WRITE_SIZE (KiB per dispatch),
+    each scaled by what the counter reads for the run's plain 1 GiB device
+    copy (bench.py --calib-copy)."""
+    import hashlib
+    lines = ["# rocprofv3 summary: " + args.summarize, ""]
+    for d, cmd in args.trace:
+        lines += ["kernel trace command (from the repository root):", "  " + cmd, ""]
+        lines.append("%-58s %9s %5s %6s %5s %6s %9s %9s %9s %9s %9s" % (
+            "kernel", "grid", "wg", "lds", "vgpr", "calls", "avg_us", "min_us", "p10_us", "p50_us",
+            "p90_us"))
+        for r in trace_table(d):
+            if not r[0].startswith("gnf4::"):
+                continue
+            lines.append("%-58s %9d %5d %6d %5d %6d %9.2f %9.2f %9.2f %9.2f %9.2f" % (
+                r[0][:58], r[1], r[2], r[3], r[4], r[5], r[6], r[7], r[8], r[9], r[10]))
+        lines.append("")
+    traffic = {}
+    for d, cmd in args.pmc:
+        lines += ["counter pass (from the repository root):", "  " + cmd]
+        tab = pmc_table(d)
+        counters = sorted({c for v in tab.values() for c in v})
+        for key in sorted(tab):
+            if not key[0].startswith("gnf4::"):
+                continue
+            vals = ["%s %.6g" % (c, np.mean(tab[key][c])) for c in counters if c in tab[key]]
+            n = max(len(v) for v in tab[key].values())
+            lines.append("  %s grid %d (%d dispatches): %s" % (key[0], key[1], n, ", ".join(vals)))
+        for c in ("FETCH_SIZE", "WRITE_SIZE"):
+            if c not in counters:
+                continue
+            copies = [np.max(v[c]) for k, v in tab.items() if "copyBuffer" in k[0] and c in v]
+            mine = [v[c] for k, v in tab.items() if args.kernel and args.kernel in k[0] and c in v]
+            if not copies or not mine:
+                continue
+            calib = max(copies)
+            factor = CALIB_COPY_BYTES / (calib * 1024.0)
+            per = float(np.mean(np.concatenate(mine)))
+            traffic[c] = per * 1024.0 * factor
+            lines.append("  %s of %s: %.1f KiB/dispatch; the plain 1 GiB device copy: %.1f KiB -> "
+                         "factor %.4f" % (c, args.kernel, per, calib, factor))
+        lines.append("")
+    if args.kernel and args.alg_bytes:
+        lines.append("algorithmic bytes per launch of %s: %d" % (args.kernel, args.alg_bytes))
+        if "FETCH_SIZE" in traffic and "WRITE_SIZE" in traffic:
+            t = traffic["FETCH_SIZE"] + traffic["WRITE_SIZE"]
+            lines.append("traffic_bytes_per_launch: %d" % int(round(t)))
+            lines.append("traffic_over_algorithmic: %.3f" % (t / args.alg_bytes))
+    if args.kernel:
+        lines.append("kernel_source: %s" % args.source)
+        lines.append("source_sha256: %s" % hashlib.sha256(open(os.path.join(ROOT, args.source), "rb")
+                                                          .read()).hexdigest())
+    print("\n".join(lines))
 
 
 def packed_bytes_per_expert(pw):
@@ -753,6 +894,9 @@ def streaming(torch, gnf4, cfg, base, steps):
 
 def main():
     args = parse()
+    if args.summarize:
+        summarize(args)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU: the library has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
