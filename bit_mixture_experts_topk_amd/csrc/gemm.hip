@@ -610,12 +610,34 @@ __global__ __launch_bounds__(kGemvWaveThreads, 1) void gemv1w_kernel(GemmArgs a,
 // float32 product the one-token GEMV forms (same lane geometry, same
 // reduction) and the sum uses the combine's operations in its order; so out
 // equals gnf4_grouped_gemm followed by gnf4_combine bit for bit, without
-// writing or reading Y. One workgroup of 8 waves per block of RW * U output
-// rows: wave w forms the products of copies j = w, w + 8, ... (its expert's
-// rows and its activation row), the products meet in LDS, and one thread
-// per output row adds them up. Each copy's expert comes from a binary search
-// of the offsets, read with the copies' rows and weights in one round trip.
+// writing or reading Y. One workgroup of 8 waves per G blocks of RW * U
+// output rows; a task is (row block, routed row p), one wave each, and the
+// products meet in LDS where one thread per output row adds them up.
+//
+// Routed row p belongs to the p-th active expert whenever every active
+// expert has one routed row (a token's k distinct ids), so a task reads
+// active[p] and streams that expert's rows at once, with a single memory
+// round trip before the weights. The expert's offsets, loaded after the
+// weights, confirm it; otherwise (repeated ids, dropped ids) the task finds
+// row p's expert by a binary search of the offsets and streams again.
 constexpr int kGemvCombineThreads = 512;
+
+// The expert of routed row p (p < k), -1 if there is no such row (dropped
+// ids): active[p] when that expert's only row is p, else the last e with
+// offsets[e] <= p. Uniform over the wave.
+__device__ __forceinline__ int gemv1c_expert(const GemmArgs &a, int p) {
+  const int E = a.w.E;
+  const int e = p < E ? a.active[p] : -1;
+  if (e >= 0 && a.offsets[e] == p && a.offsets[e + 1] == p + 1) return e;
+  if (p >= a.offsets[E]) return -1;
+  int lo = 0, hi = E;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (a.offsets[mid] <= p) lo = mid;
+    else hi = mid;
+  }
+  return lo;
+}
 
 template <int FMT, int C, int U>
 __global__ __launch_bounds__(kGemvCombineThreads, 2) void gemv1c_kernel(GemmArgs a, int L_log2,
@@ -627,15 +649,14 @@ __global__ __launch_bounds__(kGemvCombineThreads, 2) void gemv1c_kernel(GemmArgs
   constexpr int kWaves = kGemvCombineThreads / 64;
   constexpr int kMaxRows = 8 * U;                 // RW <= 8 rows per wave slot
   __shared__ uint32_t lut[kLut ? kLutWords : 1];
-  __shared__ int s_off[GNF4_MAX_EXPERTS + 1];
-  __shared__ int s_p[64], s_e[64];
+  __shared__ int s_ip[64];                        // inv[j]: routed row of copy j
   __shared__ float s_w[64];
-  __shared__ float s_y[64][kMaxRows];           // [copy or (block, copy)][row]
+  __shared__ float s_y[64][kMaxRows];             // [(block, routed row)][row]
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const uint32_t lane4 = (uint32_t)lane << 2;
-  const int N = a.w.N, K = a.w.K, E = a.w.E, k = a.k;
+  const int N = a.w.N, E = a.w.E, k = a.k;
   GemvGeom g;
   g.L_log2 = L_log2;
   g.L = 1 << L_log2;
@@ -645,43 +666,55 @@ __global__ __launch_bounds__(kGemvCombineThreads, 2) void gemv1c_kernel(GemmArgs
   g.wave = 0;
   g.ustride = 1;
   g.half = 0;
-  g.KCH = K >> 5;
+  g.KCH = a.w.K >> 5;
   g.rows_per_item = g.RW * U;
   const int G = blocks_per_wg;                    // row blocks of this workgroup (G * k <= 64)
   const int nb0 = (int)blockIdx.x * G;
 
-  for (int e = tid; e <= E; e += kGemvCombineThreads) s_off[e] = a.offsets[e];
+  int vi = 0;
+  float vw = 0.f;
   if (tid < k) {
-    s_p[tid] = inv[tid];
-    s_w[tid] = topk_w[tid];
+    vi = inv[tid];
+    vw = topk_w[tid];
   }
   if constexpr (kLut) fill_nf4_lut<kGemvCombineThreads>(lut, tid);
-  __syncthreads();
-  if (tid < k) {                                  // expert of copy tid's routed row
-    const int p = s_p[tid];
-    int lo = 0, hi = E;                           // last e with offsets[e] <= p
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (s_off[mid] <= p) lo = mid;
-      else hi = mid;
-    }
-    s_e[tid] = lo;
-  }
-  __syncthreads();
 
-  // task q = (row block q / k, copy q % k). The last workgroup may hold
+  // task q = (row block q / k, routed row q % k). The last workgroup may hold
   // fewer than G row blocks (ceil(N / rows per block) need not be a multiple
   // of G): a task whose block starts at or past N loads nothing (the branch
-  // is uniform over the wave) and its rows are never stored.
-  for (int q = wave; q < G * k; q += kWaves) {
-    const int b = q / k, j = q - b * k;
-    if ((nb0 + b) * g.rows_per_item >= N) continue;
-    const int p = s_p[j];
-    uint32_t x[1][C][16];
-    gemv_load_x_row<C>(a, g, max(p, 0), x);
-    GemvRows<U, C> R;
-    gemv_load_rows<FMT, U, C, false>(a, g, s_e[j], (nb0 + b) * g.rows_per_item, R);
-    float v[U][1];
+  // is uniform over the wave) and its rows are never stored. Each wave's
+  // first task issues its loads before the workgroup barrier, for the
+  // speculated expert active[p]; `have` says the registers hold the right
+  // expert's rows.
+  uint32_t x[1][C][16];
+  GemvRows<U, C> R;
+  float v[U][1];
+  int q = wave;
+  bool have = false;
+  if (q < G * k && (nb0 + q / k) * g.rows_per_item < N) {
+    const int p = q % k;
+    const int e = p < E ? a.active[p] : -1;
+    gemv_load_x_row<C>(a, g, p, x);
+    gemv_load_rows<FMT, U, C, false>(a, g, max(e, 0), (nb0 + q / k) * g.rows_per_item, R);
+    have = e >= 0 && a.offsets[e] == p && a.offsets[e + 1] == p + 1;
+  }
+  if (tid < k) {
+    s_ip[tid] = vi;
+    s_w[tid] = vw;
+  }
+  __syncthreads();                                // decode table, inv and weights in LDS
+
+  for (; q < G * k; q += kWaves) {
+    const int b = q / k, p = q - b * k;
+    const int n0 = (nb0 + b) * g.rows_per_item;
+    if (n0 >= N) continue;
+    if (!have) {
+      const int e = gemv1c_expert(a, p);
+      if (e < 0) continue;                        // no such row (dropped ids): never combined
+      gemv_load_x_row<C>(a, g, p, x);
+      gemv_load_rows<FMT, U, C, false>(a, g, e, n0, R);
+    }
+    have = false;
     gemv_dot<FMT, 1, U, C>(g, lut, lane4, R, x, v);
     if (g.li == 0) {
 #pragma unroll
@@ -695,7 +728,7 @@ __global__ __launch_bounds__(kGemvCombineThreads, 2) void gemv1c_kernel(GemmArgs
     if (n < N) {
       float acc = 0.f;
       for (int j = 0; j < k; ++j)
-        if (s_p[j] >= 0) acc = __builtin_fmaf(s_w[j], s_y[b * k + j][r], acc);
+        if (s_ip[j] >= 0) acc = __builtin_fmaf(s_w[j], s_y[b * k + s_ip[j]][r], acc);
       out[n] = acc;
     }
   }
@@ -1266,13 +1299,19 @@ static int gemv_pick_u(const GemvVariant &v, int fmt, int cols, int L_log2, int 
 
 // Rows per wave slot of the one-token gathered kernel for C chunks per lane
 // (measured fastest on the workload shapes, and free of register spills).
-// The SwiGLU epilogue needs an even U (slot u pairs with u + U/2).
+// The SwiGLU epilogue needs an even U (slot u pairs with u + U/2). C = 2 (K
+// of 4096, the Qwen3-235B-shaped gate_up): U = 3 gives each wave exactly two
+// items at 8 routed experts x 3072 rows, 4 % faster than U = 4 (1.5 items
+// per wave, the second round of half the waves in the tail); U = 2, 6 and 8
+// and issuing both items' loads before either's products were slower.
 template <int FMT, bool GLU, int ROUTE>
 static hipError_t gemv1w_dispatch(const GemmArgs &a, int C, int L_log2, int max_slots,
                                   hipStream_t s) {
   switch (C) {
     case 1: return gemv1w_go<FMT, 1, 4, GLU, ROUTE>(a, L_log2, max_slots, s);
-    case 2: return gemv1w_go<FMT, 2, 4, GLU, ROUTE>(a, L_log2, max_slots, s);
+    case 2:
+      if constexpr (GLU) return gemv1w_go<FMT, 2, 4, GLU, ROUTE>(a, L_log2, max_slots, s);
+      else return gemv1w_go<FMT, 2, 3, GLU, ROUTE>(a, L_log2, max_slots, s);
     case 3: return gemv1w_go<FMT, 3, 2, GLU, ROUTE>(a, L_log2, max_slots, s);
     case 4:
       if constexpr (FMT != GNF4_MXFP4 && !GLU) return gemv1w_go<FMT, 4, 1, GLU, ROUTE>(a, L_log2, max_slots, s);
