@@ -1098,6 +1098,11 @@ def main():
         f["steps"] = ("router top-k + softmax + route + gate_up GEMM with the SwiGLU epilogue "
                       "(bf16 H) (gnf4_route_logits_grouped_gemm), down GEMM on H + combine "
                       "(gnf4_grouped_gemm_combine): two launches at T = 1")
+        f["parity_bars"] = ("each GEMM call: max|err| <= 1e-2*rms and rel. Frobenius <= 2e-3 of the "
+                            "fp64 oracle; SwiGLU H: <= 2^-6*max|H|, Frobenius <= 6e-3; layer output "
+                            "(gate_up error through SwiGLU + H rounding + down error): max|err| <= "
+                            "3e-2*rms, Frobenius <= 6e-3 (tests/tolerance.py; tests/test_gpu_fullsize.py "
+                            "checks every element of this step at T = 1)")
         result["ffn_layer"] = f
     if out.get("dequant"):
         dqr = {}

@@ -278,6 +278,11 @@ gnf4_status gnf4_grouped_gemm_combine(const gnf4_weights *w, const uint16_t *X,
 /* gnf4_combine -- weighted top-k combine back to tokens.
  *   out[t][n] = sum_{j=0..k-1} topk_w[t][j] * Y[inv[t*k+j]][n]
  * float32, j ascending, an assignment with inv = -1 contributes nothing.
+ * The pages run the grouped kernel inside a mixture-of-experts layer behind
+ * a real router (section cited at the top, demonstration paragraph) but do
+ * not describe the step back to tokens; this is this library's reading, the
+ * weighted sum of a token's k expert outputs that defines such a layer, in
+ * a fixed order so that the result is deterministic.
  * Y float32 [T*k][N] (16-byte aligned), inv int32 [T*k], topk_w float32
  * [T][k], out float32 [T][N] (16-byte aligned). N % 4 == 0. */
 gnf4_status gnf4_combine(const float *Y, const int32_t *inv, const float *topk_w,
@@ -322,7 +327,13 @@ gnf4_status gnf4_swiglu(const float *Y, int32_t rows, int32_t I, uint16_t *H,
 
 /* gnf4_dequant -- decode expert e of w to float32 out [N][K] (test aid).
  * NF4: fp32(c[q] * absmax); NF4_DQ: fp32(c[q] * fp32(q8 * scale2));
- * MXFP4: e2m1(q) * 2^(s-127), exact (s = 255 gives NaN). */
+ * MXFP4: e2m1(q) * 2^(s-127), exact (s = 255 gives NaN). The pages name the
+ * formats (NF4 on the bitsandbytes layout, MXFP4 as e2m1 codes with e8m0
+ * scales: section cited at the top, first and third bullets) but print no
+ * decode rule; this is the reading of the weight layout above (QLoRA
+ * NormalFloat-4 table times the block absmax; OCP MX e2m1 times 2^(s-127)).
+ * The GEMMs never write this decode anywhere: it lets tests check the
+ * device's decode bit for bit against the CPU oracle. */
 gnf4_status gnf4_dequant(const gnf4_weights *w, int32_t e, float *out, gnf4_stream_t stream);
 
 /* gnf4_dequant_experts_bf16 -- the decode step of the dequantize-then-matmul
