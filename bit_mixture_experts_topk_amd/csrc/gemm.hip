@@ -823,33 +823,29 @@ __device__ __forceinline__ int k16_seg(int p, int j) { return 4 * (p & 1) + 2 * 
 
 constexpr int kBufferDword3 = 0x00020000;   // raw buffer, 32-bit data format
 
+// Rows of a tile: 4 row tiles of 16 (the layout above); the A staging
+// buffer is sized for them.
+constexpr int kMfmaRowTiles = 4;
+constexpr int kMfmaSegs = 16 * kMfmaRowTiles * 8;   // 16-byte A segments per block
+
+// One workgroup's tile (expert e, weight-column tile nt, routed rows row0 +
+// [0, rows_valid)) computed with RT row tiles of 16 (rows_valid <= 16 * RT).
 template <int FMT, int RT, bool BIGX, bool GLU, bool GATHER>
-__global__ __launch_bounds__(kThreads, 2) void mfma16_kernel(GemmArgs a, int n_tiles_n,
-                                                             uint32_t x_bytes) {
+__device__ __forceinline__ void mfma16_tile(const GemmArgs &a, uint32_t x_bytes, uint32_t *lut,
+                                            uint4 (*As)[kMfmaSegs], int e, int nt, int row0,
+                                            int rows_valid) {
   // NF4 and NF4_DQ decode through the table and scale each block's partial;
   // MXFP4 folds its scale into the conversion.
   constexpr bool kLut = FMT != GNF4_MXFP4;
   constexpr bool kDQ = FMT == GNF4_NF4_DQ;
   constexpr bool kWin = kLut;                   // absmax handled in 8-block windows
   constexpr int BM = 16 * RT, BN = 256;
-  static_assert(RT >= 1 && RT <= 5, "16 to 80 rows");
+  static_assert(RT >= 1 && RT <= kMfmaRowTiles, "16 to 64 rows");
   constexpr int kSegs = BM * 8;                 // 16-byte A segments per block
   constexpr int kALoads = (kSegs + kThreads - 1) / kThreads;
-  __shared__ uint32_t lut[kLut ? kLutWords : 1];
-  __shared__ uint4 As[2][kSegs];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int N = a.w.N, K = a.w.K;
-  int e, start, tiles;
-  const int bid = xcd_remap(blockIdx.x, gridDim.x);
-  find_tile<BM>(a, bid, n_tiles_n, lane, e, start, tiles);
-  if (e < 0) return;
-  const int local = bid - start;
-  const int nt = local / tiles, mt = local - nt * tiles;
-  const int seg_start = a.offsets[e];
-  const int count = a.offsets[e + 1] - seg_start;
-  const int row0 = seg_start + mt * BM;
-  const int rows_valid = min(BM, count - mt * BM);
   const int nb = GLU ? nt * (BN / 2) + wave * 32  // this wave's first (output) column
                      : nt * BN + wave * 64;
   const int half = a.w.N / 2;
@@ -1143,6 +1139,43 @@ __global__ __launch_bounds__(kThreads, 2) void mfma16_kernel(GemmArgs a, int n_t
         }
       }
   }
+}
+
+// Tiles are enumerated expert by expert with 64-row M tiles; an expert's
+// last tile holds count % 64 rows (when not 0), so the tile body is compiled
+// for 1 to 4 row tiles of 16 and each workgroup runs the smallest that
+// holds its rows: a tile of 20 rows issues the MFMAs, activation loads and
+// scale multiplies of 32 rows, not 64 (the B decode is the same). The
+// branch is uniform over the workgroup.
+template <int FMT, int RT, bool BIGX, bool GLU, bool GATHER>
+__global__ __launch_bounds__(kThreads, 2) void mfma16_kernel(GemmArgs a, int n_tiles_n,
+                                                             uint32_t x_bytes) {
+  static_assert(RT == kMfmaRowTiles, "64-row tiles");
+  constexpr bool kLut = FMT != GNF4_MXFP4;
+  constexpr int BM = 16 * RT;
+  __shared__ uint32_t lut[kLut ? kLutWords : 1];
+  __shared__ uint4 As[2][kMfmaSegs];
+
+  const int lane = threadIdx.x & 63;
+  int e, start, tiles;
+  const int bid = xcd_remap(blockIdx.x, gridDim.x);
+  find_tile<BM>(a, bid, n_tiles_n, lane, e, start, tiles);
+  if (e < 0) return;
+  const int local = bid - start;
+  const int nt = local / tiles, mt = local - nt * tiles;
+  const int seg_start = a.offsets[e];
+  const int count = a.offsets[e + 1] - seg_start;
+  const int row0 = seg_start + mt * BM;
+  const int rows_valid = min(BM, count - mt * BM);
+  const int rt = (rows_valid + 15) >> 4;
+  if (rt >= 4)
+    mfma16_tile<FMT, 4, BIGX, GLU, GATHER>(a, x_bytes, lut, As, e, nt, row0, rows_valid);
+  else if (rt == 3)
+    mfma16_tile<FMT, 3, BIGX, GLU, GATHER>(a, x_bytes, lut, As, e, nt, row0, rows_valid);
+  else if (rt == 2)
+    mfma16_tile<FMT, 2, BIGX, GLU, GATHER>(a, x_bytes, lut, As, e, nt, row0, rows_valid);
+  else
+    mfma16_tile<FMT, 1, BIGX, GLU, GATHER>(a, x_bytes, lut, As, e, nt, row0, rows_valid);
 }
 
 // ============================================================ host launch

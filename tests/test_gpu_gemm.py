@@ -251,3 +251,39 @@ def test_tiny_layer_end_to_end(T):
     r = g.route(torch.from_numpy(ids).cuda(), cfg.E)
     out = g.combine(torch.from_numpy(Y).cuda(), r["inv"], torch.from_numpy(tw).cuda(), T, cfg.k)
     assert_within(out.cpu().numpy(), oracle_combine(Y_ref, r_ref, tw, T, cfg.k), "tiny combine")
+
+
+@pytest.mark.parametrize("fmt", ["nf4", "nf4_dq", "mxfp4"])
+@pytest.mark.parametrize("gather", [1, 0])
+@pytest.mark.parametrize("swiglu", [False, True])
+def test_mfma_last_tile_row_classes(fmt, gather, swiglu):
+    """The prefill kernel computes an expert's last 64-row tile with only the
+    16-row tiles that hold rows: 65, 81, 97 and 113 routed rows leave last
+    tiles of 1, 17, 33 and 49 rows (one, two, three and four 16-row tiles).
+    Every element against the oracle (Y, or H with the SwiGLU epilogue)."""
+    from oracle import layer as olayer
+    from .tolerance import assert_within_h
+    g = gnf4()
+    E, N, K, k = 4, 320, 512, 1
+    counts = [65, 81, 97, 113]
+    ids = np.concatenate([np.full(c, e, dtype=np.int32) for e, c in enumerate(counts)])
+    ids = np.random.default_rng(31).permutation(ids).reshape(-1, 1)
+    T = ids.shape[0]
+    case = synth.small_layer(E, N, K, T, k, seed=12, gather=gather)
+    codes, scales, scales2 = oracle_pack(fmt, case["W"])
+    pw = packed_to_device(g, fmt, codes, scales, scales2, E, N, K)
+    say("mfma last tiles", fmt, "gather", gather, "swiglu", swiglu)
+    r = g.route(torch.from_numpy(ids).cuda(), E)
+    Xd = bits_to_device(case["X"])
+    got = (g.grouped_gemm_swiglu(pw, Xd, gather, r, T, k) if swiglu
+           else g.grouped_gemm(pw, Xd, gather, r, T, k)).cpu().numpy()
+    ref_r = routing.route(ids, E)
+    Y_ref = ogemm.grouped_gemm(fmt, codes, scales, scales2, case["X"], gather, ref_r["offsets"],
+                               ref_r["perm"], k, N, K)
+    if swiglu:
+        H_ref = olayer.swiglu(Y_ref, N // 2)
+        Hg = (got.view(np.uint16).astype(np.uint32) << 16).view(np.float32)
+        Hr = (H_ref.astype(np.uint32) << 16).view(np.float32)
+        assert_within_h(Hg, Hr, "H last tiles %s" % fmt)
+    else:
+        assert_within(got, Y_ref, "last tiles %s gather %d" % (fmt, gather))
