@@ -628,7 +628,9 @@ constexpr int kGemvCombineThreads = 512;
 __device__ __forceinline__ int gemv1c_expert(const GemmArgs &a, int p) {
   const int E = a.w.E;
   const int e = p < E ? a.active[p] : -1;
-  if (e >= 0 && a.offsets[e] == p && a.offsets[e + 1] == p + 1) return e;
+  const int ec = max(e, 0);
+  const int o0 = a.offsets[ec], o1 = a.offsets[ec + 1];
+  if ((e >= 0) & (o0 == p) & (o1 == p + 1)) return e;
   if (p >= a.offsets[E]) return -1;
   int lo = 0, hi = E;
   while (hi - lo > 1) {
@@ -694,9 +696,12 @@ __global__ __launch_bounds__(kGemvCombineThreads, 2) void gemv1c_kernel(GemmArgs
   if (q < G * k && (nb0 + q / k) * g.rows_per_item < N) {
     const int p = q % k;
     const int e = p < E ? a.active[p] : -1;
+    const int ec = max(e, 0);
     gemv_load_x_row<C>(a, g, p, x);
-    gemv_load_rows<FMT, U, C, false>(a, g, max(e, 0), (nb0 + q / k) * g.rows_per_item, R);
-    have = e >= 0 && a.offsets[e] == p && a.offsets[e + 1] == p + 1;
+    gemv_load_rows<FMT, U, C, false>(a, g, ec, (nb0 + q / k) * g.rows_per_item, R);
+    // both offsets in one round trip (no short-circuit between the loads)
+    const int o0 = a.offsets[ec], o1 = a.offsets[ec + 1];
+    have = (e >= 0) & (o0 == p) & (o1 == p + 1);
   }
   if (tid < k) {
     s_ip[tid] = vi;
