@@ -255,6 +255,9 @@ def summarize(args):
             t = traffic["FETCH_SIZE"] + traffic["WRITE_SIZE"]
             lines.append("traffic_bytes_per_launch: %d" % int(round(t)))
             lines.append("traffic_over_algorithmic: %.3f" % (t / args.alg_bytes))
+    import shlex
+    lines += ["", "summary command (from the repository root):",
+              "  python bench.py " + " ".join(shlex.quote(x) for x in sys.argv[1:])]
     if args.kernel:
         lines.append("kernel_source: %s" % args.source)
         lines.append("source_sha256: %s" % hashlib.sha256(open(os.path.join(ROOT, args.source), "rb")
@@ -595,6 +598,13 @@ def gate_up_launch(gnf4, sl):
         gnf4.grouped_gemm(sl.layer.projs[0], sl.X, 1, sl.r, sl.T, cfg.k, sl.Y[0])
 
 
+def down_launch(gnf4, sl):
+    """The down launch of the step (T = 1: the GEMV with the combine fused;
+    otherwise the GEMM and then the combine kernel)."""
+    cfg = sl.layer.cfg
+    gnf4.grouped_gemm_combine(sl.layer.projs[1], sl.Xd, sl.r, sl.tw, sl.T, cfg.k, sl.out, Y=sl.Y[1])
+
+
 def gate_up_dx_launch(gnf4, sl):
     cfg = sl.layer.cfg
     gnf4.grouped_gemm_dx(sl.layer.projs[0], sl.dY[0], sl.r, sl.T, cfg.k, sl.dA[0])
@@ -660,27 +670,34 @@ def gemm_kernel_name(cfg, T):
     return "mfma16_kernel"
 
 
-def profile_traffic(cfg_name, mode, kernel=None):
-    """HBM bytes per launch of the gate_up kernel (the forward GEMM's, or the
-    named kernel's) from the committed rocprofv3 counter summary for this
-    workload, if the kernel's source is unchanged since the counters were
-    taken (else None)."""
-    import glob
+def profile_fields(path):
+    """The `key: value` lines of a committed summary under profiles/ when the
+    kernel source it names is unchanged since it was taken (else None)."""
     import hashlib
-    pattern = "%s-gate_up-%s-%s.txt" % (kernel or "*", cfg_name, mode)
+    fields = {}
+    for line in open(path):
+        if ":" in line and not line.startswith(" "):
+            key, _, val = line.partition(":")
+            fields[key.strip()] = val.strip()
+    src = fields.get("kernel_source")
+    if not src or "traffic_bytes_per_launch" not in fields:
+        return None
+    digest = hashlib.sha256(open(os.path.join(ROOT, src), "rb").read()).hexdigest()
+    return fields if digest == fields.get("source_sha256") else None
+
+
+def profile_traffic(cfg_name, mode, kernel=None, proj="gate_up"):
+    """HBM bytes per launch of the kernel that runs projection `proj` (the
+    forward GEMM's, or the named kernel's) from the committed rocprofv3
+    counter summary profiles/<kernel>-<proj>-<workload>-<mode>.txt, if the
+    kernel's source is unchanged since the counters were taken (else None)."""
+    import glob
+    pattern = "%s-%s-%s-%s.txt" % (kernel or "*", proj, cfg_name, mode)
     for path in sorted(glob.glob(os.path.join(ROOT, "profiles", pattern))):
         if kernel is None and "_dx_kernel" in os.path.basename(path):
             continue
-        fields = {}
-        for line in open(path):
-            if ":" in line and not line.startswith(" "):
-                key, _, val = line.partition(":")
-                fields[key.strip()] = val.strip()
-        src = fields.get("kernel_source")
-        if not src or "traffic_bytes_per_launch" not in fields:
-            continue
-        digest = hashlib.sha256(open(os.path.join(ROOT, src), "rb").read()).hexdigest()
-        if digest == fields.get("source_sha256"):
+        fields = profile_fields(path)
+        if fields:
             return int(fields["traffic_bytes_per_launch"]), os.path.relpath(path, ROOT)
     return None, None
 
@@ -936,6 +953,10 @@ def main():
         out["decode"] = dict(T=T_dec, ms_per_step=dt * 1e3, gbs=byts / dt / 1e9,
                              kernel_us=kms * 1e3, kernel_bytes=kbytes, copies=copies,
                              graph_launches=glaunch)
+        if len(cfg.projs) > 1:
+            dms, _, _, _ = time_kernel(torch, gnf4, slots, args.steps, args.warmup, down_launch)
+            dbytes = np.mean([sl.n_active * sl.layer.projs[1].nbytes() // cfg.E for sl in slots])
+            out["decode"]["down"] = (dms * 1e3, dbytes)
         del slots, layers
         torch.cuda.empty_cache()
         out["decode"]["read"] = time_read_probe(torch, gnf4, kbytes)
@@ -949,6 +970,11 @@ def main():
         kms, kbytes, kfl, _ = time_kernel(torch, gnf4, slots, steps, max(2, args.warmup // 5))
         out["prefill"] = dict(T=T_pre, ms_per_step=dt * 1e3, tflops=fl / dt / 1e12, steps=steps,
                               kernel_us=kms * 1e3, kernel_flops=kfl, copies=copies)
+        if len(cfg.projs) > 1:
+            dms, _, _, _ = time_kernel(torch, gnf4, slots, steps, max(2, args.warmup // 5), down_launch)
+            dn = cfg.projs[1]
+            dfl = np.mean([2.0 * sl.T * cfg.k * dn.N * dn.K for sl in slots])
+            out["prefill"]["down"] = (dms * 1e3, dfl)
         del slots, layers
         torch.cuda.empty_cache()
 
@@ -1067,6 +1093,15 @@ def main():
         result["decode"] = {"step_us": round(d["ms_per_step"] * 1e3, 3),
                             "pct_hbm_peak_step": round(100 * d["gbs"] / HBM_PEAK_GBS, 2),
                             "weight_copies": d["copies"]}
+        if "down" in d:
+            dus, dbytes = d["down"]
+            dtr, dsrc = profile_traffic(cfg.name, "decode", "gemv1c_kernel", "down")
+            result["decode"]["down_kernel"] = {
+                "kernel": "gemv1c_kernel (down GEMV + combine, T=%d)" % d["T"],
+                "kernel_us": round(dus, 3), "bytes_per_launch": int(dbytes),
+                "GBps": round(dbytes / (dus * 1e-6) / 1e9, 1),
+                "frac_hbm_peak": round(dbytes / (dus * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                "traffic": dtr, "traffic_source": dsrc}
     if "prefill" in out:
         p = out["prefill"]
         kt = p["kernel_flops"] / (p["kernel_us"] * 1e-6) / 1e12
@@ -1080,6 +1115,15 @@ def main():
                                           "traffic_unit": "HBM bytes/launch", "traffic_source": ptsrc,
                                           "kernel": "%s (gate_up, T=%d)" % (gemm_kernel_name(cfg, p["T"]), p["T"]),
                                           "kernel_us": round(p["kernel_us"], 2)}}
+        if "down" in p:
+            dus, dfl = p["down"]
+            dtr, dsrc = profile_traffic(cfg.name, "prefill", "mfma16_kernel", "down")
+            result["prefill"]["down_kernel"] = {
+                "kernel": "mfma16_kernel + combine_kernel (down GEMM, then the combine, T=%d)" % p["T"],
+                "us": round(dus, 2), "gemm_flops": dfl,
+                "tflops": round(dfl / (dus * 1e-6) / 1e12, 2),
+                "frac_mfma_peak": round(dfl / (dus * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 4),
+                "gemm_traffic": dtr, "traffic_source": dsrc}
         if "decode" not in out:
             result["value"] = round(p["tflops"], 3)
             result["unit"] = "TFLOP/s"
