@@ -547,6 +547,28 @@ def time_steps(torch, gnf4, slots, steps, warmup):
     return dt, per, fl
 
 
+def time_steps_eager(torch, gnf4, slots, steps, warmup):
+    """Time `steps` consecutive steps launched one call at a time from the host
+    (no graph), step i on slot i % len(slots), between HIP events on the
+    launch stream: the time per step includes each launch's host submission
+    cost wherever the GPU waits for it."""
+    G = len(slots)
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        for i in range(max(warmup, 1)):
+            slots[i % G].run(gnf4)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        a.record(stream)
+        for i in range(steps):
+            slots[i % G].run(gnf4)
+        b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) * 1e-3 / steps
+
+
 def time_read_probe(torch, gnf4, nbytes, launches=64):
     """Achievable HBM read rate for `nbytes` read once: gnf4_read_probe over
     rotating buffers that together exceed 3x the Infinity Cache, `launches`
@@ -1015,8 +1037,12 @@ def main():
                      for i in range(nsl)]
             steps = args.steps if tag == "decode" else max(10, args.steps // 10)
             dt, byts, fl = time_steps(torch, gnf4, slots, steps, max(2, args.warmup // 5))
-            dq[tag] = (T, dt)
-            del slots, layers, wbuf
+            dt_eager = time_steps_eager(torch, gnf4, slots, steps, max(2, args.warmup // 5))
+            del slots
+            fslots = [StepSlot(torch, gnf4, cfg, layers[i % copies], T, 400 + i) for i in range(nsl)]
+            fused_eager = time_steps_eager(torch, gnf4, fslots, steps, max(2, args.warmup // 5))
+            dq[tag] = (T, dt, dt_eager, fused_eager)
+            del fslots, layers, wbuf
             torch.cuda.empty_cache()
         out["dequant"] = dq
 
@@ -1150,13 +1176,20 @@ def main():
         result["ffn_layer"] = f
     if out.get("dequant"):
         dqr = {}
-        for tag, (T, dt) in out["dequant"].items():
+        for tag, (T, dt, dt_eager, fused_eager) in out["dequant"].items():
             fused = out[tag]["ms_per_step"] * 1e-3 if tag in out else None
             dqr[tag] = {"T": T, "step_us": round(dt * 1e6, 2),
-                        "fused_speedup": round(dt / fused, 3) if fused else None}
+                        "fused_speedup": round(dt / fused, 3) if fused else None,
+                        "ungraphed_step_us": round(dt_eager * 1e6, 2),
+                        "fused_ungraphed_step_us": round(fused_eager * 1e6, 2),
+                        "fused_ungraphed_vs_graphed_dequant": round(dt / fused_eager, 3)}
         dqr["steps"] = ("route, bf16 dequant of the routed experts of each projection "
                         "(gnf4_dequant_experts_bf16), torch.bmm (T = 1) or one torch.mm per "
-                        "active expert (library GEMMs), combine; same inputs as the fused step")
+                        "active expert (library GEMMs), combine; same inputs as the fused step; "
+                        "step_us replays the steps as graphs, ungraphed_step_us launches them "
+                        "from the host one call at a time (both event-timed on the GPU), and "
+                        "fused_ungraphed_vs_graphed_dequant is the graphed dequant step over "
+                        "the host-launched fused step")
         result["dequant_path"] = dqr
     if out.get("backward"):
         b = {}
