@@ -291,6 +291,46 @@ __device__ __forceinline__ void gemv_load_x_row(const GemmArgs &a, const GemvGeo
   }
 }
 
+// The one-token kernels stage a token row in LDS once per workgroup, so that
+// the row is read from L2 once per workgroup rather than once per wave (every
+// wave of the grid reads the same row, and a few L2 channels serve it). K is
+// at most 64 lanes x 4 chunks x 32 values there.
+constexpr int kGemv1MaxK = 8192;
+
+// LDS slot of 16-byte piece j (0..3) of K chunk ch of a staged token row. The
+// pieces of a chunk are permuted by the chunk index, so that the lanes that
+// read consecutive chunks at one j fall on distinct banks (8 lanes of 16
+// bytes cover 32 banks, 16 lanes 64 banks).
+__device__ __forceinline__ int xs_slot(int ch, int j) {
+  return ch * 4 + (j ^ (((ch >> 1) ^ (ch >> 3)) & 3));
+}
+
+// Staging a token row of K / 8 <= 1024 16-byte pieces: piece i is copied
+// by thread first + (i mod stride), r = i / stride; at most two per thread
+// (stride >= 512). The piece of round r of thread tid, -1 if none.
+__device__ __forceinline__ int xs_piece(int tid, int first, int stride, int r, int n) {
+  const int i = tid - first + r * stride;
+  return (tid >= first && tid - first < stride && i < n) ? i : -1;
+}
+
+// A wave's token slice from the row staged in LDS (as gemv_load_x_row).
+template <int C>
+__device__ __forceinline__ void gemv_lds_x_row(const uint4 *s_x, const GemvGeom &g,
+                                               uint32_t (&x)[1][C][16]) {
+#pragma unroll
+  for (int c = 0; c < C; ++c) {
+    const int ch = min(g.li + c * g.L, g.KCH - 1);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint4 v = s_x[xs_slot(ch, j)];
+      x[0][c][4 * j + 0] = v.x;
+      x[0][c][4 * j + 1] = v.y;
+      x[0][c][4 * j + 2] = v.z;
+      x[0][c][4 * j + 3] = v.w;
+    }
+  }
+}
+
 // GEMV: one workgroup per (active slot, row block) item, blockIdx.x = slot *
 // items_per_expert + block; each wave holds U row slots of C chunks per lane
 // in flight. The small routing arrays (offsets and the source row of every
@@ -443,7 +483,8 @@ __global__ __launch_bounds__(kThreads, 2) void gemv1_kernel(GemmArgs a, int L_lo
 // decodes, the others' rows are in flight. Each wave walks its own items (a
 // slot and a block of RW * U rows) of the n_active * items_per_expert items,
 // interleaved over the CUs. Lane j holds slot j's expert and routed-row
-// range, read once: one token has at most 64 slots.
+// range, read once: one token has at most 64 slots. The token row is staged
+// in LDS once per workgroup.
 constexpr int kGemvWaveThreads = 1024;
 
 // Routing of one token's k <= 64 assignments, from the ids alone, computed
@@ -552,6 +593,7 @@ __global__ __launch_bounds__(kGemvWaveThreads, 1) void gemv1w_kernel(GemmArgs a,
   constexpr int kWaves = kGemvWaveThreads / 64;
   __shared__ uint32_t lut[kLut ? kLutWords : 1];
   __shared__ OneTokenRoute sr;
+  __shared__ uint4 s_x[kGemv1MaxK / 8];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const uint32_t lane4 = (uint32_t)lane << 2;
@@ -570,8 +612,16 @@ __global__ __launch_bounds__(kGemvWaveThreads, 1) void gemv1w_kernel(GemmArgs a,
 
   int nact, ej, pj0, pj1;                        // slot lane's expert and routed rows
   uint32_t x[1][C][16];
-  gemv_load_x_row<C>(a, g, 0, x);
+  // the token row to LDS, loaded by waves 1.. (wave 0 routes); the barrier
+  // below publishes it with the table
+  const int xp0 = xs_piece(tid, 64, kGemvWaveThreads - 64, 0, a.w.K / 8);
+  const int xp1 = xs_piece(tid, 64, kGemvWaveThreads - 64, 1, a.w.K / 8);
+  uint4 xv0, xv1;
+  if (xp0 >= 0) xv0 = reinterpret_cast<const uint4 *>(a.X)[xp0];
+  if (xp1 >= 0) xv1 = reinterpret_cast<const uint4 *>(a.X)[xp1];
   if constexpr (kLut) fill_nf4_lut<kGemvWaveThreads>(lut, tid);
+  if (xp0 >= 0) s_x[xs_slot(xp0 >> 2, xp0 & 3)] = xv0;
+  if (xp1 >= 0) s_x[xs_slot(xp1 >> 2, xp1 & 3)] = xv1;
   if constexpr (ROUTE) {
     route_one_token<ROUTE == 2>(a, sr, tid);      // ends with a barrier: table written too
     nact = sr.nact;
@@ -587,6 +637,7 @@ __global__ __launch_bounds__(kGemvWaveThreads, 1) void gemv1w_kernel(GemmArgs a,
     pj1 = a.offsets[ejc + 1];
     __syncthreads();                              // decode table written
   }
+  gemv_lds_x_row<C>(s_x, g, x);
 
   const int total = nact * ipe;
   const int W = (int)gridDim.x * kWaves;
