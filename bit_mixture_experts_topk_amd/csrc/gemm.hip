@@ -857,13 +857,16 @@ __device__ __forceinline__ void find_tile(const GemmArgs &a, int bid, int n_tile
 // same K values, so each block's two MFMAs form a partial that the block's
 // absmax scales before accumulation.
 //
-// Absmax values are read 8 blocks per column at a time: lane (p, c) holds
-// blocks 2p, 2p + 1 of the window for column c, and each block's value
-// reaches the 4 lanes of its column through ds_bpermute. NF4_DQ loads the two
-// int8 values and their second-level scales with the window and forms the
-// float32 absmax when the window comes into use. MXFP4 instead has each lane
-// read the e8m0 scale of its own 32-K group per block and pass it to the
-// conversion, which makes a scaled partial unnecessary. Activation rows are
+// Scales are read 8 blocks per column at a time: lane (p, c) holds blocks
+// 2p, 2p + 1 of the window for column c, and each block's value reaches the
+// 4 lanes of its column through ds_bpermute. NF4_DQ loads the two int8
+// values and their second-level scales with the window and forms the float32
+// absmax when the window comes into use. MXFP4 holds the four e8m0 bytes of
+// the two blocks (two 32-K groups each); each lane takes the byte of its own
+// group and passes it to the conversion, which makes a scaled partial
+// unnecessary. (Reading the bytes block by block instead, one uncoalesced
+// byte load per column tile and block, made the MXFP4 call 27 % slower on the
+// gpt-oss shape.) Activation rows are
 // staged through LDS per block, double buffered. All global reads are
 // buffer loads: a uniform base per expert (or the activation tensor) plus a
 // fixed 32-bit lane offset and a uniform step offset; reads past a column's
@@ -894,7 +897,7 @@ __device__ __forceinline__ void mfma16_tile(const GemmArgs &a, uint32_t x_bytes,
   // MXFP4 folds its scale into the conversion.
   constexpr bool kLut = FMT != GNF4_MXFP4;
   constexpr bool kDQ = FMT == GNF4_NF4_DQ;
-  constexpr bool kWin = kLut;                   // absmax handled in 8-block windows
+  constexpr bool kMX = FMT == GNF4_MXFP4;
   constexpr int BM = 16 * RT, BN = 256;
   static_assert(RT >= 1 && RT <= kMfmaRowTiles, "16 to 64 rows");
   constexpr int kSegs = BM * 8;                 // 16-byte A segments per block
@@ -915,7 +918,7 @@ __device__ __forceinline__ void mfma16_tile(const GemmArgs &a, uint32_t x_bytes,
       (void *)(a.w.codes + erow * (K / 2)), (short)0, (int)((uint32_t)N * (uint32_t)(K / 2)),
       kBufferDword3);
   // NF4: float32 absmax [N][K/64]; NF4_DQ: int8 [N][K/64]; MXFP4: e8m0 bytes [N][K/32]
-  const uint32_t scale_row = kDQ ? (uint32_t)(K / 64) : kWin ? (uint32_t)(K / 16) : (uint32_t)(K / 32);
+  const uint32_t scale_row = kDQ ? (uint32_t)(K / 64) : kMX ? (uint32_t)(K / 32) : (uint32_t)(K / 16);
   const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
       (void *)(reinterpret_cast<const uint8_t *>(a.w.scales) + erow * scale_row), (short)0,
       (int)((uint32_t)N * scale_row), kBufferDword3);
@@ -956,7 +959,7 @@ __device__ __forceinline__ void mfma16_tile(const GemmArgs &a, uint32_t x_bytes,
                              : (uint32_t)min(nb + ct * 16 + c16, N - 1);
     coff[ct] = col * (uint32_t)(K / 2) + 16u * (uint32_t)p;
     soff[ct] = kDQ ? col * scale_row + 2u * (uint32_t)p
-               : kWin ? col * scale_row + 8u * (uint32_t)p : col * scale_row + (uint32_t)(p & 1);
+               : kMX ? col * scale_row + 4u * (uint32_t)p : col * scale_row + 8u * (uint32_t)p;
     fblk[ct] = (erow + col) * nkb + 2 * p;
   }
 
@@ -971,7 +974,8 @@ __device__ __forceinline__ void mfma16_tile(const GemmArgs &a, uint32_t x_bytes,
   uint2 sw[4], sn[4];                 // absmax window (current / next): blocks 2p, 2p+1
   uint32_t dn[4];                     // NF4_DQ next window: int8 absmax of blocks 2p, 2p+1
   uint2 tn[4];                        //   and their second-level scales
-  uint32_t sb0[4], sb1[4];            // MXFP4 scale bytes ring (even / odd blocks)
+  uint32_t xw[4], xn[4];              // MXFP4 window (current / next): the e8m0 bytes of
+                                      //   blocks 2p, 2p+1 (two 32-K groups each)
 
 #define GNF4_LOAD_STAGE(S, Q)                                                             \
   {                                                                                       \
@@ -1000,6 +1004,10 @@ __device__ __forceinline__ void mfma16_tile(const GemmArgs &a, uint32_t x_bytes,
       const int64_t f_ = fblk[ct] + 8 * (W);                                              \
       tn[ct].x = __builtin_amdgcn_raw_buffer_load_b32(rs2, (uint32_t)(f_ >> 8) * 4u, 0, 0); \
       tn[ct].y = __builtin_amdgcn_raw_buffer_load_b32(rs2, (uint32_t)((f_ + 1) >> 8) * 4u, 0, 0); \
+    } else if constexpr (kMX) {                                                           \
+      /* two 16-bit loads (K / 32 is even, so the offsets are too) */                     \
+      xn[ct] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rs, soff[ct], 16 * (W), 0) | \
+               ((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rs, soff[ct], 16 * (W) + 2, 0) << 16); \
     } else {                                                                              \
       sn[ct] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rs, soff[ct], 32 * (W), 0)); \
     }                                                                                     \
@@ -1009,8 +1017,11 @@ __device__ __forceinline__ void mfma16_tile(const GemmArgs &a, uint32_t x_bytes,
   // group's scale
 #define GNF4_TAKE_WINDOW()                                                                \
   _Pragma("unroll") for (int ct = 0; ct < 4; ++ct) {                                     \
-    float a0_, a1_;                                                                       \
-    if constexpr (kDQ) {                                                                  \
+    float a0_ = 0.f, a1_ = 0.f;                                                           \
+    if constexpr (kMX) {                                                                  \
+      xw[ct] = xn[ct];                                                                    \
+      continue;                                                                           \
+    } else if constexpr (kDQ) {                                                                  \
       a0_ = (float)(int8_t)(dn[ct] & 0xffu) * __builtin_bit_cast(float, tn[ct].x);        \
       a1_ = (float)(int8_t)((dn[ct] >> 8) & 0xffu) * __builtin_bit_cast(float, tn[ct].y); \
     } else {                                                                              \
@@ -1020,16 +1031,8 @@ __device__ __forceinline__ void mfma16_tile(const GemmArgs &a, uint32_t x_bytes,
     sw[ct].x = __builtin_bit_cast(uint32_t, a0_ * kNF4InvScale);                          \
     sw[ct].y = __builtin_bit_cast(uint32_t, a1_ * kNF4InvScale);                          \
   }
-#define GNF4_LOAD_SBYTES(KB, SB)                                                          \
-  _Pragma("unroll") for (int ct = 0; ct < 4; ++ct)                                       \
-      SB[ct] = __builtin_amdgcn_raw_buffer_load_b8(rs, soff[ct], 2 * min((KB), nkb - 1), 0);
 
-  if constexpr (kWin) {
-    GNF4_LOAD_WINDOW(0);
-  } else {
-    GNF4_LOAD_SBYTES(0, sb0);
-    GNF4_LOAD_SBYTES(1, sb1);
-  }
+  GNF4_LOAD_WINDOW(0);
   GNF4_LOAD_STAGE(0, qs0);
   GNF4_LOAD_A(0, ar0);
   GNF4_LOAD_A(1, ar1);
@@ -1059,20 +1062,17 @@ __device__ __forceinline__ void mfma16_tile(const GemmArgs &a, uint32_t x_bytes,
   }
 
   // One 64-K block KB = 2 S + B of stage S, codes in Q. AC: this block's A
-  // staging registers (refilled with block KB + 2); AN: block KB + 1's. SB:
-  // this block's MXFP4 scale bytes (refilled with block KB + 2).
-#define GNF4_BLOCK(S, B, Q, AC, AN, SB)                                                   \
+  // staging registers (refilled with block KB + 2); AN: block KB + 1's.
+#define GNF4_BLOCK(S, B, Q, AC, AN)                                                       \
   {                                                                                       \
     const int kb = 2 * (S) + (B);                                                         \
     __builtin_amdgcn_sched_barrier(0);                                                    \
     __syncthreads(); /* As[kb & 1] holds block kb; As[(kb & 1) ^ 1] is free */            \
     __builtin_amdgcn_sched_barrier(0);                                                    \
     if ((B) == 0) {                                                                       \
-      if constexpr (kWin) {                                                               \
-        if (((S) & 3) == 0) {                                                             \
-          GNF4_TAKE_WINDOW();                                                             \
-          GNF4_LOAD_WINDOW(((S) >> 2) + 1);                                               \
-        }                                                                                 \
+      if (((S) & 3) == 0) {                                                               \
+        GNF4_TAKE_WINDOW();                                                               \
+        GNF4_LOAD_WINDOW(((S) >> 2) + 1);                                                 \
       }                                                                                   \
       _Pragma("unroll") for (int ct = 0; ct < 4; ++ct) {                                 \
         auto r0 = __builtin_amdgcn_permlane32_swap(Q[ct].x, Q[ct].z, false, false);      \
@@ -1080,18 +1080,22 @@ __device__ __forceinline__ void mfma16_tile(const GemmArgs &a, uint32_t x_bytes,
         Q[ct] = make_uint4(r0[0], r1[0], r0[1], r1[1]);                                   \
       }                                                                                   \
     }                                                                                     \
-    /* NF4, NF4_DQ: absmax of block kb for this lane's column: window slot */            \
-    /* kb & 7, held by lane group (kb & 7) >> 1 = S & 3, element kb & 1 = B. */            \
-    /* MXFP4: the scale of the lane's own 32-K group, loaded two blocks ahead */          \
+    /* The block's scale for this lane's column sits in window slot kb & 7, */           \
+    /* held by lane group (kb & 7) >> 1 = S & 3. NF4, NF4_DQ: the absmax, */              \
+    /* element kb & 1 = B. MXFP4: the e8m0 byte of the lane's own 32-K group */           \
+    /* (p & 1), byte 2 B + (p & 1) of the group's dword. */                              \
     float scl[4];                                                                         \
-    if constexpr (kWin) {                                                                 \
+    {                                                                                     \
       const int src = (16 * ((S) & 3) + c16) << 2;                                        \
-      _Pragma("unroll") for (int ct = 0; ct < 4; ++ct)                                   \
-        scl[ct] = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(                \
-            src, (int)((B) == 0 ? sw[ct].x : sw[ct].y)));                                 \
-    } else {                                                                              \
-      _Pragma("unroll") for (int ct = 0; ct < 4; ++ct) scl[ct] = e8m0_to_f32(SB[ct] & 0xffu); \
-      GNF4_LOAD_SBYTES(kb + 2, SB);                                                       \
+      _Pragma("unroll") for (int ct = 0; ct < 4; ++ct) {                                 \
+        if constexpr (kMX) {                                                              \
+          const uint32_t w_ = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)xw[ct]);   \
+          scl[ct] = e8m0_to_f32((w_ >> (16 * (B) + 8 * (p & 1))) & 0xffu);                \
+        } else {                                                                          \
+          scl[ct] = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(              \
+              src, (int)((B) == 0 ? sw[ct].x : sw[ct].y)));                               \
+        }                                                                                 \
+      }                                                                                   \
     }                                                                                     \
     GNF4_LOAD_A(kb + 2, AC);                                                              \
     const uint4 *Ab = As[kb & 1];                                                         \
@@ -1148,18 +1152,17 @@ __device__ __forceinline__ void mfma16_tile(const GemmArgs &a, uint32_t x_bytes,
   // stages in pairs (slot qs0 even, qs1 odd); a trailing odd block ends early
   int S = 0;
   for (; S + 1 < nst; S += 2) {
-    GNF4_BLOCK(S, 0, qs0, ar0, ar1, sb0);
-    GNF4_BLOCK(S, 1, qs0, ar1, ar0, sb1);
-    GNF4_BLOCK(S + 1, 0, qs1, ar0, ar1, sb0);
-    if (2 * (S + 1) + 1 < nkb) GNF4_BLOCK(S + 1, 1, qs1, ar1, ar0, sb1);
+    GNF4_BLOCK(S, 0, qs0, ar0, ar1);
+    GNF4_BLOCK(S, 1, qs0, ar1, ar0);
+    GNF4_BLOCK(S + 1, 0, qs1, ar0, ar1);
+    if (2 * (S + 1) + 1 < nkb) GNF4_BLOCK(S + 1, 1, qs1, ar1, ar0);
   }
   if (S < nst) {
-    GNF4_BLOCK(S, 0, qs0, ar0, ar1, sb0);
-    if (2 * S + 1 < nkb) GNF4_BLOCK(S, 1, qs0, ar1, ar0, sb1);
+    GNF4_BLOCK(S, 0, qs0, ar0, ar1);
+    if (2 * S + 1 < nkb) GNF4_BLOCK(S, 1, qs0, ar1, ar0);
   }
 #undef GNF4_BLOCK
 #undef GNF4_DECODE
-#undef GNF4_LOAD_SBYTES
 #undef GNF4_TAKE_WINDOW
 #undef GNF4_LOAD_WINDOW
 #undef GNF4_STORE_A
