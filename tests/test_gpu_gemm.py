@@ -31,6 +31,9 @@ SHAPES = [
     (4, 256, 1024, 200, 2),    # prefill, 400 rows over 4 experts: ~100 rows each, so
                                # one whole 64-row tile and a ragged tail per expert
     (3, 130, 2880, 37, 3),     # prefill, K = 2880, ragged N
+    (4, 192, 384, 50, 2),      # prefill, K = 384: three 128-K stages, no tail
+    (3, 64, 64, 40, 2),        # prefill, K = 64: one block, one stage
+    (3, 96, 192, 40, 2),       # prefill, K = 192: a last stage with one block
 ]
 
 
