@@ -502,8 +502,11 @@ struct OneTokenRoute {
   int nact, total;
 };
 
+// id0: wave 0's lane-j id e_j (-1 past k), loaded by the caller beforehand
+// (unused with LOGITS).
 template <bool LOGITS>
-__device__ __forceinline__ void route_one_token(const GemmArgs &a, OneTokenRoute &sr, int tid) {
+__device__ __forceinline__ void route_one_token(const GemmArgs &a, OneTokenRoute &sr, int tid,
+                                                int id0) {
   const int lane = tid & 63, k = a.k, E = a.w.E;
   if (tid < 64) {
     int e;
@@ -516,7 +519,7 @@ __device__ __forceinline__ void route_one_token(const GemmArgs &a, OneTokenRoute
       }
       if (lane >= k) e = -1;
     } else {
-      e = lane < k ? a.ids[lane] : -1;
+      e = id0;
     }
     const bool valid = lane < k && (unsigned)e < (unsigned)E;
     const uint64_t vmask = __ballot(valid);
@@ -612,8 +615,13 @@ __global__ __launch_bounds__(kGemvWaveThreads, 1) void gemv1w_kernel(GemmArgs a,
 
   int nact, ej, pj0, pj1;                        // slot lane's expert and routed rows
   uint32_t x[1][C][16];
-  // the token row to LDS, loaded by waves 1.. (wave 0 routes); the barrier
-  // below publishes it with the table
+  // the token's ids first (wave 0 routes: the load is in flight during its
+  // share of the table fill), then the token row to LDS, loaded by waves
+  // 1..; the barrier below publishes it with the table
+  int id0 = -1;
+  if constexpr (ROUTE == 1) {
+    if (tid < 64 && lane < a.k) id0 = a.ids[lane];
+  }
   const int xp0 = xs_piece(tid, 64, kGemvWaveThreads - 64, 0, a.w.K / 8);
   const int xp1 = xs_piece(tid, 64, kGemvWaveThreads - 64, 1, a.w.K / 8);
   uint4 xv0, xv1;
@@ -623,7 +631,7 @@ __global__ __launch_bounds__(kGemvWaveThreads, 1) void gemv1w_kernel(GemmArgs a,
   if (xp0 >= 0) s_x[xs_slot(xp0 >> 2, xp0 & 3)] = xv0;
   if (xp1 >= 0) s_x[xs_slot(xp1 >> 2, xp1 & 3)] = xv1;
   if constexpr (ROUTE) {
-    route_one_token<ROUTE == 2>(a, sr, tid);      // ends with a barrier: table written too
+    route_one_token<ROUTE == 2>(a, sr, tid, id0); // ends with a barrier: table written too
     nact = sr.nact;
     const int sl = min(lane, 63);
     ej = lane < nact ? sr.exp[sl] : -1;
