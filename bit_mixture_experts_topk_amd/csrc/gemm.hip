@@ -978,8 +978,8 @@ __device__ __forceinline__ void mfma16_tile(const GemmArgs &a, uint32_t x_bytes,
     for (int ct = 0; ct < 4; ++ct) acc[rt][ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   // stage slots, raw codes: stage S in slot S mod kSlots. MXFP4 keeps a
-  // third stage in flight (3.5 % faster on the gpt-oss shape); the NF4 paths
-  // have no registers for it.
+  // third stage in flight (about 3 % faster on the gpt-oss shape); the NF4
+  // paths have no registers for it.
   constexpr int kSlots = kMX ? 3 : 2;
   uint4 qs0[4], qs1[4], qs2[4];
   uint4 ar0[kALoads], ar1[kALoads];   // A staging ring (even / odd blocks)
@@ -1033,7 +1033,7 @@ __device__ __forceinline__ void mfma16_tile(const GemmArgs &a, uint32_t x_bytes,
     if constexpr (kMX) {                                                                  \
       xw[ct] = xn[ct];                                                                    \
       continue;                                                                           \
-    } else if constexpr (kDQ) {                                                                  \
+    } else if constexpr (kDQ) {                                                           \
       a0_ = (float)(int8_t)(dn[ct] & 0xffu) * __builtin_bit_cast(float, tn[ct].x);        \
       a1_ = (float)(int8_t)((dn[ct] >> 8) & 0xffu) * __builtin_bit_cast(float, tn[ct].y); \
     } else {                                                                              \
@@ -1152,7 +1152,7 @@ __device__ __forceinline__ void mfma16_tile(const GemmArgs &a, uint32_t x_bytes,
     }                                                                                     \
     __builtin_amdgcn_sched_barrier(0);                                                    \
     __builtin_amdgcn_s_setprio(0);                                                       \
-    /* stage S + 2 reuses this stage's slot once block 1 is decoded */                   \
+    /* stage S + kSlots reuses this stage's slot once block 1 is decoded */              \
     if ((B) == 1) GNF4_LOAD_STAGE((S) + kSlots, Q);                                       \
     if constexpr (kLut) {                                                                 \
       _Pragma("unroll") for (int r2 = 0; r2 < 4; ++r2) acc[RT - 1][3][r2] =              \
