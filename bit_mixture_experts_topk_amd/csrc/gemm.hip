@@ -800,12 +800,21 @@ __global__ __launch_bounds__(kGemvCombineThreads, 2) void gemv1c_kernel(GemmArgs
 
 // ===================================================================== MFMA
 
-// Logical tile id from the hardware workgroup id: consecutive logical ids on
-// the same XCD (workgroups are dealt round-robin over the 8 XCDs). The grid
-// is a multiple of 8, so the map is a bijection.
-__device__ __forceinline__ int xcd_remap(int bid, int grid) {
-  const int per = grid >> 3;
-  return (bid & 7) * per + (bid >> 3);
+// M tiles of BM rows over all experts (ceil(count / BM) each), the same
+// value in every lane. The grid is sized on the host from an upper bound of
+// this count; the real count lets each XCD take an equal share.
+template <int BM>
+__device__ __forceinline__ int total_m_tiles(const GemmArgs &a, int lane) {
+  int total = 0;
+  for (int e0 = 0; e0 < a.w.E; e0 += 64) {
+    const int ee = e0 + lane;
+    int t = 0;
+    if (ee < a.w.E) t = (a.offsets[ee + 1] - a.offsets[ee] + BM - 1) / BM;
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) t += __shfl_xor(t, d, 64);
+    total += t;
+  }
+  return total;
 }
 
 // XOR swizzle of the 8 16-byte K segments of activation row r in LDS. An
@@ -1249,8 +1258,17 @@ __global__ __launch_bounds__(kThreads, 2) void mfma16_kernel(GemmArgs a, int n_t
   __shared__ uint4 As[2][kMfmaSegs];
 
   const int lane = threadIdx.x & 63;
+  // Logical tile id from the hardware workgroup id: workgroups are dealt
+  // round-robin over the 8 XCDs, so XCD x (bid & 7) runs bid >> 3 = 0, 1, ...
+  // in turn; it takes the x-th eighth of the real tiles, consecutive ids, and
+  // its workgroups past that share exit. (An eighth of the grid's upper bound
+  // instead left the last XCD most of the empty tail: about 10 % longer.)
+  const int total = total_m_tiles<BM>(a, lane) * n_tiles_n;
+  const int per = (total + 7) >> 3;
+  const int j = (int)(blockIdx.x >> 3);
+  const int bid = (int)(blockIdx.x & 7) * per + j;
+  if (j >= per || bid >= total) return;
   int e, start, tiles;
-  const int bid = xcd_remap(blockIdx.x, gridDim.x);
   find_tile<BM>(a, bid, n_tiles_n, lane, e, start, tiles);
   if (e < 0) return;
   const int local = bid - start;
