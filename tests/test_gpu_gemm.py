@@ -47,6 +47,30 @@ def test_gemm_small(fmt, shape):
     compare_rows(Y, Y_ref, r_ref, "%s %s" % (fmt, shape))
 
 
+# Prefill shapes for the MFMA kernel's tile count and its share per XCD:
+# each workgroup counts the real M tiles over all experts (in chunks of 64
+# experts) and takes one eighth of them per XCD, so the cases cover a ragged
+# last chunk of experts, fewer tiles than XCDs, and a few busy experts among
+# many empty ones (HOT: every token picks k of the HOT experts 0, E/2, E-1).
+@pytest.mark.parametrize("fmt", ["nf4", "nf4_dq", "mxfp4"])
+@pytest.mark.parametrize("E,N,K,T,k,hot", [
+    (200, 96, 128, 100, 4, False),     # 4 chunks of experts, the last one ragged
+    (2, 64, 128, 40, 2, False),        # 40 rows on each of 2 experts: 2 tiles, fewer than the XCDs
+    (300, 320, 128, 70, 2, True),      # 140 rows on 3 of 300 experts, 2 N tiles
+])
+def test_mfma_tile_count_and_xcd_share(fmt, E, N, K, T, k, hot):
+    g = gnf4()
+    case = synth.small_layer(E, N, K, T, k, seed=9)
+    ids = case["ids"]
+    if hot:
+        busy = np.array([0, E // 2, E - 1], dtype=np.int32)
+        rng = np.random.Generator(np.random.PCG64(11))
+        ids = np.stack([rng.permutation(busy)[:k] for _ in range(T)]).astype(np.int32)
+    assert T * k > 64                              # the MFMA path
+    Y, Y_ref, r_ref = run_layer_call(g, fmt, case["W"], case["X"], ids, 1, k, "tile share")
+    compare_rows(Y, Y_ref, r_ref, "tile share %s E=%d" % (fmt, E))
+
+
 @pytest.mark.parametrize("fmt", ["nf4", "mxfp4"])
 @pytest.mark.parametrize("T,k,distinct", [(1, 4, True), (1, 6, False), (4, 4, True), (30, 4, True)])
 def test_gemm_permuted_input(fmt, T, k, distinct):
