@@ -146,6 +146,12 @@ __device__ __forceinline__ void gemv_load_rows(const GemmArgs &a, const GemvGeom
           reinterpret_cast<const u32x4_t *>(cb + (r[u] * (uint32_t)(K / 2) + ch[c] * 16u)));
       R.q[u][c] = make_uint4(q[0], q[1], q[2], q[3]);
     }
+  // MXFP4: every load of the item is issued before anything waits for one of
+  // them (the compiler otherwise starts converting the first row's scales,
+  // and waits for them, before the last code rows are requested): 3.6 %
+  // faster on the gpt-oss-shaped one-token GEMV. The NF4 paths measured 0 to
+  // 4 % slower with the same barrier and keep the compiler's order.
+  if constexpr (FMT == GNF4_MXFP4) __builtin_amdgcn_sched_barrier(0);
 }
 
 // Token slices in registers: x[t][c][i] holds the bf16 pair for K values
